@@ -1,0 +1,334 @@
+"""Plain CPU oracle for the routed FP4 expert FFN of a DeepSeek-style MoE decoder layer.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The product path
+(``fp4_expert_ffn_amd``: HIP kernels behind a C ABI) never imports it, and this module
+imports nothing from the product path: NumPy and the standard library only.
+
+Everything here is fp64 and written for checking by eye, not for speed: no blocking, no
+fusion, no reordering beyond what each definition states. Library primitives used as steps:
+``numpy.matmul`` (a plain fp64 matrix product), ``numpy.exp`` and ``numpy.ldexp``.
+
+Sources. The pages this follows, cited by title and section:
+
+* [A100-FP4] shi3z, "DeepSeek v4.1 Flashを動かしたくてFP4に対応していないA100を、33tok/sから
+  673 tok/sまで持っていって気がつくと公式APIより速くなっていた話" (note.com), and its Chinese
+  translation "把不支持 FP4 的 A100 拉到 673 tok/s". Section 「FP4非対応」という言葉を疑う
+  (Chinese: 质疑「不支持 FP4」这句话): E2M1 has 2 exponent bits and 1 mantissa bit; twice
+  its values are the small integers 0, ±1, ±2, ±3, ±4, ±6, ±8, ±12; a 4-bit by 4-bit product
+  has only 256 cases.
+* [8GB-GPU] "在 8 GB 显卡上运行 510 GB 的 DeepSeek-V4.1-Flash——以及三个从不抛错的 Bug".
+  Section 每 token 字节数决定一切: 384 experts per layer, 6 chosen per token, 17.93 MiB per
+  FP4 expert with scales. Section 方案：不重写模型，只迁移其存储: the three matrices of an
+  expert are stored next to each other (17.7 MB) and the scales are a separate block
+  (1.1 MB). Section RTX 50xx 上的三个从不抛错的 Bug: the scale format is ue8m0.
+
+Readings taken where the pages are silent (each is listed with its reason in the design notes):
+
+* E2M1 code layout is the OCP MX one: bit 3 sign, bits 2:1 exponent with bias 1, bit 0
+  mantissa. Two codes per byte, the low nibble holds the even K index.
+* A ue8m0 scale byte ``e`` means 2**(e - 127); e == 255 means NaN.
+* One scale per 32 consecutive elements along K (the only block size that gives 1.1 MB of
+  one-byte scales next to 17.7 MB of codes for hidden 4096 and intermediate 2880).
+* Matrices per expert, in this order: gate [I x H], up [I x H], down [H x I], each row-major
+  [out x in] (K = in is the contiguous axis).
+* Router: logits = W_r x accumulated in fp64; the k largest logits, ordered by descending
+  logit with ties going to the lower expert id; weights = softmax over those k logits only
+  (a full softmax renormalised over the chosen k gives the same numbers, since the full
+  denominator cancels).
+* SwiGLU: h = silu(g) * u with silu(z) = z / (1 + exp(-z)); no clamp, no shared expert,
+  routed scaling factor 1.
+* Combine: y = sum_j w_j * y_{e_j}, summed in ascending expert id. Ids outside [0, E)
+  contribute nothing. Duplicate ids are legal and add up.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Callable, Tuple
+
+import numpy as np
+
+# ---------------------------------------------------------------------------------------
+# 1. Number formats
+# ---------------------------------------------------------------------------------------
+
+#: The 16-entry E2M1 value table, indexed by the 4-bit code. Codes 0..7 are the positive
+#: values (exponent field 0 is subnormal: 0 and 0.5), codes 8..15 the same magnitudes with
+#: the sign bit set ([A100-FP4], 「FP4非対応」という言葉を疑う; code layout per the OCP MX reading).
+E2M1_VALUES: Tuple[float, ...] = (
+    0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+    -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0,
+)
+
+#: Elements per ue8m0 scale block along K.
+BLOCK = 32
+
+#: Matrix order inside one expert blob ([8GB-GPU], 方案：不重写模型，只迁移其存储).
+GATE, UP, DOWN = 0, 1, 2
+
+
+def e2m1_table() -> np.ndarray:
+    """The E2M1 table as a float64 array of 16 entries."""
+    return np.array(E2M1_VALUES, dtype=np.float64)
+
+
+def ue8m0_to_f64(e: np.ndarray) -> np.ndarray:
+    """Decode ue8m0 scale bytes: 2**(e - 127) exactly in fp64, NaN for e == 255
+    ([8GB-GPU], RTX 50xx 上的三个从不抛错的 Bug names the format; the meaning is the OCP
+    E8M0 reading)."""
+    e = np.asarray(e, dtype=np.int64)
+    out = np.ldexp(np.ones(e.shape, dtype=np.float64), e - 127)
+    return np.where(e == 255, np.nan, out)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bfloat16 bit patterns (uint16) exactly: a bf16 is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bfloat16 (round to nearest, ties to even, subnormals kept,
+    overflow to infinity) and return the bit patterns. One value at a time, on the exact
+    binary value, so no double rounding through fp32 can occur."""
+    v = np.asarray(v, dtype=np.float64)
+    flat = v.ravel()
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for i in range(flat.shape[0]):
+        out[i] = _f64_to_bf16_scalar(float(flat[i]))
+    return out.reshape(v.shape)
+
+
+def _f64_to_bf16_scalar(val: float) -> int:
+    if math.isnan(val):
+        return 0x7FC0
+    sign = 1 if math.copysign(1.0, val) < 0 else 0
+    if val == 0.0:
+        return sign << 15
+    if math.isinf(val):
+        return (sign << 15) | 0x7F80
+    m, q = math.frexp(abs(val))  # abs(val) = m * 2**q, 0.5 <= m < 1
+    # bf16 normal: 1.f (7 bits) * 2**(E-127), E in 1..254; subnormal: 0.f * 2**-126.
+    exp = q - 1  # abs(val) = (2m) * 2**exp with 1 <= 2m < 2
+    if exp < -126:
+        exp_eff = -126
+    else:
+        exp_eff = exp
+    # quantum of the target grid at this exponent: 2**(exp_eff - 7)
+    scaled = abs(val) / math.ldexp(1.0, exp_eff - 7)  # exact: power-of-two division
+    lo = math.floor(scaled)
+    frac = scaled - lo
+    if frac > 0.5 or (frac == 0.5 and (lo & 1)):
+        lo += 1
+    # lo is the integer significand on the 2**(exp_eff-7) grid (may carry into next binade)
+    if exp < -126:
+        # subnormal range: lo in [0, 128]; 128 means the smallest normal
+        bits = lo  # exponent field 0 plus mantissa, or 0x80 -> exponent field 1
+    else:
+        if lo == 256:  # carried into the next binade
+            lo = 128
+            exp_eff += 1
+        if exp_eff > 127:
+            return (sign << 15) | 0x7F80  # overflow to infinity
+        bits = ((exp_eff + 127) << 7) | (lo - 128)
+    return (sign << 15) | bits
+
+
+def dequant_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantise one FP4 matrix to fp64.
+
+    codes:  uint8 [N, K/2]; byte b of a row holds element 2b in its low nibble and element
+            2b+1 in its high nibble.
+    scales: uint8 [N, K/32]; one ue8m0 byte per 32 consecutive elements along K.
+    Returns W [N, K] with W[n, k] = E2M1_VALUES[code[n, k]] * 2**(scale[n, k // 32] - 127),
+    which is exact in fp64.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    n, half_k = codes.shape
+    k = 2 * half_k
+    if scales.shape != (n, k // BLOCK) or k % BLOCK:
+        raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
+    nib = np.empty((n, k), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    vals = e2m1_table()[nib]
+    return vals * np.repeat(ue8m0_to_f64(scales), BLOCK, axis=1)
+
+
+# ---------------------------------------------------------------------------------------
+# 2. Expert blobs
+# ---------------------------------------------------------------------------------------
+
+def expert_matrix_shapes(hidden: int, inter: int) -> Tuple[Tuple[int, int], ...]:
+    """(rows, K) of gate, up and down for one expert."""
+    return ((inter, hidden), (inter, hidden), (hidden, inter))
+
+
+def expert_bytes(hidden: int, inter: int) -> Tuple[int, int]:
+    """(code bytes, scale bytes) of one expert: 3 matrices of hidden*inter elements, half a
+    byte per code and one byte per 32 elements ([8GB-GPU], 每 token 字节数决定一切 and
+    方案：不重写模型，只迁移其存储)."""
+    n = 3 * hidden * inter
+    return n // 2, n // BLOCK
+
+
+def split_expert(codes_flat: np.ndarray, scales_flat: np.ndarray, hidden: int, inter: int):
+    """Split one canonical expert blob (codes: gate|up|down row-major, scales likewise) into
+    three (codes [N, K/2], scales [N, K/32]) pairs."""
+    out = []
+    c_off = s_off = 0
+    for rows, k in expert_matrix_shapes(hidden, inter):
+        nc, ns = rows * k // 2, rows * k // BLOCK
+        out.append((codes_flat[c_off:c_off + nc].reshape(rows, k // 2),
+                    scales_flat[s_off:s_off + ns].reshape(rows, k // BLOCK)))
+        c_off += nc
+        s_off += ns
+    return out
+
+
+def dequant_expert(codes_flat: np.ndarray, scales_flat: np.ndarray, hidden: int, inter: int):
+    """Dequantised (W_gate [I,H], W_up [I,H], W_down [H,I]) of one canonical expert blob."""
+    return tuple(dequant_fp4(c, s) for c, s in split_expert(codes_flat, scales_flat, hidden, inter))
+
+
+# ---------------------------------------------------------------------------------------
+# 3. Router
+# ---------------------------------------------------------------------------------------
+
+def router_logits(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
+    """logits[t, e] = sum_h W_r[e, h] * x[t, h] in fp64. Every bf16 x bf16 product is exact
+    in fp64; only the sum rounds."""
+    x = bf16_to_f64(x_bits)
+    wr = bf16_to_f64(w_router_bits)
+    return np.matmul(x, wr.T)
+
+
+def topk_softmax(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k selection with renormalised softmax weights, per token.
+
+    ids[t]: the k experts with the largest logits, ordered by descending logit, equal logits
+            ordered by ascending expert id.
+    w[t, j] = exp(l_j - l_max) / sum over the k chosen of exp(l_i - l_max)   (fp64).
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    t_count, n_exp = logits.shape
+    if not 1 <= k <= n_exp:
+        raise ValueError("k out of range")
+    ids = np.empty((t_count, k), dtype=np.int32)
+    w = np.empty((t_count, k), dtype=np.float64)
+    expert_ids = np.arange(n_exp)
+    for t in range(t_count):
+        # lexsort: last key is primary -> primary descending logit, secondary ascending id
+        order = np.lexsort((expert_ids, -logits[t]))[:k]
+        ids[t] = order
+        chosen = logits[t, order]
+        ex = np.exp(chosen - chosen.max())
+        w[t] = ex / ex.sum()
+    return ids, w
+
+
+def route(x_bits: np.ndarray, w_router_bits: np.ndarray, k: int):
+    """Router GEMV then top-k softmax. Returns (ids int32 [T,k], w fp64 [T,k], logits)."""
+    logits = router_logits(x_bits, w_router_bits)
+    ids, w = topk_softmax(logits, k)
+    return ids, w, logits
+
+
+# ---------------------------------------------------------------------------------------
+# 4. Expert FFN and combine
+# ---------------------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)). For very negative z, exp(-z) overflows to inf and the
+    quotient is the correct limit -0."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on a batch of rows x [T, H]: g = x W_g^T, u = x W_u^T,
+    h = silu(g) * u, y = h W_d^T. All fp64."""
+    g = np.matmul(x, w_gate.T)
+    u = np.matmul(x, w_up.T)
+    h = silu(g) * u
+    return np.matmul(h, w_down.T)
+
+
+ExpertSource = Callable[[int], Tuple[np.ndarray, np.ndarray]]
+
+
+def expert_ffn(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, expert_source: ExpertSource,
+               n_experts: int, hidden: int, inter: int) -> np.ndarray:
+    """The routed expert FFN with the router-weighted combine, fp64.
+
+    x_bits: bf16 bits [T, H]; ids: int [T, k]; w: float [T, k] (used as given);
+    expert_source(e) returns the canonical (codes, scales) of expert e.
+    y[t] = sum over j, in ascending expert id, of w[t, j] * expert_{ids[t, j]}(x[t]).
+    Ids outside [0, n_experts) contribute nothing.
+    """
+    x = bf16_to_f64(x_bits)
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    t_count = x.shape[0]
+    y = np.zeros((t_count, hidden), dtype=np.float64)
+    valid = (ids >= 0) & (ids < n_experts)
+    # Visiting experts in ascending id makes every token's sum run in ascending id order.
+    for e in np.unique(ids[valid]):
+        rows_t, slots = np.nonzero(ids == e)
+        wg, wu, wd = dequant_expert(*expert_source(int(e)), hidden, inter)
+        # one token may pick the same expert twice: each (t, slot) pair adds its own term
+        ye = swiglu_expert(x[rows_t], wg, wu, wd)
+        for r in range(rows_t.shape[0]):
+            y[rows_t[r]] += w[rows_t[r], slots[r]] * ye[r]
+    return y
+
+
+def moe_layer(x_bits: np.ndarray, w_router_bits: np.ndarray, k: int, expert_source: ExpertSource,
+              n_experts: int, hidden: int, inter: int):
+    """Route then expert FFN: returns (y fp64 [T,H], ids, w)."""
+    ids, w, _ = route(x_bits, w_router_bits, k)
+    return expert_ffn(x_bits, ids, w, expert_source, n_experts, hidden, inter), ids, w
+
+
+# ---------------------------------------------------------------------------------------
+# 5. Layer chaining used by the multi-layer decode workload
+# ---------------------------------------------------------------------------------------
+
+def residual_rmsnorm(r: np.ndarray, y: np.ndarray, eps: float = 1e-6):
+    """r' = r + y; x' = bf16(r' / sqrt(mean(r'^2) + eps)) with unit gain.
+    Returns (r' fp64, x' bf16 bits). The pages name RMSNorm among the per-layer kernels
+    ([A100-FP4], 然后又发现每 token 启动 2000 次内核); residual and eps are the plain reading."""
+    r2 = np.asarray(r, dtype=np.float64) + np.asarray(y, dtype=np.float64)
+    rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True) + eps)
+    return r2, f64_to_bf16_bits(r2 / rms)
+
+
+def expert_sources_from_arrays(codes: np.ndarray, scales: np.ndarray) -> ExpertSource:
+    """Expert source over in-memory canonical arrays codes [E, nc], scales [E, ns]."""
+    def src(e: int):
+        return codes[e], scales[e]
+    return src
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    if na == 0.0 and nb == 0.0:
+        return 1.0
+    if na == 0.0 or nb == 0.0:
+        return 0.0
+    return float(np.dot(a, b) / (na * nb))
+
+
+def normwise_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    """max_h |y - ref| / max_h |ref| for one token (0 if both are zero)."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref))
+    num = np.max(np.abs(y - ref))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return float(num / den)

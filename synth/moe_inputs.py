@@ -1,0 +1,155 @@
+"""Seeded synthetic inputs for the routed FP4 expert FFN workloads.
+
+Shared by the tests, the bench and the smoke check: both the HIP path and the oracle are fed
+from here. This module holds none of the method's arithmetic (no decoding, no routing, no
+FFN): it only draws random numbers and lays them out in the canonical input formats.
+
+Every tensor has its own stream, seeded by
+``SeedSequence([root, workload_id, layer, index, tensor_id])``, so any one expert (or any one
+token's activations) can be regenerated on its own, in any order.
+
+Canonical formats (the inputs the library's pack and FFN calls consume):
+* expert codes: uint8 [3 * H * I / 2] per expert = gate [I x H/2] | up [I x H/2] |
+  down [H x I/2], row-major, two E2M1 codes per byte (low nibble = even K index);
+* expert scales: uint8 [3 * H * I / 32] per expert, same matrix order, one byte per 32 K;
+* activations and router weights: bfloat16 bit patterns (uint16), row-major.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+T_CODES, T_SCALES, T_X, T_ROUTER, T_LOGITS, T_PERM = range(6)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes and value distributions."""
+    name: str
+    wid: int                 # workload id, part of every seed
+    hidden: int
+    inter: int
+    n_experts: int
+    k: int
+    tokens: int              # tokens per step
+    layers: int = 1
+    routing: str = "router"  # "router" (x -> W_r GEMV), "zipf", "uniform", "fixed"
+    zipf_s: float = 1.1
+    scale_lo: int = 120      # ue8m0 scale bytes drawn uniformly from [scale_lo, scale_hi]
+    scale_hi: int = 130
+    router_std: float = 0.02
+    steps: int = 1           # sequential steps (tokens for decode)
+    note: str = field(default="", compare=False)
+
+    @property
+    def expert_code_bytes(self) -> int:
+        return 3 * self.hidden * self.inter // 2
+
+    @property
+    def expert_scale_bytes(self) -> int:
+        return 3 * self.hidden * self.inter // 32
+
+
+WORKLOADS = {
+    # One SwiGLU expert, batch 1, every code uniform over 16 values, scales in [120, 130].
+    "expert_h256_i128": Workload("expert_h256_i128", 1, 256, 128, 1, 1, 1, routing="fixed",
+                                 note="single expert, hidden 256, intermediate 128, batch 1"),
+    # One 384-expert MoE layer, batch-1 decode, router N(0, 0.02), top-6.
+    "layer_decode_h4096_i2880_e384": Workload(
+        "layer_decode_h4096_i2880_e384", 2, 4096, 2880, 384, 6, 1, steps=1000,
+        note="one MoE layer decode, batch 1, 384 experts, top-6, fresh x per token"),
+    # 16 chained layers, batch 1.
+    "stack16_decode": Workload("stack16_decode", 3, 4096, 2880, 384, 6, 1, layers=16, steps=1000,
+                               note="16 MoE layers, residual + RMSNorm between layers"),
+    # 64 tokens per step, Zipf(1.1)-skewed router logits.
+    "batched64_zipf": Workload("batched64_zipf", 4, 4096, 2880, 384, 6, 64, routing="zipf",
+                               note="64 tokens per step, Zipf(1.1) logits"),
+    # 8192 tokens, uniform router logits.
+    "prefill8192_uniform": Workload("prefill8192_uniform", 5, 4096, 2880, 384, 6, 8192,
+                                    routing="uniform", note="8192 tokens, U(0,1) logits"),
+    # Supplementary compute-bound shape.
+    "prefill32768_uniform": Workload("prefill32768_uniform", 6, 4096, 2880, 384, 6, 32768,
+                                     routing="uniform", note="32768 tokens, U(0,1) logits"),
+}
+
+
+def rng_for(root: int, wid: int, layer: int, index: int, tensor: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([root, wid, layer, index, tensor]))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns, round to nearest even (inputs are finite)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def expert_blob(wl: Workload, layer: int, expert: int, root: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Canonical (codes, scales) of one expert: code bytes uniform over 0..255 (so both
+    nibbles are uniform over the 16 codes), scale bytes uniform over [scale_lo, scale_hi]."""
+    codes = np.frombuffer(rng_for(root, wl.wid, layer, expert, T_CODES).bytes(wl.expert_code_bytes),
+                          dtype=np.uint8).copy()
+    scales = rng_for(root, wl.wid, layer, expert, T_SCALES).integers(
+        wl.scale_lo, wl.scale_hi + 1, size=wl.expert_scale_bytes, dtype=np.uint8)
+    return codes, scales
+
+
+def expert_source(wl: Workload, layer: int = 0, root: int = 0):
+    """Callable e -> canonical (codes, scales), regenerating expert e from its seed."""
+    def src(e: int):
+        return expert_blob(wl, layer, e, root)
+    return src
+
+
+def activations(wl: Workload, layer: int, step: int, tokens: Optional[int] = None,
+                root: int = 0) -> np.ndarray:
+    """bf16 bits [T, H] with values bf16(N(0, 1))."""
+    t = wl.tokens if tokens is None else tokens
+    z = rng_for(root, wl.wid, layer, step, T_X).standard_normal((t, wl.hidden), dtype=np.float32)
+    return f32_to_bf16_bits(z)
+
+
+def router_weights(wl: Workload, layer: int, root: int = 0) -> np.ndarray:
+    """bf16 bits [E, H] with values bf16(router_std * N(0, 1))."""
+    z = rng_for(root, wl.wid, layer, 0, T_ROUTER).standard_normal((wl.n_experts, wl.hidden),
+                                                                   dtype=np.float32)
+    return f32_to_bf16_bits(z * np.float32(wl.router_std))
+
+
+def router_logits(wl: Workload, layer: int, step: int, tokens: Optional[int] = None,
+                  root: int = 0) -> np.ndarray:
+    """Synthetic router logits fp32 [T, E] for workloads that draw them directly.
+
+    zipf:    logits[t, e] = ln p_{pi(e)} + Gumbel(0, 1), p_r proportional to r**-s for rank
+             r = 1..E and pi a seeded permutation fixed per layer; the top-k of these is a
+             draw of k experts without replacement with probabilities p.
+    uniform: logits i.i.d. U(0, 1), so the top-k is a uniform k-subset.
+    """
+    t = wl.tokens if tokens is None else tokens
+    rng = rng_for(root, wl.wid, layer, step, T_LOGITS)
+    if wl.routing == "uniform":
+        return rng.random((t, wl.n_experts), dtype=np.float32)
+    if wl.routing == "zipf":
+        perm = rng_for(root, wl.wid, layer, 0, T_PERM).permutation(wl.n_experts)
+        ranks = np.arange(1, wl.n_experts + 1, dtype=np.float64)
+        logp = -wl.zipf_s * np.log(ranks)
+        logp -= np.log(np.exp(logp).sum())
+        base = logp[perm]  # expert e gets rank perm[e] + 1
+        gumbel = -np.log(-np.log(rng.random((t, wl.n_experts))))
+        return (base[None, :] + gumbel).astype(np.float32)
+    raise ValueError(f"workload {wl.name} does not draw logits directly")
+
+
+def random_codes(rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
+    """Uniform code bytes [rows, k/2] for ad-hoc small matrices in tests."""
+    return rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+
+
+def small_workload(hidden: int, inter: int, n_experts: int, k: int, tokens: int,
+                   wid: int = 100, **kw) -> Workload:
+    """A reduced-size workload with the same value distributions, for parity tests."""
+    return Workload(f"small_h{hidden}_i{inter}_e{n_experts}_k{k}_t{tokens}", wid, hidden, inter,
+                    n_experts, k, tokens, **kw)

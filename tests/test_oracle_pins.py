@@ -1,0 +1,349 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test is chosen so that a plausible mistake in the oracle (a wrong table entry, a swapped
+nibble, a dropped term, a transposed operand, a wrong sign) fails at least one of them.
+CPU only.
+"""
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synth import moe_inputs as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_ints():
+    with open(os.path.join(GOLDEN, "e2m1_doubled_integers.txt")) as f:
+        line = [l for l in f if l.strip() and not l.startswith("#")][0]
+    return [int(v) for v in line.split()]
+
+
+# --------------------------------------------------------------------------- decode table
+
+def test_e2m1_doubled_values_are_the_pages_integer_set():
+    ints = _golden_ints()
+    doubled = [2.0 * v for v in O.E2M1_VALUES]
+    assert all(d == int(d) for d in doubled)
+    assert sorted(set(int(d) for d in doubled)) == sorted(set(ints))
+    # 16 codes onto 15 values: only +0 and -0 coincide
+    assert len(set(int(d) for d in doubled)) == 15
+
+
+def test_e2m1_code_order_sign_and_monotonicity():
+    # The integer set does not fix which code maps to which value; the OCP layout does:
+    # codes 0..7 ascend, and code 8+i is the negation of code i (sign bit 3).
+    v = O.E2M1_VALUES
+    assert all(v[i] < v[i + 1] for i in range(7))
+    for i in range(8):
+        assert v[8 + i] == -v[i]
+        assert math.copysign(1.0, v[8 + i]) == -1.0
+    # exponent field 0 is the subnormal pair {0, 0.5}; code 2 (exponent 1, mantissa 0) is 1.0
+    assert v[0] == 0.0 and v[1] == 0.5 and v[2] == 1.0 and v[7] == 6.0
+
+
+def test_all_256_products_are_exact_small_integers_over_4():
+    ints = set(_golden_ints())
+    pair_products = {a * b for a in ints for b in ints}
+    seen = set()
+    for a in range(16):
+        for b in range(16):
+            p4 = 4.0 * O.E2M1_VALUES[a] * O.E2M1_VALUES[b]
+            assert p4 == int(p4) and -144 <= p4 <= 144
+            assert int(p4) == int(2 * O.E2M1_VALUES[a]) * int(2 * O.E2M1_VALUES[b])
+            seen.add(int(p4))
+    assert seen == pair_products
+
+
+def test_ue8m0_scale_decoding():
+    e = np.arange(256)
+    s = O.ue8m0_to_f64(e)
+    assert s[127] == 1.0 and s[128] == 2.0 and s[126] == 0.5
+    assert s[0] == 2.0 ** -127 and s[254] == 2.0 ** 127
+    assert np.isnan(s[255])
+    assert np.all(s[1:255] == 2.0 * s[0:254])
+
+
+def test_dequant_matches_per_element_bitfield_decode():
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 256, size=(5, 32), dtype=np.uint8)       # [5 rows, K=64]
+    scales = rng.integers(100, 150, size=(5, 2), dtype=np.uint8)
+    w = O.dequant_fp4(codes, scales)
+    assert w.shape == (5, 64)
+    for n in range(5):
+        for k in range(64):
+            byte = int(codes[n, k // 2])
+            c = (byte & 0xF) if k % 2 == 0 else (byte >> 4)
+            sign, exp, man = c >> 3, (c >> 1) & 3, c & 1
+            mag = man * 0.5 if exp == 0 else 2.0 ** (exp - 1) * (1 + man / 2)
+            ref = (-mag if sign else mag) * 2.0 ** (int(scales[n, k // 32]) - 127)
+            assert w[n, k] == ref
+
+
+# --------------------------------------------------------------------------- sizes
+
+def test_expert_byte_counts_match_the_pages():
+    with open(os.path.join(GOLDEN, "expert_bytes.json")) as f:
+        g = json.load(f)
+    codes, scales = O.expert_bytes(g["hidden"], g["intermediate"])
+    assert codes == 17_694_720 and scales == 1_105_920
+    assert round(codes / 1e6, 1) == g["expert_weight_MB"]
+    assert round(scales / 1e6, 1) == g["expert_scale_MB"]
+    assert round((codes + scales) / 2 ** 20, 2) == g["expert_MiB"]
+    per_token = g["layers"] * g["experts_per_token"] * (codes + scales)
+    assert round(per_token / 2 ** 30, 1) == g["per_token_GiB"]
+    full = g["layers"] * g["experts_per_layer"] * (codes + scales)
+    assert round(full / 2 ** 30) == g["full_expert_set_GiB"]
+    # a 16- or 64-element block would not give 1.1 MB of scales
+    n = 3 * g["hidden"] * g["intermediate"]
+    assert round(n / 16 / 1e6, 1) != g["expert_scale_MB"]
+    assert round(n / 64 / 1e6, 1) != g["expert_scale_MB"]
+
+
+def test_synthetic_blob_sizes_and_determinism():
+    wl = S.small_workload(64, 32, 4, 2, 3)
+    c1, s1 = S.expert_blob(wl, 0, 2)
+    c2, s2 = S.expert_blob(wl, 0, 2)
+    assert c1.shape == (3 * 64 * 32 // 2,) and s1.shape == (3 * 64 * 32 // 32,)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    c3, _ = S.expert_blob(wl, 0, 3)
+    assert not np.array_equal(c1, c3)
+    assert s1.min() >= 120 and s1.max() <= 130
+
+
+# --------------------------------------------------------------------------- brute force
+
+def _bf16(x):
+    return O.bf16_to_f64(x)
+
+
+def _brute_ffn_token(x, ids, w, src, H, I):
+    """Exact rational arithmetic for the linear parts, 50-digit decimal for SiLU."""
+    getcontext().prec = 50
+    xs = [Fraction(float(v)) for v in x]
+    total = [Decimal(0)] * H
+    for e, wj in sorted(zip(ids, w), key=lambda p: p[0]):
+        codes, scales = src(int(e))
+        mats = O.split_expert(codes, scales, H, I)
+        wmat = []
+        for c, s in mats:
+            rows, hk = c.shape
+            m = []
+            for r in range(rows):
+                row = []
+                for k in range(2 * hk):
+                    byte = int(c[r, k // 2])
+                    code = (byte & 0xF) if k % 2 == 0 else (byte >> 4)
+                    val = Fraction(O.E2M1_VALUES[code]) * Fraction(2) ** (int(s[r, k // 32]) - 127)
+                    row.append(val)
+                m.append(row)
+            wmat.append(m)
+        g = [sum(wmat[0][i][k] * xs[k] for k in range(H)) for i in range(I)]
+        u = [sum(wmat[1][i][k] * xs[k] for k in range(H)) for i in range(I)]
+        h = []
+        for i in range(I):
+            gd = Decimal(g[i].numerator) / Decimal(g[i].denominator)
+            ud = Decimal(u[i].numerator) / Decimal(u[i].denominator)
+            h.append(gd / (Decimal(1) + (-gd).exp()) * ud)
+        for n in range(H):
+            acc = Decimal(0)
+            for i in range(I):
+                f = wmat[2][n][i]
+                acc += Decimal(f.numerator) / Decimal(f.denominator) * h[i]
+            total[n] += Decimal(repr(float(wj))) * acc
+    return np.array([float(v) for v in total])
+
+
+def test_ffn_matches_exact_brute_force_on_tiny_shapes():
+    H, I, E, k, T = 64, 32, 4, 2, 2
+    wl = S.small_workload(H, I, E, k, T, wid=101)
+    src = S.expert_source(wl)
+    x = S.activations(wl, 0, 0)
+    ids = np.array([[3, 1], [2, 2]], dtype=np.int32)   # second token: a duplicated id
+    w = np.array([[0.625, 0.375], [0.5, 0.25]])
+    y = O.expert_ffn(x, ids, w, src, E, H, I)
+    xf = _bf16(x)
+    for t in range(T):
+        ref = _brute_ffn_token(xf[t], ids[t], w[t], src, H, I)
+        assert O.normwise_rel_err(y[t], ref) < 1e-12
+        assert np.max(np.abs(y[t] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def _identity_expert(H, I):
+    """gate = up = [I x H] with 1.0 on the diagonal, down = [H x I] with 1.0 on the
+    diagonal, every scale 127 (factor 1)."""
+    def mat(rows, k):
+        c = np.zeros((rows, k // 2), dtype=np.uint8)
+        for r in range(min(rows, k)):
+            byte_idx, hi = divmod(r, 2)
+            c[r, byte_idx] |= (0x2 << 4) if hi else 0x2      # code 0b0010 = 1.0
+        s = np.full((rows, k // 32), 127, dtype=np.uint8)
+        return c, s
+    parts = [mat(I, H), mat(I, H), mat(H, I)]
+    codes = np.concatenate([p[0].ravel() for p in parts])
+    scales = np.concatenate([p[1].ravel() for p in parts])
+    return codes, scales
+
+
+def test_identity_weights_give_w_silu_x_times_x():
+    H, I = 64, 32
+    codes, scales = _identity_expert(H, I)
+    rng = np.random.default_rng(5)
+    x = S.f32_to_bf16_bits(rng.standard_normal((3, H), dtype=np.float32))
+    ids = np.zeros((3, 1), dtype=np.int32)
+    w = np.array([[0.75], [1.0], [-2.0]])
+    y = O.expert_ffn(x, ids, w, lambda e: (codes, scales), 1, H, I)
+    xf = _bf16(x)
+    for t in range(3):
+        z = xf[t, :I]
+        expect = w[t, 0] * (z / (1 + np.exp(-z))) * z
+        assert np.allclose(y[t, :I], expect, rtol=1e-15, atol=0)
+        assert np.all(y[t, I:] == 0.0)
+
+
+def test_zero_input_gives_zero_output():
+    wl = S.small_workload(64, 32, 3, 2, 2, wid=102)
+    x = np.zeros((2, 64), dtype=np.uint16)
+    y = O.expert_ffn(x, np.array([[0, 1], [2, 0]]), np.ones((2, 2)), S.expert_source(wl), 3, 64, 32)
+    assert np.all(y == 0.0)
+
+
+def test_one_hot_input_selects_scaled_columns():
+    H, I = 64, 32
+    wl = S.small_workload(H, I, 1, 1, 1, wid=103)
+    codes, scales = S.expert_blob(wl, 0, 0)
+    wg, wu, wd = O.dequant_expert(codes, scales, H, I)
+    c, a = 17, 1.5
+    x = np.zeros((1, H), dtype=np.uint16)
+    x[0, c] = S.f32_to_bf16_bits(np.array([a], dtype=np.float32))[0]
+    y = O.expert_ffn(x, np.zeros((1, 1), np.int32), np.ones((1, 1)), lambda e: (codes, scales), 1, H, I)
+    g, u = a * wg[:, c], a * wu[:, c]
+    h = g / (1 + np.exp(-g)) * u
+    assert np.allclose(y[0], wd @ h, rtol=1e-13, atol=1e-300)
+
+
+def test_k_copies_of_one_expert_equal_that_expert():
+    H, I, E = 64, 32, 3
+    wl = S.small_workload(H, I, E, 4, 2, wid=104)
+    src = S.expert_source(wl)
+    x = S.activations(wl, 0, 0)
+    single = O.expert_ffn(x, np.full((2, 1), 1, np.int32), np.ones((2, 1)), src, E, H, I)
+    copies = O.expert_ffn(x, np.full((2, 4), 1, np.int32), np.full((2, 4), 0.25), src, E, H, I)
+    assert np.allclose(copies, single, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("mat", [O.UP, O.DOWN])
+def test_adding_one_to_every_up_or_down_scale_doubles_y_exactly(mat):
+    H, I, E = 64, 32, 2
+    wl = S.small_workload(H, I, E, 2, 3, wid=105)
+    src = S.expert_source(wl)
+    x = S.activations(wl, 0, 0)
+    ids = np.array([[0, 1], [1, 0], [1, 1]], np.int32)
+    w = np.array([[0.3, 0.7], [0.6, 0.4], [0.5, 0.5]])
+    y = O.expert_ffn(x, ids, w, src, E, H, I)
+    n_gu = I * H // 32
+
+    def src2(e):
+        c, s = src(e)
+        s = s.copy()
+        lo = mat * n_gu
+        s[lo:lo + n_gu] += 1
+        return c, s
+    y2 = O.expert_ffn(x, ids, w, src2, E, H, I)
+    assert np.array_equal(y2, 2.0 * y)
+
+
+def test_permuting_pairs_and_relabelling_experts():
+    H, I, E, k, T = 64, 32, 5, 3, 4
+    wl = S.small_workload(H, I, E, k, T, wid=106)
+    src = S.expert_source(wl)
+    x = S.activations(wl, 0, 0)
+    rng = np.random.default_rng(7)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k))
+    y = O.expert_ffn(x, ids, w, src, E, H, I)
+    perm_slots = np.stack([rng.permutation(k) for _ in range(T)])
+    ids_p = np.take_along_axis(ids, perm_slots, 1)
+    w_p = np.take_along_axis(w, perm_slots, 1)
+    assert np.array_equal(O.expert_ffn(x, ids_p, w_p, src, E, H, I), y)
+    # relabel: blob'[pi(e)] = blob[e], ids' = pi(ids)
+    pi = rng.permutation(E)
+    inv = np.argsort(pi)
+    y_r = O.expert_ffn(x, pi[ids].astype(np.int32), w, lambda e: src(int(inv[e])), E, H, I)
+    assert np.allclose(y_r, y, rtol=1e-14, atol=1e-300)
+
+
+def test_invalid_ids_contribute_nothing():
+    H, I, E = 64, 32, 3
+    wl = S.small_workload(H, I, E, 2, 2, wid=107)
+    src = S.expert_source(wl)
+    x = S.activations(wl, 0, 0)
+    y = O.expert_ffn(x, np.array([[1, -1], [E, 2]], np.int32), np.ones((2, 2)), src, E, H, I)
+    y1 = O.expert_ffn(x, np.array([[1], [2]], np.int32), np.ones((2, 1)), src, E, H, I)
+    assert np.array_equal(y, y1)
+
+
+# --------------------------------------------------------------------------- router
+
+def test_topk_against_python_sort_with_exact_ties():
+    rng = np.random.default_rng(11)
+    T, E, k = 40, 64, 6
+    logits = rng.standard_normal((T, E))
+    # exact ties around the selection boundary
+    logits[0, 5] = logits[0, 9] = logits[0, 40] = 10.0
+    logits[1, :] = 0.0
+    logits[2, 3] = logits[2, 60]
+    ids, w = O.topk_softmax(logits, k)
+    for t in range(T):
+        ref = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        assert list(ids[t]) == ref
+    assert list(ids[1]) == [0, 1, 2, 3, 4, 5]
+    assert list(ids[0][:3]) == [5, 9, 40]
+
+
+def test_softmax_weights_equal_renormalised_full_softmax():
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((10, 384)) * 3
+    ids, w = O.topk_softmax(logits, 6)
+    full = np.exp(logits) / np.exp(logits).sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(full, ids.astype(np.int64), 1)
+    ref = sel / sel.sum(axis=1, keepdims=True)
+    assert np.allclose(w, ref, rtol=1e-14, atol=0)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=1e-15)
+    assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_router_logits_against_exact_rational_sum():
+    rng = np.random.default_rng(13)
+    x = S.f32_to_bf16_bits(rng.standard_normal((2, 96), dtype=np.float32))
+    wr = S.f32_to_bf16_bits(0.02 * rng.standard_normal((5, 96), dtype=np.float32))
+    lg = O.router_logits(x, wr)
+    xf, wf = _bf16(x), _bf16(wr)
+    for t in range(2):
+        for e in range(5):
+            exact = sum(Fraction(float(wf[e, h])) * Fraction(float(xf[t, h])) for h in range(96))
+            assert abs(lg[t, e] - float(exact)) <= 1e-15 * max(1.0, abs(float(exact)))
+
+
+# --------------------------------------------------------------------------- bf16 helpers
+
+def test_bf16_round_trip_and_rounding_against_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(14)
+    v = np.concatenate([rng.standard_normal(2000).astype(np.float32),
+                        np.float32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 3e-39, -1e-40, 3.4e38, 0.0, -0.0])])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.f64_to_bf16_bits(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+    assert np.array_equal(O.bf16_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+    # the generator's fp32 -> bf16 rounding agrees with torch too
+    assert np.array_equal(S.f32_to_bf16_bits(v), ref)
