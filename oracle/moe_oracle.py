@@ -45,7 +45,7 @@ Readings taken where the pages are silent (each is listed with its reason in the
 from __future__ import annotations
 
 import math
-from typing import Callable, Tuple
+from typing import Callable, Optional, Tuple
 
 import numpy as np
 
@@ -135,14 +135,14 @@ def _f64_to_bf16_scalar(val: float) -> int:
     return (sign << 15) | bits
 
 
-def dequant_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+def dequant_fp4(codes: np.ndarray, scales: np.ndarray, out: Optional[np.ndarray] = None) -> np.ndarray:
     """Dequantise one FP4 matrix to fp64.
 
     codes:  uint8 [N, K/2]; byte b of a row holds element 2b in its low nibble and element
             2b+1 in its high nibble.
     scales: uint8 [N, K/32]; one ue8m0 byte per 32 consecutive elements along K.
     Returns W [N, K] with W[n, k] = E2M1_VALUES[code[n, k]] * 2**(scale[n, k // 32] - 127),
-    which is exact in fp64.
+    which is exact in fp64. ``out`` (float64 [N, K]) may be given to reuse memory.
     """
     codes = np.asarray(codes, dtype=np.uint8)
     scales = np.asarray(scales, dtype=np.uint8)
@@ -150,11 +150,16 @@ def dequant_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     k = 2 * half_k
     if scales.shape != (n, k // BLOCK) or k % BLOCK:
         raise ValueError(f"scales shape {scales.shape} does not match codes {codes.shape}")
-    nib = np.empty((n, k), dtype=np.uint8)
-    nib[:, 0::2] = codes & 0x0F
-    nib[:, 1::2] = codes >> 4
-    vals = e2m1_table()[nib]
-    return vals * np.repeat(ue8m0_to_f64(scales), BLOCK, axis=1)
+    # byte -> (value of its low nibble, value of its high nibble): element order 2b, 2b+1
+    table = e2m1_table()
+    byte = np.arange(256)
+    pair_values = np.stack([table[byte & 0x0F], table[byte >> 4]], axis=1)   # [256, 2]
+    if out is None:
+        out = np.empty((n, k), dtype=np.float64)
+    np.take(pair_values, codes, axis=0, out=out.reshape(n, half_k, 2))
+    blocks = out.reshape(n, k // BLOCK, BLOCK)
+    blocks *= ue8m0_to_f64(scales)[:, :, None]
+    return out
 
 
 # ---------------------------------------------------------------------------------------
@@ -188,9 +193,16 @@ def split_expert(codes_flat: np.ndarray, scales_flat: np.ndarray, hidden: int, i
     return out
 
 
-def dequant_expert(codes_flat: np.ndarray, scales_flat: np.ndarray, hidden: int, inter: int):
-    """Dequantised (W_gate [I,H], W_up [I,H], W_down [H,I]) of one canonical expert blob."""
-    return tuple(dequant_fp4(c, s) for c, s in split_expert(codes_flat, scales_flat, hidden, inter))
+def dequant_expert(codes_flat: np.ndarray, scales_flat: np.ndarray, hidden: int, inter: int,
+                   bufs: Optional[list] = None):
+    """Dequantised (W_gate [I,H], W_up [I,H], W_down [H,I]) of one canonical expert blob.
+    ``bufs`` (a list, filled on first use) lets consecutive calls reuse three fp64 buffers."""
+    mats = split_expert(codes_flat, scales_flat, hidden, inter)
+    if bufs is None:
+        return tuple(dequant_fp4(c, s) for c, s in mats)
+    if not bufs:
+        bufs.extend(np.empty((r, kk), dtype=np.float64) for r, kk in expert_matrix_shapes(hidden, inter))
+    return tuple(dequant_fp4(c, s, out=b) for (c, s), b in zip(mats, bufs))
 
 
 # ---------------------------------------------------------------------------------------
@@ -274,10 +286,11 @@ def expert_ffn(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, expert_source
     t_count = x.shape[0]
     y = np.zeros((t_count, hidden), dtype=np.float64)
     valid = (ids >= 0) & (ids < n_experts)
+    bufs: list = []
     # Visiting experts in ascending id makes every token's sum run in ascending id order.
     for e in np.unique(ids[valid]):
         rows_t, slots = np.nonzero(ids == e)
-        wg, wu, wd = dequant_expert(*expert_source(int(e)), hidden, inter)
+        wg, wu, wd = dequant_expert(*expert_source(int(e)), hidden, inter, bufs)
         # one token may pick the same expert twice: each (t, slot) pair adds its own term
         ye = swiglu_expert(x[rows_t], wg, wu, wd)
         for r in range(rows_t.shape[0]):
