@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed FP4 expert FFN hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: for the batch-1 decode workload
+(one 384-expert MoE layer, hidden 4096, intermediate 2880, top-6, FP4 E2M1 weights with
+ue8m0 block-32 scales) that is moe_fp4_route (router GEMV in fp64 + top-6 softmax) then
+moe_fp4_expert_ffn (gate/up/SiLU, down and the weighted combine) for one fresh token.
+Every step reads a different token's activations, already resident in HBM, so routing
+(and the experts read) changes from step to step.
+
+Prints one JSON line (the last line of stdout).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench {time.strftime('%H:%M:%S')}] {msg}\n")
+    sys.stderr.flush()
+
+
+def expert_bytes(hidden: int, inter: int) -> int:
+    n = 3 * hidden * inter
+    return n // 2 + n // 32
+
+
+def gate_up_bytes(hidden: int, inter: int) -> int:
+    n = 2 * hidden * inter
+    return n // 2 + n // 32
+
+
+def cpu_baseline(wl, n_tokens: int, first_step: int):
+    """Time the fp64 oracle (route + expert FFN) on the host for a bounded sample of the
+    same workload: n_tokens tokens, one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as O
+    from synth import moe_inputs as S
+
+    wr = S.router_weights(wl, 0)
+    xs = [S.activations(wl, 0, first_step + i) for i in range(n_tokens)]
+    # expert blobs generated up front (input preparation, not timed)
+    ids_all = [O.route(x, wr, wl.k)[0] for x in xs]
+    need = sorted(set(int(e) for ids in ids_all for e in ids.ravel()))
+    blobs = {e: S.expert_blob(wl, 0, e) for e in need}
+    src = lambda e: blobs[e]  # noqa: E731
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for x in xs:
+            ids, w, _ = O.route(x, wr, wl.k)
+            O.expert_ffn(x, ids, w, src, wl.n_experts, wl.hidden, wl.inter)
+        dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the same one-layer batch-1 decode workload "
+                      f"(route + expert FFN, fp64 NumPy, 1 thread), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--mode", choices=["graph", "stream"], default="graph")
+    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline-pass", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from fp4_expert_ffn_amd import device as D
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    from synth import moe_inputs as S
+
+    C.lib()
+    dev = torch.device("cuda:0")
+    wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
+    H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.k
+    K, W = args.steps, args.warmup
+
+    log(f"uploading {E} experts ({E * expert_bytes(H, I) / 1e9:.2f} GB)")
+    t0 = time.time()
+    packed = D.upload_experts(S.expert_source(wl, 0), E, H, I, dev, chunk=32)
+    wr = D.upload_bf16(S.router_weights(wl, 0), dev)
+    layer = D.MoeFp4Layer(packed, E, H, I, k, wr)
+    n_x = W + 2 * K
+    xs_bits = np.concatenate([S.activations(wl, 0, s) for s in range(n_x)])
+    xs = D.upload_bf16(xs_bits, dev)
+    log(f"setup done in {time.time() - t0:.1f} s")
+
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    w = torch.empty((1, k), dtype=torch.float32, device=dev)
+    y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+    layer._workspace(1)
+    layer._route_workspace(1)
+
+    def step(i: int) -> None:
+        x = xs[i:i + 1]
+        layer.route(x, ids, w)
+        layer.ffn(x, ids, w, y)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.mode == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(W, W + K):
+                step(i)
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(W, W + K):
+            step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed_s = max(gpu_ms / 1e3, 1e-9)
+    value = K / elapsed_s
+    ms_per_step = gpu_ms / K
+    step_bytes = k * expert_bytes(H, I) + E * H * 2 + 2 * H * 2
+    log(f"timed {K} steps ({args.mode}): {gpu_ms:.3f} ms GPU, {wall * 1e3:.3f} ms wall -> "
+        f"{value:.0f} layer-tokens/s, {step_bytes * K / elapsed_s / 1e9:.0f} GB/s algorithmic")
+
+    # Per-kernel durations: the library's own HIP events bracket each launch on the launch
+    # stream. A second pass over fresh tokens, stream-launched, with timing enabled.
+    roofline = None
+    kernels = {}
+    if not args.no_roofline_pass:
+        C.moe_fp4_timing_reset()
+        C.moe_fp4_timing_enable(True)
+        for i in range(W + K, W + 2 * K):
+            step(i)
+        torch.cuda.synchronize()
+        C.moe_fp4_timing_enable(False)
+        for kind, name in enumerate(C.KERNEL_NAMES):
+            n, ms = C.moe_fp4_timing_read(kind)
+            if n:
+                kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+        C.moe_fp4_timing_reset()
+        gu = kernels.get("gate_up")
+        if gu:
+            # algorithmic bytes of one gate_up launch at batch 1: the k selected experts'
+            # gate and up codes + scales, the token's x, and h (bf16) written
+            alg = k * gate_up_bytes(H, I) + H * 2 + k * I * 2
+            achieved = alg / (gu["avg_us"] * 1e-6) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None, "kernel": "gate_up", "bytes_per_launch": alg,
+                        "avg_launch_us": round(gu["avg_us"], 3)}
+        log("kernels: " + json.dumps(kernels))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(wl, args.cpu_tokens, first_step=0)
+        log(f"cpu baseline: {cpu['value']:.3f} tokens/s")
+
+    out = {
+        "metric": "MoE-layer tokens/s at batch 1 (+ achieved HBM GB/s)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
+                   "weights": "fp4-e2m1 + ue8m0/32", "batch_tokens": 1, "launch": args.mode,
+                   "parallelism": "none (1 GPU)"},
+        "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
+        "hbm_frac_step": round(step_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_step": step_bytes,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

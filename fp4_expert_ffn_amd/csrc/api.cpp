@@ -1,0 +1,256 @@
+// C ABI of the routed FP4 expert FFN library: argument checks, workspace sizing, kernel
+// dispatch on the caller's stream, and the optional kernel timing hooks.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/moe_fp4.h"
+#include "moe_fp4_internal.hpp"
+
+using namespace moe_fp4;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dim(int d) { return d > 0 && d % kBlock == 0 && d <= kMaxDim; }
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MOE_FP4_OK : MOE_FP4_ERR_HIP; }
+
+// ---------------------------------------------------------------------------------------
+// Timing: pairs of events around each launch, kept per kernel kind until read.
+// ---------------------------------------------------------------------------------------
+struct TimingState {
+  bool enabled = false;
+  struct Rec {
+    int kind;
+    hipEvent_t start, stop;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> free_events;
+  hipEvent_t pending_start = nullptr;
+  int pending_kind = -1;
+};
+
+TimingState& timing() {
+  static TimingState st;
+  return st;
+}
+
+hipEvent_t take_event() {
+  TimingState& st = timing();
+  if (!st.free_events.empty()) {
+    hipEvent_t e = st.free_events.back();
+    st.free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace moe_fp4 {
+
+void timing_begin(int kind, hipStream_t s) {
+  TimingState& st = timing();
+  if (!st.enabled) return;
+  st.pending_start = take_event();
+  st.pending_kind = kind;
+  if (st.pending_start) (void)hipEventRecord(st.pending_start, s);
+}
+
+void timing_end(int kind, hipStream_t s) {
+  TimingState& st = timing();
+  if (!st.enabled || !st.pending_start || st.pending_kind != kind) return;
+  hipEvent_t stop = take_event();
+  if (!stop) return;
+  (void)hipEventRecord(stop, s);
+  st.recs.push_back({kind, st.pending_start, stop});
+  st.pending_start = nullptr;
+}
+
+}  // namespace moe_fp4
+
+#define MOE_FP4_TIMED(KIND, STREAM, CALL) \
+  ([&]() -> hipError_t {                  \
+    timing_begin((KIND), (STREAM));       \
+    hipError_t _e = (CALL);               \
+    timing_end((KIND), (STREAM));         \
+    return _e;                            \
+  }())
+
+extern "C" {
+
+int moe_fp4_version(void) { return 100; }
+
+const char* moe_fp4_strerror(int status) {
+  switch (status) {
+    case MOE_FP4_OK: return "ok";
+    case MOE_FP4_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or k out of range)";
+    case MOE_FP4_ERR_BAD_SHAPE: return "unsupported shape (hidden/inter must be multiples of 32, at most 16384; k*inter <= 32768)";
+    case MOE_FP4_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case MOE_FP4_ERR_WORKSPACE: return "workspace or packed buffer too small";
+    case MOE_FP4_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_fp4_packed_expert_stride(int hidden, int inter) {
+  if (!valid_dim(hidden) || !valid_dim(inter)) return 0;
+  return packed_layout(hidden, inter).stride;
+}
+
+size_t moe_fp4_packed_bytes(int n_experts, int hidden, int inter) {
+  if (n_experts <= 0) return 0;
+  const size_t stride = moe_fp4_packed_expert_stride(hidden, inter);
+  return stride * (size_t)n_experts;
+}
+
+int moe_fp4_pack(const uint8_t* codes, const uint8_t* scales, int n_experts, int hidden,
+                 int inter, void* packed, size_t packed_bytes, void* stream) {
+  if (!codes || !scales || !packed || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed)) return MOE_FP4_ERR_MISALIGNED;
+  if (packed_bytes < moe_fp4_packed_bytes(n_experts, hidden, inter)) return MOE_FP4_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_PACK, s,
+                                launch_pack(codes, scales, n_experts, hidden, inter,
+                                            static_cast<uint8_t*>(packed), s)));
+}
+
+size_t moe_fp4_route_workspace_bytes(int T, int n_experts) {
+  if (T < 0 || n_experts <= 0) return 0;
+  return align256((size_t)T * (size_t)n_experts * sizeof(double));
+}
+
+static int check_topk_args(int T, int n_experts, int k) {
+  if (T < 0 || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxK || k > n_experts) return MOE_FP4_ERR_INVALID_ARG;
+  if (n_experts > kMaxExpertsTopk) return MOE_FP4_ERR_BAD_SHAPE;
+  return MOE_FP4_OK;
+}
+
+int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden, int n_experts,
+                  int k, int32_t* topk_ids, float* topk_w, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!x || !w_router || !topk_ids || !topk_w || !workspace) return MOE_FP4_ERR_INVALID_ARG;
+  int st = check_topk_args(T, n_experts, k);
+  if (st != MOE_FP4_OK) return st;
+  if (!valid_dim(hidden)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+      !aligned16(workspace))
+    return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < moe_fp4_route_workspace_bytes(T, n_experts)) return MOE_FP4_ERR_WORKSPACE;
+  if (T == 0) return MOE_FP4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* logits = static_cast<double*>(workspace);
+  hipError_t e = MOE_FP4_TIMED(MOE_FP4_KERNEL_ROUTER_GEMV, s,
+                               launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s));
+  if (e != hipSuccess) return MOE_FP4_ERR_HIP;
+  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_TOPK, s,
+                                launch_topk_f64(logits, T, n_experts, k, topk_ids, topk_w, s)));
+}
+
+int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,
+                         float* topk_w, void* stream) {
+  if (!logits || !topk_ids || !topk_w) return MOE_FP4_ERR_INVALID_ARG;
+  int st = check_topk_args(T, n_experts, k);
+  if (st != MOE_FP4_OK) return st;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_FP4_ERR_MISALIGNED;
+  if (T == 0) return MOE_FP4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_TOPK, s,
+                                launch_topk_f32(logits, T, n_experts, k, topk_ids, topk_w, s)));
+}
+
+size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
+  (void)n_experts;
+  (void)hidden;
+  if (T < 0 || k < 1 || k > kMaxK || !valid_dim(inter)) return 0;
+  // h for every (token, slot) pair, bf16
+  return align256((size_t)T * (size_t)k * (size_t)inter * 2);
+}
+
+int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int k, const void* packed, int n_experts, int hidden, int inter,
+                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !topk_ids || !topk_w || !packed || !y || !workspace) return MOE_FP4_ERR_INVALID_ARG;
+  if (T < 0 || n_experts <= 0 || k < 1 || k > kMaxK || k > n_experts) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if ((size_t)k * (size_t)inter * 2 > (size_t)kMaxLdsH) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(packed) ||
+      !aligned16(y) || !aligned16(workspace))
+    return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < moe_fp4_workspace_bytes(T, k, n_experts, hidden, inter))
+    return MOE_FP4_ERR_WORKSPACE;
+  if (T == 0) return MOE_FP4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  uint16_t* hbuf = static_cast<uint16_t*>(workspace);
+  hipError_t e = MOE_FP4_TIMED(MOE_FP4_KERNEL_GATE_UP, s,
+                               launch_gate_up(x, topk_ids, T, k, pk, n_experts, hidden, inter,
+                                              hbuf, s));
+  if (e != hipSuccess) return MOE_FP4_ERR_HIP;
+  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_DOWN_COMBINE, s,
+                                launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden,
+                                                    inter, hbuf, y, s)));
+}
+
+int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts, int32_t* bad_count,
+                         void* stream) {
+  if (!topk_ids || !bad_count || T < 0 || k < 1 || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!aligned16(topk_ids)) return MOE_FP4_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(launch_validate_ids(topk_ids, T, k, n_experts, bad_count, s));
+}
+
+int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int inter, int expert,
+                          int matrix, float* out, void* stream) {
+  if (!packed || !out || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (expert < 0 || expert >= n_experts || matrix < 0 || matrix > 2) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(packed) || !aligned16(out)) return MOE_FP4_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(launch_debug_dequant(static_cast<const uint8_t*>(packed), hidden, inter, expert,
+                                       matrix, out, s));
+}
+
+int moe_fp4_timing_enable(int enable) {
+  timing().enabled = enable != 0;
+  return MOE_FP4_OK;
+}
+
+int moe_fp4_timing_reset(void) {
+  TimingState& st = timing();
+  for (auto& r : st.recs) {
+    st.free_events.push_back(r.start);
+    st.free_events.push_back(r.stop);
+  }
+  st.recs.clear();
+  return MOE_FP4_OK;
+}
+
+int moe_fp4_timing_read(int kind, int* launches, double* total_ms) {
+  if (!launches || !total_ms || kind < 0 || kind >= MOE_FP4_KERNEL_KINDS) return MOE_FP4_ERR_INVALID_ARG;
+  TimingState& st = timing();
+  int n = 0;
+  double sum = 0.0;
+  for (auto& r : st.recs) {
+    if (r.kind != kind) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return MOE_FP4_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return MOE_FP4_ERR_HIP;
+    sum += ms;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = sum;
+  return MOE_FP4_OK;
+}
+
+}  // extern "C"

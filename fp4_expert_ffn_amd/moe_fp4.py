@@ -1,0 +1,191 @@
+"""Python binding of the C ABI in ``include/moe_fp4.h`` (ctypes, argument marshalling only).
+
+Every compute step runs in the HIP library ``libmoe_fp4.so``; this module only turns
+torch tensors (device memory) and streams into the raw pointers the C functions take,
+and raises :class:`MoeFp4Error` on a non-OK status. It fails loudly when the library has
+not been built: there is no fallback path.
+
+Functions carry the C names. Tensor arguments may also be given as raw integer device
+addresses; ``stream`` is a ``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None
+for torch's current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmoe_fp4.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_BAD_SHAPE = -2
+ERR_MISALIGNED = -3
+ERR_WORKSPACE = -4
+ERR_HIP = -5
+
+KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
+KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine")
+
+
+class MoeFp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({strerror(status)})")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_fp4_version": (_I, []),
+    "moe_fp4_strerror": (ctypes.c_char_p, [_I]),
+    "moe_fp4_packed_bytes": (_Z, [_I, _I, _I]),
+    "moe_fp4_packed_expert_stride": (_Z, [_I, _I]),
+    "moe_fp4_pack": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P]),
+    "moe_fp4_route_workspace_bytes": (_Z, [_I, _I]),
+    "moe_fp4_route": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "moe_fp4_route_logits": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_fp4_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "moe_fp4_expert_ffn": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_fp4_timing_enable": (_I, [_I]),
+    "moe_fp4_timing_reset": (_I, []),
+    "moe_fp4_timing_read": (_I, [_I, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_double)]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m fp4_expert_ffn_amd.build` "
+                "(there is no CPU fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_names() -> Tuple[str, ...]:
+    return tuple(_SIGNATURES)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise MoeFp4Error(status, where)
+
+
+def strerror(status: int) -> str:
+    return lib().moe_fp4_strerror(status).decode()
+
+
+def moe_fp4_version() -> int:
+    return lib().moe_fp4_version()
+
+
+def moe_fp4_packed_bytes(n_experts: int, hidden: int, inter: int) -> int:
+    return lib().moe_fp4_packed_bytes(n_experts, hidden, inter)
+
+
+def moe_fp4_packed_expert_stride(hidden: int, inter: int) -> int:
+    return lib().moe_fp4_packed_expert_stride(hidden, inter)
+
+
+def moe_fp4_pack(codes, scales, n_experts: int, hidden: int, inter: int, packed,
+                 packed_bytes: Optional[int] = None, stream=None) -> None:
+    if packed_bytes is None:
+        packed_bytes = packed.numel() * packed.element_size()
+    _check(lib().moe_fp4_pack(_ptr(codes), _ptr(scales), n_experts, hidden, inter, _ptr(packed),
+                              packed_bytes, _stream(stream)), "moe_fp4_pack")
+
+
+def moe_fp4_route_workspace_bytes(T: int, n_experts: int) -> int:
+    return lib().moe_fp4_route_workspace_bytes(T, n_experts)
+
+
+def moe_fp4_route(x, w_router, T: int, hidden: int, n_experts: int, k: int, topk_ids, topk_w,
+                  workspace, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_fp4_route(_ptr(x), _ptr(w_router), T, hidden, n_experts, k, _ptr(topk_ids),
+                               _ptr(topk_w), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "moe_fp4_route")
+
+
+def moe_fp4_route_logits(logits, T: int, n_experts: int, k: int, topk_ids, topk_w,
+                         stream=None) -> None:
+    _check(lib().moe_fp4_route_logits(_ptr(logits), T, n_experts, k, _ptr(topk_ids), _ptr(topk_w),
+                                      _stream(stream)), "moe_fp4_route_logits")
+
+
+def moe_fp4_workspace_bytes(T: int, k: int, n_experts: int, hidden: int, inter: int) -> int:
+    return lib().moe_fp4_workspace_bytes(T, k, n_experts, hidden, inter)
+
+
+def moe_fp4_expert_ffn(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: int, hidden: int,
+                       inter: int, y, workspace, workspace_bytes: Optional[int] = None,
+                       stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_fp4_expert_ffn(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(packed),
+                                    n_experts, hidden, inter, _ptr(y), _ptr(workspace),
+                                    workspace_bytes, _stream(stream)), "moe_fp4_expert_ffn")
+
+
+def moe_fp4_validate_ids(topk_ids, T: int, k: int, n_experts: int, bad_count, stream=None) -> None:
+    _check(lib().moe_fp4_validate_ids(_ptr(topk_ids), T, k, n_experts, _ptr(bad_count),
+                                      _stream(stream)), "moe_fp4_validate_ids")
+
+
+def moe_fp4_debug_dequant(packed, n_experts: int, hidden: int, inter: int, expert: int,
+                          matrix: int, out, stream=None) -> None:
+    _check(lib().moe_fp4_debug_dequant(_ptr(packed), n_experts, hidden, inter, expert, matrix,
+                                       _ptr(out), _stream(stream)), "moe_fp4_debug_dequant")
+
+
+def moe_fp4_timing_enable(enable: bool) -> None:
+    _check(lib().moe_fp4_timing_enable(1 if enable else 0), "moe_fp4_timing_enable")
+
+
+def moe_fp4_timing_reset() -> None:
+    _check(lib().moe_fp4_timing_reset(), "moe_fp4_timing_reset")
+
+
+def moe_fp4_timing_read(kind: int) -> Tuple[int, float]:
+    n = _I(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().moe_fp4_timing_read(kind, ctypes.byref(n), ctypes.byref(ms)), "moe_fp4_timing_read")
+    return n.value, ms.value

@@ -1,0 +1,170 @@
+/*
+ * moe_fp4.h -- C ABI of the routed FP4 expert FFN library for AMD MI355X (gfx950).
+ *
+ * The operation is the routed-expert FFN of a DeepSeek-style MoE decoder layer: every
+ * token picks k of E SwiGLU experts; each expert holds three FP4 E2M1 matrices with one
+ * ue8m0 power-of-two scale per 32 elements along K; the token's output is the
+ * router-weighted sum of its experts' outputs.
+ *
+ * Pages this follows (cited by title and section):
+ *  [A100-FP4] shi3z, "DeepSeek v4.1 Flashを動かしたくてFP4に対応していないA100を、33tok/sから
+ *             673 tok/sまで持っていって気がつくと公式APIより速くなっていた話" (note.com) and its
+ *             Chinese translation "把不支持 FP4 的 A100 拉到 673 tok/s".
+ *  [8GB-GPU]  "在 8 GB 显卡上运行 510 GB 的 DeepSeek-V4.1-Flash——以及三个从不抛错的 Bug".
+ *
+ * Conventions for every call:
+ *  - All array arguments are DEVICE pointers (hipMalloc'd or equivalent) unless stated.
+ *    The caller allocates and owns every buffer; the library allocates no device memory
+ *    and keeps no per-call state.
+ *  - bfloat16 values are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
+ *    only enqueues work on that stream and returns; none synchronises with the host, so
+ *    routing ids never travel to the host ([8GB-GPU], section 提速之路：v1 到 v4: the
+ *    per-expert host synchronisation on indices was a measured cost).
+ *  - Return value: MOE_FP4_OK (0) or a negative status below. Arguments are checked on the
+ *    host before anything is enqueued; a non-OK status means nothing was enqueued.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - T = 0 (no tokens) is a no-op that returns MOE_FP4_OK.
+ *  - Shapes: hidden and inter must be positive multiples of 32 and at most 16384;
+ *    1 <= k <= min(n_experts, 8); k * inter <= 32768 for moe_fp4_expert_ffn (the k h
+ *    vectors of a token are staged in 64 KB of LDS); every device pointer must be
+ *    16-byte aligned.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FP4_OK 0
+#define MOE_FP4_ERR_INVALID_ARG (-1)   /* null pointer, negative size, k out of range */
+#define MOE_FP4_ERR_BAD_SHAPE (-2)     /* hidden or inter not a multiple of 32 / too large */
+#define MOE_FP4_ERR_MISALIGNED (-3)    /* a device pointer is not 16-byte aligned */
+#define MOE_FP4_ERR_WORKSPACE (-4)     /* workspace or packed buffer smaller than required */
+#define MOE_FP4_ERR_HIP (-5)           /* a HIP launch or runtime call failed */
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int moe_fp4_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* moe_fp4_strerror(int status);
+
+/* ------------------------------------------------------------------------------------
+ * Expert weights: canonical blob and packed device layout.
+ *
+ * Canonical blob of one expert ([8GB-GPU], section 方案：不重写模型，只迁移其存储: the three
+ * matrices of an expert lie next to each other, the scales are a separate block;
+ * section 每 token 字节数决定一切: 17.93 MiB per expert at hidden 4096, inter 2880):
+ *   codes : gate [inter x hidden/2] | up [inter x hidden/2] | down [hidden x inter/2]
+ *           uint8, row-major [out x in]; a byte holds two E2M1 codes, the low nibble is
+ *           the even K index. E2M1: bit 3 sign, bits 2:1 exponent (bias 1), bit 0
+ *           mantissa ([A100-FP4], section 「FP4非対応」という言葉を疑う).
+ *   scales: gate [inter x hidden/32] | up [inter x hidden/32] | down [hidden x inter/32]
+ *           uint8 ue8m0: byte e scales its 32-element K block by 2^(e-127); e = 255 is NaN.
+ * For n_experts experts the canonical arrays are codes [E][3*hidden*inter/2] and
+ * scales [E][3*hidden*inter/32], expert after expert.
+ * ------------------------------------------------------------------------------------ */
+
+/* Bytes of the packed device layout for n_experts experts (0 if the shape is invalid). */
+size_t moe_fp4_packed_bytes(int n_experts, int hidden, int inter);
+
+/* Byte distance between consecutive experts in the packed layout (a multiple of 256), so
+ * that a caller can pack a large expert set one expert (or one chunk) at a time by passing
+ * packed + e * stride. 0 if the shape is invalid. */
+size_t moe_fp4_packed_expert_stride(int hidden, int inter);
+
+/* Load-time re-layout ([A100-FP4], section 但 CPU 也没那么快: weights are rearranged once at
+ * load time into the order the compute kernels read best).
+ * codes, scales: canonical arrays for n_experts experts (device).
+ * packed: destination of at least moe_fp4_packed_bytes(n_experts, hidden, inter) bytes.
+ * Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE (packed_bytes too small), HIP. */
+int moe_fp4_pack(const uint8_t* codes, const uint8_t* scales, int n_experts, int hidden,
+                 int inter, void* packed, size_t packed_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Routing ([8GB-GPU], section 每 token 字节数决定一切: 6 of 384 experts per token).
+ * logits[t, e] = sum_h w_router[e, h] * x[t, h], accumulated in fp64; the k largest
+ * logits of each token are returned in descending order, equal logits ordered by
+ * ascending expert id; topk_w[t, j] = softmax over the token's k selected logits
+ * (equivalently the full softmax renormalised over the selection).
+ * ------------------------------------------------------------------------------------ */
+
+/* Workspace bytes moe_fp4_route needs for T tokens and n_experts experts. */
+size_t moe_fp4_route_workspace_bytes(int T, int n_experts);
+
+/* x [T x hidden] bf16, w_router [n_experts x hidden] bf16 (row-major), outputs
+ * topk_ids int32 [T x k], topk_w fp32 [T x k]. workspace: device scratch of at least
+ * moe_fp4_route_workspace_bytes(T, n_experts) bytes (contents on entry are ignored).
+ * Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, HIP. */
+int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden, int n_experts,
+                  int k, int32_t* topk_ids, float* topk_w, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* The selection and weighting of moe_fp4_route applied to given fp32 logits
+ * [T x n_experts] (for workloads whose router logits are drawn directly). No workspace. */
+int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,
+                         float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Routed expert FFN with the router-weighted combine.
+ * For every token t and slot j with e = topk_ids[t, j] in [0, n_experts):
+ *   g = W_gate[e] x_t, u = W_up[e] x_t, h = silu(g) * u, y_e = W_down[e] h,
+ * and y[t] = sum_j topk_w[t, j] * y_e, summed in ascending expert id (so permuting a
+ * token's (id, weight) pairs does not change the result). Ids outside [0, n_experts)
+ * contribute nothing; duplicate ids add up; weights are used as given.
+ * Numerics: FP4 weights are dequantised exactly in registers, products and sums are fp32,
+ * h is rounded to bf16 before the down projection, y is rounded to bf16.
+ * ------------------------------------------------------------------------------------ */
+
+/* Workspace bytes moe_fp4_expert_ffn needs. */
+size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter);
+
+/* x [T x hidden] bf16; topk_ids int32 [T x k]; topk_w fp32 [T x k];
+ * packed: the output of moe_fp4_pack for n_experts experts; y [T x hidden] bf16 (output,
+ * may not alias x); workspace of at least moe_fp4_workspace_bytes(...) bytes.
+ * Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, HIP. */
+int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int k, const void* packed, int n_experts, int hidden, int inter,
+                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug helper: counts the entries of topk_ids [T x k] outside [0, n_experts) into
+ * *bad_count (a device int32 that this call overwrites). */
+int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,
+                         int32_t* bad_count, void* stream);
+
+/* Debug helper: dequantises matrix `matrix` (0 gate, 1 up, 2 down) of expert `expert` of
+ * a packed buffer to fp32 out [rows x K] (gate/up: [inter x hidden], down: [hidden x
+ * inter]) with the same in-register decode the FFN kernels use:
+ * out = E2M1(code) * 2^(e-127), exact in fp32 unless it overflows (NaN for e = 255).
+ * Errors: INVALID_ARG (null, expert or matrix out of range), BAD_SHAPE, MISALIGNED, HIP. */
+int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int inter, int expert,
+                          int matrix, float* out, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Built-in kernel timing, for measurement. When enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events on the launch stream (host-side event
+ * objects created here; no device memory). moe_fp4_timing_read synchronises on the
+ * recorded events and returns, for one kernel kind, the number of launches and the
+ * summed GPU time in milliseconds since the last reset. Kinds are the MOE_FP4_KERNEL_*
+ * values. Not thread-safe; meant for single-threaded benchmarks.
+ * ------------------------------------------------------------------------------------ */
+#define MOE_FP4_KERNEL_PACK 0
+#define MOE_FP4_KERNEL_ROUTER_GEMV 1
+#define MOE_FP4_KERNEL_TOPK 2
+#define MOE_FP4_KERNEL_GATE_UP 3
+#define MOE_FP4_KERNEL_DOWN_COMBINE 4
+#define MOE_FP4_KERNEL_KINDS 5
+
+int moe_fp4_timing_enable(int enable);
+int moe_fp4_timing_reset(void);
+int moe_fp4_timing_read(int kind, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

@@ -1,0 +1,124 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before any HIP call (fake, never
+dereferenced pointer values are used, so no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_expert_ffn_amd import moe_fp4 as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp4.h")
+
+A = 0x10000  # an aligned fake device address (never dereferenced)
+MIS = 0x10008  # misaligned
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_fp4_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return C.lib()
+    except RuntimeError as e:  # not built yet
+        pytest.fail(str(e))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(C.exported_names())
+
+
+def test_status_strings_and_version(L):
+    assert C.moe_fp4_version() >= 100
+    for st in (0, -1, -2, -3, -4, -5):
+        assert C.strerror(st)
+    assert C.strerror(-99) == "unknown status"
+
+
+def test_packed_sizes():
+    stride = C.moe_fp4_packed_expert_stride(4096, 2880)
+    assert stride == 18_800_640 and stride % 256 == 0
+    assert C.moe_fp4_packed_bytes(384, 4096, 2880) == 384 * stride
+    assert C.moe_fp4_packed_expert_stride(256, 128) == 3 * 256 * 128 // 2 + 3 * 256 * 128 // 32
+    assert C.moe_fp4_packed_expert_stride(100, 128) == 0
+    assert C.moe_fp4_packed_bytes(0, 4096, 2880) == 0
+
+
+def test_workspace_sizes():
+    assert C.moe_fp4_workspace_bytes(1, 6, 384, 4096, 2880) >= 6 * 2880 * 2
+    assert C.moe_fp4_workspace_bytes(8192, 6, 384, 4096, 2880) >= 8192 * 6 * 2880 * 2
+    assert C.moe_fp4_route_workspace_bytes(1, 384) >= 384 * 8
+
+
+def ffn(L, x=A, ids=A, w=A, T=1, k=6, packed=A, E=384, H=4096, I=2880, y=A, ws=A, wsb=1 << 20):
+    return L.moe_fp4_expert_ffn(x, ids, w, T, k, packed, E, H, I, y, ws, wsb, None)
+
+
+def test_expert_ffn_argument_checks(L):
+    assert ffn(L, x=None) == C.ERR_INVALID_ARG
+    assert ffn(L, y=None) == C.ERR_INVALID_ARG
+    assert ffn(L, ws=None) == C.ERR_INVALID_ARG
+    assert ffn(L, T=-1) == C.ERR_INVALID_ARG
+    assert ffn(L, k=0) == C.ERR_INVALID_ARG
+    assert ffn(L, k=9) == C.ERR_INVALID_ARG
+    assert ffn(L, k=4, E=3) == C.ERR_INVALID_ARG
+    assert ffn(L, H=4010) == C.ERR_BAD_SHAPE
+    assert ffn(L, I=2881) == C.ERR_BAD_SHAPE
+    assert ffn(L, H=16384 + 32) == C.ERR_BAD_SHAPE
+    assert ffn(L, k=8, I=8192) == C.ERR_BAD_SHAPE          # k * inter > 32768
+    assert ffn(L, x=MIS) == C.ERR_MISALIGNED
+    assert ffn(L, packed=MIS) == C.ERR_MISALIGNED
+    assert ffn(L, wsb=100) == C.ERR_WORKSPACE
+    # T = 0 is a no-op: OK without touching any pointer
+    assert ffn(L, T=0, wsb=0) == C.OK
+
+
+def test_route_argument_checks(L):
+    def route(x=A, wr=A, T=1, H=4096, E=384, k=6, ids=A, w=A, ws=A, wsb=1 << 20):
+        return L.moe_fp4_route(x, wr, T, H, E, k, ids, w, ws, wsb, None)
+    assert route(wr=None) == C.ERR_INVALID_ARG
+    assert route(k=0) == C.ERR_INVALID_ARG
+    assert route(k=7, E=6) == C.ERR_INVALID_ARG
+    assert route(E=4096) == C.ERR_BAD_SHAPE
+    assert route(H=31) == C.ERR_BAD_SHAPE
+    assert route(ids=MIS) == C.ERR_MISALIGNED
+    assert route(wsb=8) == C.ERR_WORKSPACE
+    assert route(T=0) == C.OK
+    assert L.moe_fp4_route_logits(A, 0, 384, 6, A, A, None) == C.OK
+    assert L.moe_fp4_route_logits(None, 1, 384, 6, A, A, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_route_logits(A, 1, 384, 9, A, A, None) == C.ERR_INVALID_ARG
+
+
+def test_pack_and_debug_argument_checks(L):
+    assert L.moe_fp4_pack(None, A, 1, 256, 128, A, 1 << 30, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_pack(A, A, 0, 256, 128, A, 1 << 30, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_pack(A, A, 1, 250, 128, A, 1 << 30, None) == C.ERR_BAD_SHAPE
+    assert L.moe_fp4_pack(A, MIS, 1, 256, 128, A, 1 << 30, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_pack(A, A, 2, 256, 128, A, 1000, None) == C.ERR_WORKSPACE
+    assert L.moe_fp4_debug_dequant(A, 2, 256, 128, 2, 0, A, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_debug_dequant(A, 2, 256, 128, 0, 3, A, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_validate_ids(None, 1, 6, 384, A, None) == C.ERR_INVALID_ARG
+
+
+def test_timing_read_without_records(L):
+    C.moe_fp4_timing_reset()
+    assert C.moe_fp4_timing_read(C.KERNEL_GATE_UP) == (0, 0.0)
+    with pytest.raises(C.MoeFp4Error):
+        C.moe_fp4_timing_read(99)
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        C.moe_fp4_expert_ffn(torch.zeros(4), A, A, 1, 6, A, 384, 4096, 2880, A, A, 1 << 20, stream=0)

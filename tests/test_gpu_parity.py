@@ -1,0 +1,333 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: router ids bit-exact (same order), router weights within 2^-22 relative, dequantised
+weights bit-exact in fp32, FFN outputs per token within normwise relative error 2e-2 and
+cosine >= 0.9995, repeated runs bit-identical.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synth import moe_inputs as S
+from tests.gpu_helpers import check_ffn, check_route, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    C.lib()  # fail loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+def _mods():
+    from fp4_expert_ffn_amd import device as D
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    return C, D
+
+
+def _layer(wl, dev, layer=0):
+    C, D = _mods()
+    packed = D.upload_experts(S.expert_source(wl, layer), wl.n_experts, wl.hidden, wl.inter, dev)
+    wr = D.upload_bf16(S.router_weights(wl, layer), dev)
+    return D.MoeFp4Layer(packed, wl.n_experts, wl.hidden, wl.inter, wl.k, wr)
+
+
+def _random_routing(rng, T, k, E, distinct=True):
+    if distinct:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    else:
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32) + np.float32(0.05)
+    return ids, w
+
+
+def _run_ffn(layer, x_bits, ids, w, dev):
+    _, D = _mods()
+    x = D.upload_bf16(x_bits, dev)
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev)
+    w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev)
+    y = layer.ffn(x, ids_d, w_d)
+    torch.cuda.synchronize()
+    return D.bf16_bits(y)
+
+
+# ------------------------------------------------------------------------------ dequant
+
+def test_dequant_all_codes_and_scales_bit_exact(dev):
+    C, D = _mods()
+    H, I = 256, 128
+    # gate: 1024 blocks; block b has bytes 16b..16b+15 (mod 256): every low nibble 0..15,
+    # and scale byte b mod 256: every (code, scale) pair occurs.
+    n = I * H // 2
+    gate_codes = (np.arange(n) % 256).astype(np.uint8)
+    gate_scales = (np.arange(I * H // 32) % 256).astype(np.uint8)
+    rng = np.random.default_rng(3)
+    codes = np.concatenate([gate_codes, rng.integers(0, 256, 2 * n, dtype=np.uint8)])
+    scales = np.concatenate([gate_scales, rng.integers(0, 255, 2 * I * H // 32, dtype=np.uint8)])
+    packed = D.upload_experts(lambda e: (codes, scales), 1, H, I, dev)
+    mats = O.split_expert(codes, scales, H, I)
+    for m, (c, s) in enumerate(mats):
+        out = torch.empty(c.shape[0] * c.shape[1] * 2, dtype=torch.float32, device=dev)
+        C.moe_fp4_debug_dequant(packed, 1, H, I, 0, m, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(c.shape[0], -1)
+        ref = O.dequant_fp4(c, s).astype(np.float32)
+        nan_g, nan_r = np.isnan(got), np.isnan(ref)
+        assert np.array_equal(nan_g, nan_r), f"matrix {m}: NaN positions differ"
+        gb, rb = got.view(np.uint32)[~nan_g], ref.view(np.uint32)[~nan_r]
+        bad = np.nonzero(gb != rb)[0]
+        assert bad.size == 0, f"matrix {m}: {bad.size} mismatches, first {got[~nan_g][bad[:4]]} vs {ref[~nan_r][bad[:4]]}"
+    log("dequant: all 16 codes x 256 scale bytes bit-exact")
+
+
+@pytest.mark.parametrize("H,I,E", [(256, 128, 3), (4096, 2880, 2), (320, 96, 4)])
+def test_pack_round_trip_bit_exact(dev, H, I, E):
+    C, D = _mods()
+    wl = S.small_workload(H, I, E, 1, 1, wid=201)
+    packed = D.upload_experts(S.expert_source(wl), E, H, I, dev, chunk=2)
+    for e in range(E):
+        mats = O.split_expert(*S.expert_blob(wl, 0, e), H, I)
+        for m, (c, s) in enumerate(mats):
+            out = torch.empty(c.shape[0] * c.shape[1] * 2, dtype=torch.float32, device=dev)
+            C.moe_fp4_debug_dequant(packed, E, H, I, e, m, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().reshape(c.shape[0], -1)
+            assert np.array_equal(got, O.dequant_fp4(c, s).astype(np.float32)), (e, m)
+
+
+# ------------------------------------------------------------------------------ router
+
+def test_route_ids_bit_exact_full_size(dev):
+    C, D = _mods()
+    wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
+    wr_bits = S.router_weights(wl, 0)
+    # exact ties: rows 12 and 300 equal row 7; token 0 points along row 7
+    wr_bits[12] = wr_bits[7]
+    wr_bits[300] = wr_bits[7]
+    T = 256
+    x_bits = np.concatenate([S.activations(wl, 0, s) for s in range(T)])
+    x_bits[0] = wr_bits[7]
+    ids_ref, w_ref, _ = O.route(x_bits, wr_bits, wl.k)
+    assert list(ids_ref[0][:3]) == [7, 12, 300]
+    layer = D.MoeFp4Layer(torch.empty(256, dtype=torch.uint8, device=dev), wl.n_experts,
+                          wl.hidden, wl.inter, wl.k, D.upload_bf16(wr_bits, dev))
+    ids, w = layer.route(D.upload_bf16(x_bits, dev))
+    torch.cuda.synchronize()
+    check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, "route")
+
+
+@pytest.mark.parametrize("routing", ["zipf", "uniform", "ties"])
+def test_route_logits_bit_exact(dev, routing):
+    C, D = _mods()
+    if routing == "ties":
+        wl = S.WORKLOADS["batched64_zipf"]
+        lg = S.router_logits(wl, 0, 0, tokens=300)
+        lg = np.round(lg * 2) / 2  # many exact ties
+        lg[0, :] = 0.0
+        lg = lg.astype(np.float32)
+    else:
+        wl = S.WORKLOADS["batched64_zipf" if routing == "zipf" else "prefill8192_uniform"]
+        lg = S.router_logits(wl, 0, 0, tokens=1000)
+    T = lg.shape[0]
+    ids_ref, w_ref = O.topk_softmax(lg.astype(np.float64), 6)
+    layer = D.MoeFp4Layer(torch.empty(256, dtype=torch.uint8, device=dev), 384, 4096, 2880, 6)
+    ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
+    torch.cuda.synchronize()
+    check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, routing)
+    if routing == "ties":
+        assert list(ids.cpu().numpy()[0]) == [0, 1, 2, 3, 4, 5]
+
+
+# ------------------------------------------------------------------------------ FFN
+
+def test_single_expert_h256_i128(dev):
+    wl = S.WORKLOADS["expert_h256_i128"]
+    layer = _layer(wl, dev)
+    x_bits = S.activations(wl, 0, 0)
+    ids = np.zeros((1, 1), np.int32)
+    w = np.ones((1, 1), np.float32)
+    y = _run_ffn(layer, x_bits, ids, w, dev)
+    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), 1, 256, 128)
+    err, cos = check_ffn(y, ref, "expert_h256_i128")
+    log(f"single expert: normwise {err:.2e} cosine {cos:.7f}")
+
+
+SMALL_SHAPES = [
+    # H, I, E, k, T: row maps (LPR, BPL) for K = H and K = I, ragged tails
+    (64, 32, 4, 2, 3),
+    (320, 96, 5, 3, 7),
+    (512, 2880, 8, 6, 5),
+    (4096, 256, 7, 6, 2),
+    (7168, 512, 4, 4, 2),
+    (16384, 64, 3, 2, 2),
+    (96, 16384, 3, 2, 2),
+    (1024, 1024, 16, 8, 17),
+]
+
+
+@pytest.mark.parametrize("H,I,E,k,T", SMALL_SHAPES)
+def test_ffn_small_shapes(dev, H, I, E, k, T):
+    wl = S.small_workload(H, I, E, k, T, wid=300 + H % 97 + I % 89)
+    layer = _layer(wl, dev)
+    rng = np.random.default_rng(H * 7 + I)
+    ids, w = _random_routing(rng, T, k, E)
+    x_bits = S.activations(wl, 0, 0)
+    y = _run_ffn(layer, x_bits, ids, w, dev)
+    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), E, H, I)
+    err, cos = check_ffn(y, ref, f"H{H} I{I} E{E} k{k} T{T}")
+    log(f"H{H} I{I} E{E} k{k} T{T}: normwise {err:.2e} cosine {cos:.7f}")
+
+
+@pytest.fixture(scope="module")
+def decode_layer(dev):
+    wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
+    log("uploading 384 experts (7.2 GB)")
+    return wl, _layer(wl, dev)
+
+
+def test_layer_decode_full_size_route_and_ffn(dev, decode_layer):
+    """One 384-expert layer at full size, batch 1, token by token: route on the GPU (ids
+    bit-exact against the oracle) then the expert FFN (tolerance against the oracle)."""
+    _, D = _mods()
+    wl, layer = decode_layer
+    n_tok = 16
+    wr_bits = S.router_weights(wl, 0)
+    src = S.expert_source(wl)
+    for s in range(n_tok):
+        x_bits = S.activations(wl, 0, s)
+        x = D.upload_bf16(x_bits, dev)
+        y, ids, w = layer.forward(x)
+        torch.cuda.synchronize()
+        ids_ref, w_ref, _ = O.route(x_bits, wr_bits, wl.k)
+        check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"token {s}")
+        ref = O.expert_ffn(x_bits, ids_ref, w_ref, src, wl.n_experts, wl.hidden, wl.inter)
+        err, cos = check_ffn(D.bf16_bits(y), ref, f"token {s}")
+        if s % 4 == 0:
+            log(f"decode token {s}: normwise {err:.2e} cosine {cos:.7f}")
+
+
+def test_layer_batched64_zipf_full_size(dev, decode_layer):
+    """64 tokens per step through the 384-expert layer, Zipf(1.1)-skewed logits."""
+    _, D = _mods()
+    wl_l, layer = decode_layer
+    wl = S.WORKLOADS["batched64_zipf"]
+    lg = S.router_logits(wl, 0, 0)
+    ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
+    ids_ref, w_ref = O.topk_softmax(lg.astype(np.float64), 6)
+    torch.cuda.synchronize()
+    check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, "zipf64")
+    x_bits = S.activations(wl, 0, 0)
+    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w)
+    torch.cuda.synchronize()
+    # the layer holds the decode workload's experts
+    ref = O.expert_ffn(x_bits, ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
+    err, cos = check_ffn(D.bf16_bits(y), ref, "zipf64")
+    log(f"batched64 zipf: {len(np.unique(ids_ref))} distinct experts, normwise {err:.2e} cosine {cos:.7f}")
+
+
+def test_layer_prefill8192_sampled(dev, decode_layer):
+    """8192 tokens with uniform logits; the oracle checks a seeded sample of tokens."""
+    _, D = _mods()
+    wl_l, layer = decode_layer
+    wl = S.WORKLOADS["prefill8192_uniform"]
+    lg = S.router_logits(wl, 0, 0)
+    ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
+    x_bits = S.activations(wl, 0, 0)
+    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w)
+    torch.cuda.synchronize()
+    sample = np.sort(np.random.default_rng(55).choice(8192, size=24, replace=False))
+    ids_ref, w_ref = O.topk_softmax(lg[sample].astype(np.float64), 6)
+    check_route(ids.cpu().numpy()[sample], w.cpu().numpy()[sample], ids_ref, w_ref, "prefill")
+    ref = O.expert_ffn(x_bits[sample], ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
+    err, cos = check_ffn(D.bf16_bits(y)[sample], ref, "prefill8192")
+    log(f"prefill8192 sample of 24: normwise {err:.2e} cosine {cos:.7f}")
+
+
+# ------------------------------------------------------------------------------ edge cases
+
+@pytest.fixture(scope="module")
+def small_layer(dev):
+    wl = S.small_workload(512, 384, 12, 6, 1, wid=400)
+    return wl, _layer(wl, dev)
+
+
+def test_t0_is_a_no_op(dev, small_layer):
+    C, D = _mods()
+    wl, layer = small_layer
+    y = torch.full((1, wl.hidden), 7, dtype=torch.int16, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    x = torch.zeros((1, wl.hidden), dtype=torch.int16, device=dev)
+    ids = torch.zeros((1, 6), dtype=torch.int32, device=dev)
+    w = torch.zeros((1, 6), dtype=torch.float32, device=dev)
+    C.moe_fp4_expert_ffn(x, ids, w, 0, 6, layer.packed, wl.n_experts, wl.hidden, wl.inter, y, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7)
+
+
+def test_invalid_and_duplicate_ids(dev, small_layer):
+    C, D = _mods()
+    wl, layer = small_layer
+    E = wl.n_experts
+    ids = np.array([[3, -1, 5, E, 1000, 2],
+                    [4, 4, 4, 1, 1, 0],
+                    [-5, -1, E, E + 1, 99, 2 ** 31 - 1]], np.int32)
+    w = np.random.default_rng(9).random((3, 6)).astype(np.float32)
+    x_bits = S.activations(wl, 0, 1, tokens=3)
+    y = _run_ffn(layer, x_bits, ids, w, dev)
+    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), E, wl.hidden, wl.inter)
+    check_ffn(y[:2], ref[:2], "invalid/duplicate ids")
+    assert np.all(O.bf16_to_f64(y[2]) == 0.0)  # no valid id: exactly zero
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    C.moe_fp4_validate_ids(torch.from_numpy(ids).to(dev), 3, 6, E, bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == int(np.sum((ids < 0) | (ids >= E)))
+
+
+@pytest.mark.parametrize("k", [1, 8])
+def test_k_extremes(dev, small_layer, k):
+    wl, layer = small_layer
+    rng = np.random.default_rng(10 + k)
+    ids, w = _random_routing(rng, 5, k, wl.n_experts)
+    x_bits = S.activations(wl, 0, 2, tokens=5)
+    y = _run_ffn(layer, x_bits, ids, w, dev)
+    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
+    check_ffn(y, ref, f"k={k}")
+
+
+def test_slot_permutation_is_bit_identical(dev, small_layer):
+    wl, layer = small_layer
+    rng = np.random.default_rng(11)
+    T = 9
+    ids, w = _random_routing(rng, T, 6, wl.n_experts)
+    ids[0, 1] = ids[0, 0]  # a duplicate id with its own weight
+    x_bits = S.activations(wl, 0, 3, tokens=T)
+    y0 = _run_ffn(layer, x_bits, ids, w, dev)
+    for trial in range(3):
+        perm = np.stack([rng.permutation(6) for _ in range(T)])
+        y1 = _run_ffn(layer, x_bits, np.take_along_axis(ids, perm, 1), np.take_along_axis(w, perm, 1), dev)
+        assert np.array_equal(y0, y1), f"trial {trial}"
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 300, 1024])
+def test_row_counts_and_repeat_determinism(dev, small_layer, T):
+    """Same input five times: bit-identical outputs and no NaN/Inf, at token counts on both
+    sides of 64."""
+    wl, layer = small_layer
+    rng = np.random.default_rng(T)
+    ids, w = _random_routing(rng, T, 6, wl.n_experts)
+    x_bits = S.activations(wl, 0, 4, tokens=T)
+    outs = [_run_ffn(layer, x_bits, ids, w, dev) for _ in range(5)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert np.all(np.isfinite(O.bf16_to_f64(outs[0])))
+    sample = np.unique(np.linspace(0, T - 1, min(T, 8)).astype(int))
+    ref = O.expert_ffn(x_bits[sample], ids[sample], w[sample], S.expert_source(wl), wl.n_experts,
+                       wl.hidden, wl.inter)
+    check_ffn(outs[0][sample], ref, f"T={T}")
