@@ -75,6 +75,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=["graph", "stream"], default="graph")
+    ap.add_argument("--api", choices=["fused", "split"], default="fused",
+                    help="fused: moe_fp4_moe_forward (3 launches); split: moe_fp4_route + "
+                         "moe_fp4_expert_ffn (4 launches)")
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
@@ -112,11 +115,15 @@ def main() -> int:
     y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
     layer._workspace(1)
     layer._route_workspace(1)
+    layer._forward_workspace(1)
 
     def step(i: int) -> None:
         x = xs[i:i + 1]
-        layer.route(x, ids, w)
-        layer.ffn(x, ids, w, y)
+        if args.api == "fused":
+            layer.forward_fused(x, ids, w, y)
+        else:
+            layer.route(x, ids, w)
+            layer.ffn(x, ids, w, y)
 
     for i in range(W):
         step(i)
@@ -203,7 +210,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
-                   "weights": "fp4-e2m1 + ue8m0/32", "batch_tokens": 1, "launch": args.mode,
+                   "weights": "fp4-e2m1 + ue8m0/32", "batch_tokens": 1, "launch": args.mode, "api": args.api,
                    "parallelism": "none (1 GPU)"},
         "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
         "hbm_frac_step": round(step_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),

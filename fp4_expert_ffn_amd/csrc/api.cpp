@@ -31,8 +31,6 @@ struct TimingState {
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> free_events;
-  hipEvent_t pending_start = nullptr;
-  int pending_kind = -1;
 };
 
 TimingState& timing() {
@@ -56,33 +54,23 @@ hipEvent_t take_event() {
 
 namespace moe_fp4 {
 
-void timing_begin(int kind, hipStream_t s) {
+bool timing_slot(int kind, hipEvent_t* start, hipEvent_t* stop) {
   TimingState& st = timing();
-  if (!st.enabled) return;
-  st.pending_start = take_event();
-  st.pending_kind = kind;
-  if (st.pending_start) (void)hipEventRecord(st.pending_start, s);
-}
-
-void timing_end(int kind, hipStream_t s) {
-  TimingState& st = timing();
-  if (!st.enabled || !st.pending_start || st.pending_kind != kind) return;
-  hipEvent_t stop = take_event();
-  if (!stop) return;
-  (void)hipEventRecord(stop, s);
-  st.recs.push_back({kind, st.pending_start, stop});
-  st.pending_start = nullptr;
+  if (!st.enabled) return false;
+  hipEvent_t a = take_event();
+  if (!a) return false;
+  hipEvent_t b = take_event();
+  if (!b) {
+    st.free_events.push_back(a);
+    return false;
+  }
+  st.recs.push_back({kind, a, b});
+  *start = a;
+  *stop = b;
+  return true;
 }
 
 }  // namespace moe_fp4
-
-#define MOE_FP4_TIMED(KIND, STREAM, CALL) \
-  ([&]() -> hipError_t {                  \
-    timing_begin((KIND), (STREAM));       \
-    hipError_t _e = (CALL);               \
-    timing_end((KIND), (STREAM));         \
-    return _e;                            \
-  }())
 
 extern "C" {
 
@@ -118,8 +106,7 @@ int moe_fp4_pack(const uint8_t* codes, const uint8_t* scales, int n_experts, int
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed)) return MOE_FP4_ERR_MISALIGNED;
   if (packed_bytes < moe_fp4_packed_bytes(n_experts, hidden, inter)) return MOE_FP4_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_PACK, s,
-                                launch_pack(codes, scales, n_experts, hidden, inter,
+  return from_hip((launch_pack(codes, scales, n_experts, hidden, inter,
                                             static_cast<uint8_t*>(packed), s)));
 }
 
@@ -149,11 +136,9 @@ int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden
   if (T == 0) return MOE_FP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* logits = static_cast<double*>(workspace);
-  hipError_t e = MOE_FP4_TIMED(MOE_FP4_KERNEL_ROUTER_GEMV, s,
-                               launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s));
+  hipError_t e = (launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s));
   if (e != hipSuccess) return MOE_FP4_ERR_HIP;
-  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_TOPK, s,
-                                launch_topk_f64(logits, T, n_experts, k, topk_ids, topk_w, s)));
+  return from_hip((launch_topk_f64(logits, T, n_experts, k, topk_ids, topk_w, s)));
 }
 
 int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,
@@ -164,8 +149,7 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
   if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_FP4_ERR_MISALIGNED;
   if (T == 0) return MOE_FP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_TOPK, s,
-                                launch_topk_f32(logits, T, n_experts, k, topk_ids, topk_w, s)));
+  return from_hip((launch_topk_f32(logits, T, n_experts, k, topk_ids, topk_w, s)));
 }
 
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
@@ -192,13 +176,48 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* pk = static_cast<const uint8_t*>(packed);
   uint16_t* hbuf = static_cast<uint16_t*>(workspace);
-  hipError_t e = MOE_FP4_TIMED(MOE_FP4_KERNEL_GATE_UP, s,
-                               launch_gate_up(x, topk_ids, T, k, pk, n_experts, hidden, inter,
-                                              hbuf, s));
+  hipError_t e = launch_gate_up(x, topk_ids, nullptr, T, k, nullptr, nullptr, pk, n_experts,
+                                hidden, inter, hbuf, s);
   if (e != hipSuccess) return MOE_FP4_ERR_HIP;
-  return from_hip(MOE_FP4_TIMED(MOE_FP4_KERNEL_DOWN_COMBINE, s,
-                                launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden,
+  return from_hip((launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden,
                                                     inter, hbuf, y, s)));
+}
+
+size_t moe_fp4_moe_forward_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
+  if (T < 0 || n_experts <= 0) return 0;
+  const size_t ffn = moe_fp4_workspace_bytes(T, k, n_experts, hidden, inter);
+  if (ffn == 0) return 0;
+  return moe_fp4_route_workspace_bytes(T, n_experts) + ffn;
+}
+
+int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int hidden,
+                        int n_experts, int k, const void* packed, int inter, int32_t* topk_ids,
+                        float* topk_w, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!x || !w_router || !packed || !topk_ids || !topk_w || !y || !workspace)
+    return MOE_FP4_ERR_INVALID_ARG;
+  int st = check_topk_args(T, n_experts, k);
+  if (st != MOE_FP4_OK) return st;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if ((size_t)k * (size_t)inter * 2 > (size_t)kMaxLdsH) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(packed) || !aligned16(topk_ids) ||
+      !aligned16(topk_w) || !aligned16(y) || !aligned16(workspace))
+    return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < moe_fp4_moe_forward_workspace_bytes(T, k, n_experts, hidden, inter))
+    return MOE_FP4_ERR_WORKSPACE;
+  if (T == 0) return MOE_FP4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  double* logits = static_cast<double*>(workspace);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) +
+                                               moe_fp4_route_workspace_bytes(T, n_experts));
+  if (launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s) != hipSuccess)
+    return MOE_FP4_ERR_HIP;
+  if (launch_gate_up(x, nullptr, logits, T, k, topk_ids, topk_w, pk, n_experts, hidden, inter,
+                     hbuf, s) != hipSuccess)
+    return MOE_FP4_ERR_HIP;
+  return from_hip(launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, hbuf,
+                                      y, s));
 }
 
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts, int32_t* bad_count,

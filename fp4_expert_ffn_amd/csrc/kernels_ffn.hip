@@ -1,18 +1,24 @@
-// Routed expert FFN, GEMV form: every (token, slot) pair streams its expert's rows.
+// Routed expert FFN, one (token, slot) pair at a time, on the bf16 matrix cores.
 //
-// Stage 1 (gate_up): g = W_gate[e] x, u = W_up[e] x, h = silu(g) * u, for every pair
-//   (t, j) with a valid id; h is written as bf16 to the workspace, natural order [pair][I].
-// Stage 2 (down_combine): for every token t and output row n,
-//   y[t, n] = sum over the token's valid slots, in ascending expert id, of
-//             w_j * (W_down[e_j] h_j)[n],
-//   with the k h vectors of the token staged in LDS; y is written as bf16.
+// Stage 1 (gate_up): g = W_gate[e] x, u = W_up[e] x, h = silu(g) * u for every pair
+//   (t, j) with a valid id; h goes to the workspace as bf16, natural order [pair][I].
+// Stage 2 (down_combine): y[t, n] = sum over the token's valid slots, in canonical order
+//   (ascending expert id), of w_j * (W_down[e_j] h_j)[n]; y is written as bf16.
 //
-// The FP4 weights are read once per pair with 16-byte loads: a wave's 64 lanes read 64
-// consecutive 32-code blocks (1 KB) of a row per load instruction. Each block is
-// dequantised in registers (hardware FP4 -> bf16 conversion, exact), dotted with the
-// activations in fp32 (bf16 dot2), then multiplied by its ue8m0 scale 2^(e-127). The
-// weights are never expanded in memory: storage format and compute format differ only in
-// registers ([A100-FP4], section 「FP4非対応」という言葉を疑う).
+// Both stages are matrix-vector products with FP4 weights. A workgroup owns a tile of 16
+// weight rows; its wavefronts split K. Per 128-element chunk of K, lane l (column
+// j = l % 16 of the MFMA, group g = l / 16) loads the 16 bytes of one 32-code block of
+// weight row (row0 + j), block 4 * chunk + g: a wavefront load covers 16 rows x 4 blocks.
+// The block is dequantised in registers by the hardware FP4 -> bf16 conversion, its ue8m0
+// scale applied in the same instruction (exact for scale bytes 2..252), and fed as the B
+// operand of v_mfma_f32_16x16x32_bf16; the token's activations are row 0 of the A operand
+// (read from LDS by the four lanes with l % 16 == 0, zeros elsewhere), so row 0 of the
+// 16 x 16 accumulator holds the 16 dot products. The weights are never expanded in memory:
+// storage and compute formats meet only in registers ([A100-FP4], section
+// 「FP4非対応」という言葉を疑う). The same lane order is used for the A and B K-slots, so
+// each MFMA covers elements 32g + 8m .. 32g + 8m + 7 of the chunk for m = 0..3.
+#include <algorithm>
+
 #include "moe_fp4_device.hpp"
 #include "moe_fp4_internal.hpp"
 
@@ -20,311 +26,370 @@ namespace moe_fp4 {
 
 namespace {
 
-constexpr int kThreads = 256;  // 4 wavefronts per workgroup
-constexpr int kWaves = kThreads / 64;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Launch shapes, tuned by measurement on MI355X; overridable at build time.
+#ifndef MOE_FP4_GU_WAVES
+#define MOE_FP4_GU_WAVES 4      // wavefronts per gate/up tile (split of K)
+#endif
+#ifndef MOE_FP4_GU_BATCH
+#define MOE_FP4_GU_BATCH 4      // 128-element chunks loaded per wave before use
+#endif
+#ifndef MOE_FP4_DC_WAVES
+#define MOE_FP4_DC_WAVES 8      // wavefronts per down/combine tile
+#endif
+#ifndef MOE_FP4_DC_BATCH
+#define MOE_FP4_DC_BATCH 18     // (expert, chunk) steps loaded per wave before use
+#endif
+
+constexpr int kGUWaves = MOE_FP4_GU_WAVES;
+constexpr int kGUThreads = kGUWaves * 64;
+constexpr int kGUBatch = MOE_FP4_GU_BATCH;
+constexpr int kDCWaves = MOE_FP4_DC_WAVES;
+constexpr int kDCThreads = kDCWaves * 64;
+constexpr int kDCBatch = MOE_FP4_DC_BATCH;
+constexpr int kTile = 16;  // weight rows per tile (MFMA N)
+
+// Weight streams are read once per call: non-temporal loads keep them from displacing
+// the small reused data (activations, h) in the caches.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Scale bytes: ordinary cached loads (neighbouring lanes read neighbouring bytes of one
+// cache line in separate instructions; through the cache the line is fetched once).
+__device__ __forceinline__ uint32_t ld_scale(const uint8_t* p) { return *p; }
+
+// The scale operand of the FP4 conversion is a float whose exponent field is the ue8m0
+// byte: 2^(e-127) for e = 1..254, 2^-127 for e = 0, NaN for e = 255.
+__device__ __forceinline__ float scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Eight FP4 codes (one dword, element 2i in the low nibble of byte i) -> eight bf16 values
+// times the block scale.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float s) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  return bf16x8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t dword(const uint4& v, int m) {
+  return m == 0 ? v.x : m == 1 ? v.y : m == 2 ? v.z : v.w;
+}
 
 // ---------------------------------------------------------------------------------------
-// Stage 1: gate/up/SiLU. One wave owns `rows_per_wave` consecutive rows of one pair.
-// LPR lanes per row, BPL blocks per lane; UNR row-iterations are loaded before any is
-// consumed so that UNR * BPL * 2 16-byte loads per lane are in flight.
+// Stage 1: gate/up/SiLU. Workgroup = one tile of 16 rows of gate and up of one pair; the
+// kGUWaves waves take equal shares of the K chunks, in batches of kGUBatch chunks.
+// PER = 0: the expert comes from ids. PER > 0: from fp64 router logits [T x E], the
+// first wave selecting the token's top-k itself (PER keys per lane); the tile with row 0
+// of slot 0 writes the token's ids and weights.
+// LDS: the token's x (H bf16) followed by one zero 16-byte word.
 // ---------------------------------------------------------------------------------------
-template <int LPR, int BPL, int UNR>
-__global__ __launch_bounds__(kThreads) void gate_up_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int n_pairs, int k,
+template <int PER>
+__global__ __launch_bounds__(kGUThreads) void gate_up_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const double* __restrict__ logits,
+    int k, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     const uint8_t* __restrict__ packed, size_t stride, size_t off_gc, size_t off_uc,
-    size_t off_gs, size_t off_us, int n_experts, int H, int I, int rows_per_wave,
-    int tasks_per_pair, uint16_t* __restrict__ hbuf) {
-  constexpr int RPI = 64 / LPR;  // rows per iteration
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int pair = wave / tasks_per_pair;
-  if (pair >= n_pairs) return;  // whole wave leaves together
-  const int e = ids[pair];
-  if (e < 0 || e >= n_experts) return;
+    size_t off_gs, size_t off_us, int n_experts, int H, int I, int tiles_per_pair,
+    uint16_t* __restrict__ hbuf) {
+  extern __shared__ uint4 smem[];
+  __shared__ float red_g[kGUWaves][kTile], red_u[kGUWaves][kTile];
+  __shared__ int s_e;
+  const int tile = blockIdx.x;
+  const int pair = tile / tiles_per_pair;
+  const int row0 = (tile - pair * tiles_per_pair) * kTile;
   const int t = pair / k;
-  const int row0 = (wave - pair * tasks_per_pair) * rows_per_wave;
-  const int row_end = min(row0 + rows_per_wave, I);
-  const int sub = lane / LPR;
-  const int li = lane - sub * LPR;
+  const int slot = pair - t * k;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
   const int KB = H / kBlock;
+  const int nch = (KB + 3) / 4;  // 128-element chunks of K
+  const int nx = H / 8;          // 16-byte words of x
 
-  // Activations for this lane's blocks, kept in registers for all rows.
-  uint4 xa[BPL][4];
+  int e;
+  if constexpr (PER > 0) {
+    if (wv == 0) {
+      int sid[8];
+      float sw[8];
+      wave_topk<PER>(logits + (size_t)t * n_experts, n_experts, k, lane, sid, sw);
+      int ej = sid[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if (q == slot) ej = sid[q];
+      if (lane == 0) s_e = ej;
+      if (slot == 0 && row0 == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (q < k && lane == q) {
+            ids_out[(size_t)t * k + q] = sid[q];
+            w_out[(size_t)t * k + q] = sw[q];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    e = s_e;
+  } else {
+    e = ids[pair];
+    if (e < 0 || e >= n_experts) return;  // whole workgroup
+  }
+
+  // 1. x into registers (indices clamped: every load is issued)
+  constexpr int kXRounds = kMaxDim / 8 / kGUThreads;
+  uint4 xr[kXRounds];
   const uint4* xv = reinterpret_cast<const uint4*>(x + (size_t)t * H);
 #pragma unroll
-  for (int i = 0; i < BPL; ++i) {
-    const int b = li + i * LPR;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xa[i][q] = (b < KB) ? xv[b * 4 + q] : make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < kXRounds; ++r) {
+    xr[r] = make_uint4(0, 0, 0, 0);
+    if (r * kGUThreads < nx) xr[r] = xv[min(tid + r * kGUThreads, nx - 1)];
   }
 
+  // 2. this wave's first batch of weights
+  const int c_begin = wv * nch / kGUWaves;
+  const int c_end = (wv + 1) * nch / kGUWaves;
+  // tile-major packed layout: word (tile, c, g, j) at tile * 16 * KB + 64 c + lane
+  const size_t tbase = (size_t)(row0 / kTile) * kTile * KB;
   const uint8_t* base = packed + (size_t)e * stride;
-  const uint4* gcodes = reinterpret_cast<const uint4*>(base + off_gc);
-  const uint4* ucodes = reinterpret_cast<const uint4*>(base + off_uc);
-  const uint8_t* gscales = base + off_gs;
-  const uint8_t* uscales = base + off_us;
-  const int n_iter = (row_end - row0 + RPI - 1) / RPI;
+  const uint4* gcodes = reinterpret_cast<const uint4*>(base + off_gc) + tbase;
+  const uint4* ucodes = reinterpret_cast<const uint4*>(base + off_uc) + tbase;
+  const uint8_t* gscales = base + off_gs + tbase;
+  const uint8_t* uscales = base + off_us + tbase;
 
-  for (int it0 = 0; it0 < n_iter; it0 += UNR) {
-    uint4 cg[UNR][BPL], cu[UNR][BPL];
-    uint32_t sg[UNR][BPL], su[UNR][BPL];
+  uint4 cg[kGUBatch], cu[kGUBatch];
+  uint32_t sg[kGUBatch], su[kGUBatch];
+  auto load_batch = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int r = row0 + (it0 + u) * RPI + sub;
-      const bool rv = r < row_end;
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        const int b = li + i * LPR;
-        if (rv && b < KB) {
-          const size_t blk = (size_t)r * KB + b;
-          cg[u][i] = gcodes[blk];
-          cu[u][i] = ucodes[blk];
-          sg[u][i] = gscales[blk];
-          su[u][i] = uscales[blk];
-        } else {
-          cg[u][i] = make_uint4(0, 0, 0, 0);
-          cu[u][i] = make_uint4(0, 0, 0, 0);
-          sg[u][i] = 127u;
-          su[u][i] = 127u;
-        }
-      }
+    for (int q = 0; q < kGUBatch; ++q) {
+      const int c = min(c0 + q, c_end - 1);
+      const int w = (4 * c + g < KB) ? 64 * c + lane : 64 * c;  // blocks past K: any valid word
+      cg[q] = ld_stream(gcodes + w);
+      cu[q] = ld_stream(ucodes + w);
+      sg[q] = ld_scale(gscales + w);
+      su[q] = ld_scale(uscales + w);
     }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      float ag = 0.f, au = 0.f;
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        ag += ue8m0_to_f32(sg[u][i]) *
-              fp4_block_dot(cg[u][i], xa[i][0], xa[i][1], xa[i][2], xa[i][3]);
-        au += ue8m0_to_f32(su[u][i]) *
-              fp4_block_dot(cu[u][i], xa[i][0], xa[i][1], xa[i][2], xa[i][3]);
-      }
-      ag = group_sum<LPR>(ag);
-      au = group_sum<LPR>(au);
-      const int r = row0 + (it0 + u) * RPI + sub;
-      if (li == 0 && r < row_end) {
-        hbuf[(size_t)pair * I + r] = f32_to_bf16_rne(silu_f32(ag) * au);
-      }
-    }
-  }
-}
+  };
+  if (c_begin < c_end) load_batch(c_begin);
 
-// ---------------------------------------------------------------------------------------
-// Stage 2: down projection and weighted combine. One workgroup owns `rows_per_block`
-// output rows of one token; its waves take RPI rows at a time.
-// LDS holds the token's h vectors as bf16 in a layout where, for part q (elements
-// 8q..8q+7 of a block) of block b of slot j, the 16 bytes sit at ((j*4 + q) * KBI + b):
-// the lanes of a row group read consecutive 16-byte words.
-// ---------------------------------------------------------------------------------------
-template <int LPR, int BPL>
-__global__ __launch_bounds__(kThreads) void down_combine_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ wts, int T, int k,
-    const uint8_t* __restrict__ packed, size_t stride, size_t off_dc, size_t off_ds,
-    int n_experts, int H, int I, int rows_per_block, int chunks_per_token,
-    const uint16_t* __restrict__ hbuf, uint16_t* __restrict__ y) {
-  extern __shared__ uint4 lds_h[];
-  constexpr int RPI = 64 / LPR;
-  const int t = blockIdx.x / chunks_per_token;
-  const int n0 = (blockIdx.x - t * chunks_per_token) * rows_per_block;
-  const int n_end = min(n0 + rows_per_block, H);
-  const int KBI = I / kBlock;
-
-  // Canonical slot order: ascending expert id, then ascending weight bits; invalid ids
-  // dropped. Ranks are computed with static indexing only (no private-memory arrays).
-  int ev[kMaxK];
-  uint32_t wb[kMaxK];
-  bool ok[kMaxK];
+  // 3. x into LDS
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    ev[j] = -1;
-    wb[j] = 0u;
-    ok[j] = false;
-    if (j < k) {
-      ev[j] = ids[(size_t)t * k + j];
-      wb[j] = __float_as_uint(wts[(size_t)t * k + j]);
-      ok[j] = ev[j] >= 0 && ev[j] < n_experts;
-    }
+  for (int r = 0; r < kXRounds; ++r) {
+    const int i = tid + r * kGUThreads;
+    if (r * kGUThreads < nx && i < nx) smem[i] = xr[r];
   }
-  int sid[kMaxK], sslot[kMaxK];
-  float sw[kMaxK];
-  int nv = 0;
-#pragma unroll
-  for (int p = 0; p < kMaxK; ++p) {
-    sid[p] = 0;
-    sslot[p] = 0;
-    sw[p] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    int rank = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxK; ++i) {
-      const bool before = ev[i] < ev[j] || (ev[i] == ev[j] && (wb[i] < wb[j] || (wb[i] == wb[j] && i < j)));
-      rank += (ok[i] && before) ? 1 : 0;
-    }
-    nv += ok[j] ? 1 : 0;
-#pragma unroll
-    for (int p = 0; p < kMaxK; ++p) {
-      if (ok[j] && rank == p) {
-        sid[p] = ev[j];
-        sslot[p] = j;
-        sw[p] = __uint_as_float(wb[j]);
-      }
-    }
-  }
-
-  // Stage h of the valid slots into LDS.
-  const int chunks = I / 8;  // 16-byte chunks per h vector
-  for (int c = threadIdx.x; c < nv * chunks; c += kThreads) {
-    const int j = c / chunks;
-    const int cc = c - j * chunks;
-    int slot = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxK; ++q)
-      if (q == j) slot = sslot[q];
-    const uint4 v =
-        reinterpret_cast<const uint4*>(hbuf + ((size_t)t * k + slot) * I)[cc];
-    const int b = cc >> 2, q = cc & 3;
-    lds_h[(j * 4 + q) * KBI + b] = v;
-  }
+  if (tid == 0) smem[nx] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int sub = lane / LPR;
-  const int li = lane - sub * LPR;
-
-  for (int nb = n0 + wv * RPI; nb < n_end; nb += kWaves * RPI) {
-    const int n = nb + sub;
-    const bool rv = n < n_end;
-    uint4 cd[kMaxK][BPL];
-    uint32_t sd[kMaxK][BPL];
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = c_begin; c0 < c_end; c0 += kGUBatch) {
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < nv) {
-        const uint8_t* base = packed + (size_t)sid[j] * stride;
-        const uint4* dcodes = reinterpret_cast<const uint4*>(base + off_dc);
-        const uint8_t* dscales = base + off_ds;
+    for (int q = 0; q < kGUBatch; ++q) {
+      const int c = c0 + q;
+      const int blk = 4 * c + g;
+      const bool bv = (c < c_end) && (blk < KB);  // wave-uniform c, per-lane blk
+      const uint4 wg = bv ? cg[q] : make_uint4(0, 0, 0, 0);
+      const uint4 wu = bv ? cu[q] : make_uint4(0, 0, 0, 0);
+      const float fg = scale_operand(bv ? sg[q] : 127u);
+      const float fu = scale_operand(bv ? su[q] : 127u);
 #pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-          const int b = li + i * LPR;
-          if (rv && b < KBI) {
-            const size_t blk = (size_t)n * KBI + b;
-            cd[j][i] = dcodes[blk];
-            sd[j][i] = dscales[blk];
-          } else {
-            cd[j][i] = make_uint4(0, 0, 0, 0);
-            sd[j][i] = 127u;
-          }
-        }
+      for (int m = 0; m < 4; ++m) {
+        const int ai = (j == 0 && bv) ? (16 * c + 4 * g + m) : nx;
+        const bf16x8_t a = as_bf16x8(smem[ai]);
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wg, m), fg), accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wu, m), fu), accu, 0, 0, 0);
       }
     }
-    float acc = 0.f;
+    if (c0 + kGUBatch < c_end) load_batch(c0 + kGUBatch);
+  }
+  // row 0 of the accumulators: lanes 0..15, element 0
+  if (lane < kTile) {
+    red_g[wv][lane] = accg[0];
+    red_u[wv][lane] = accu[0];
+  }
+  __syncthreads();
+  if (tid < kTile && row0 + tid < I) {
+    float gs = 0.f, us = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < nv) {
-        float pj = 0.f;
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-          const int b = li + i * LPR;
-          if (b < KBI) {
-            const uint4 h0 = lds_h[(j * 4 + 0) * KBI + b];
-            const uint4 h1 = lds_h[(j * 4 + 1) * KBI + b];
-            const uint4 h2 = lds_h[(j * 4 + 2) * KBI + b];
-            const uint4 h3 = lds_h[(j * 4 + 3) * KBI + b];
-            pj += ue8m0_to_f32(sd[j][i]) * fp4_block_dot(cd[j][i], h0, h1, h2, h3);
-          }
-        }
-        acc += sw[j] * pj;
-      }
+    for (int w = 0; w < kGUWaves; ++w) {
+      gs += red_g[w][tid];
+      us += red_u[w][tid];
     }
-    acc = group_sum<LPR>(acc);
-    if (li == 0 && rv) y[(size_t)t * H + n] = f32_to_bf16_rne(acc);
+    hbuf[(size_t)pair * I + row0 + tid] = f32_to_bf16_rne(silu_f32(gs) * us);
   }
 }
 
-template <int LPR, int BPL>
-hipError_t gate_up_dispatch(const uint16_t* x, const int32_t* ids, int T, int k,
-                            const uint8_t* packed, int n_experts, int H, int I,
-                            uint16_t* hbuf, hipStream_t s) {
-  constexpr int UNR = (BPL <= 2) ? 4 : 2;
-  constexpr int RPI = 64 / LPR;
-  const PackedLayout L = packed_layout(H, I);
-  const long n_pairs = (long)T * k;
-  // Rows per wave: enough waves to cover the GPU several times over, in multiples of the
-  // rows one unrolled step covers.
-  const long step = (long)RPI * UNR;
-  long rpw = (n_pairs * I + 4095) / 4096;
-  rpw = (rpw + step - 1) / step * step;
-  if (rpw < step) rpw = step;
-  if (rpw > 64 && rpw > step) rpw = (64 / step > 0 ? 64 / step : 1) * step;
-  const long tasks_per_pair = (I + rpw - 1) / rpw;
-  const long waves = n_pairs * tasks_per_pair;
-  const long blocks = (waves + kWaves - 1) / kWaves;
-  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gate_up_kernel<LPR, BPL, UNR>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     s, x, ids, (int)n_pairs, k, packed, L.stride, L.gate_codes, L.up_codes,
-                     L.gate_scales, L.up_scales, n_experts, H, I, (int)rpw, (int)tasks_per_pair,
-                     hbuf);
-  return hipGetLastError();
-}
+// ---------------------------------------------------------------------------------------
+// Stage 2: down projection and weighted combine. Workgroup = one tile of 16 output rows of
+// one token. The token's valid slots are put in canonical order (ascending expert id, then
+// weight bits; invalid ids dropped) and the (slot, chunk) steps split evenly over the
+// waves; each wave keeps one accumulator for the slot it is on and stores it to LDS when
+// it moves on. The final sum over waves and slots runs in a fixed order, so permuting a
+// token's (id, weight) pairs gives bit-identical output.
+// Load order per thread: its share of the token's h vectors (into LDS), then its first
+// batch of down weights, so the LDS stores wait only for the h loads.
+// LDS: h of the KT slots (bf16, natural order) then one zero 16-byte word.
+// ---------------------------------------------------------------------------------------
+template <int KT>
+__global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int T,
+    const uint8_t* __restrict__ packed, size_t stride, size_t off_dc, size_t off_ds,
+    int n_experts, int H, int I, int tiles_per_token, const uint16_t* __restrict__ hbuf,
+    uint16_t* __restrict__ y) {
+  extern __shared__ uint4 smem[];
+  __shared__ float red[kDCWaves][KT][kTile];
+  __shared__ int s_sid[KT], s_slot[KT], s_nv;
+  __shared__ float s_w[KT];
+  const int t = blockIdx.x / tiles_per_token;
+  const int row0 = (blockIdx.x - t * tiles_per_token) * kTile;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int j16 = lane & 15;
+  const int g = lane >> 4;
+  const int KBI = I / kBlock;
+  const int nch = (KBI + 3) / 4;
+  const int hx = I / 8;  // 16-byte words per h vector
 
-template <int LPR, int BPL>
-hipError_t down_dispatch(const int32_t* ids, const float* w, int T, int k, const uint8_t* packed,
-                         int n_experts, int H, int I, const uint16_t* hbuf, uint16_t* y,
-                         hipStream_t s) {
-  constexpr int RPI = 64 / LPR;
-  const PackedLayout L = packed_layout(H, I);
-  // Rows per workgroup: about 256 workgroups in total (one per CU) for a single token,
-  // growing with T so that the h staging (k * I * 2 bytes per workgroup) is amortised.
-  const long minr = (long)kWaves * RPI;
-  long rpb = ((long)T * H + 255) / 256;
-  rpb = (rpb + minr - 1) / minr * minr;
-  if (rpb > H) rpb = H;
-  const long chunks = (H + rpb - 1) / rpb;
-  const long blocks = (long)T * chunks;
-  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  const size_t lds = (size_t)k * I * 2;
-  hipLaunchKernelGGL((down_combine_kernel<LPR, BPL>), dim3((unsigned)blocks), dim3(kThreads),
-                     lds, s, ids, w, T, k, packed, L.stride, L.down_codes, L.down_scales,
-                     n_experts, H, I, (int)rpb, (int)chunks, hbuf, y);
-  return hipGetLastError();
-}
+  // canonical slot order: lane jj < KT of wave 0 ranks slot jj
+  if (tid < 64) {
+    const int jj = tid;
+    const int ej = (jj < KT) ? ids[(size_t)t * KT + jj] : -1;
+    const uint32_t wj = (jj < KT) ? __float_as_uint(wts[(size_t)t * KT + jj]) : 0u;
+    const bool okj = ej >= 0 && ej < n_experts;
+    int rank = 0, nvl = 0;
+#pragma unroll
+    for (int i = 0; i < KT; ++i) {
+      const int ei = __shfl(ej, i, 64);
+      const uint32_t wi = (uint32_t)__shfl((int)wj, i, 64);
+      const bool oki = ei >= 0 && ei < n_experts;
+      const bool before = ei < ej || (ei == ej && (wi < wj || (wi == wj && i < jj)));
+      rank += (oki && before) ? 1 : 0;
+      nvl += oki ? 1 : 0;
+    }
+    if (jj < KT && okj) {
+      s_sid[rank] = ej;
+      s_slot[rank] = jj;
+      s_w[rank] = __uint_as_float(wj);
+    }
+    if (jj == 0) s_nv = nvl;
+  }
+  for (int i = tid; i < kDCWaves * KT * kTile; i += kDCThreads) (&red[0][0][0])[i] = 0.f;
+  __syncthreads();
+  const int nv = s_nv;
+  // The slot table is read from LDS with the (wave-uniform) slot index: a select chain over
+  // a register array would be turned back into an indexed private-memory access.
 
-#define MOE_FP4_ROWMAP_SWITCH(FN, ...)                                 \
-  switch (rm.lpr * 16 + rm.bpl) {                                      \
-    case 64 * 16 + 1: return FN<64, 1>(__VA_ARGS__);                   \
-    case 64 * 16 + 2: return FN<64, 2>(__VA_ARGS__);                   \
-    case 64 * 16 + 3: return FN<64, 3>(__VA_ARGS__);                   \
-    case 64 * 16 + 4: return FN<64, 4>(__VA_ARGS__);                   \
-    case 64 * 16 + 5: return FN<64, 5>(__VA_ARGS__);                   \
-    case 64 * 16 + 6: return FN<64, 6>(__VA_ARGS__);                   \
-    case 64 * 16 + 7: return FN<64, 7>(__VA_ARGS__);                   \
-    case 64 * 16 + 8: return FN<64, 8>(__VA_ARGS__);                   \
-    case 32 * 16 + 1: return FN<32, 1>(__VA_ARGS__);                   \
-    case 32 * 16 + 2: return FN<32, 2>(__VA_ARGS__);                   \
-    case 32 * 16 + 3: return FN<32, 3>(__VA_ARGS__);                   \
-    case 32 * 16 + 4: return FN<32, 4>(__VA_ARGS__);                   \
-    case 16 * 16 + 1: return FN<16, 1>(__VA_ARGS__);                   \
-    case 16 * 16 + 2: return FN<16, 2>(__VA_ARGS__);                   \
-    case 16 * 16 + 3: return FN<16, 3>(__VA_ARGS__);                   \
-    case 16 * 16 + 4: return FN<16, 4>(__VA_ARGS__);                   \
-    case 8 * 16 + 1: return FN<8, 1>(__VA_ARGS__);                     \
-    case 8 * 16 + 2: return FN<8, 2>(__VA_ARGS__);                     \
-    case 8 * 16 + 3: return FN<8, 3>(__VA_ARGS__);                     \
-    case 8 * 16 + 4: return FN<8, 4>(__VA_ARGS__);                     \
-    default: return hipErrorInvalidValue;                              \
+  // 1. h of the valid slots into registers
+  constexpr int kHRounds = (kMaxLdsH / 16 + kDCThreads - 1) / kDCThreads;
+  const int nwords = nv * hx;
+  uint4 hr[kHRounds];
+#pragma unroll
+  for (int r = 0; r < kHRounds; ++r) {
+    hr[r] = make_uint4(0, 0, 0, 0);
+    if (r * kDCThreads < nwords) {
+      const int c = min(tid + r * kDCThreads, nwords - 1);
+      const int p = c / hx;
+      const int slot = s_slot[p];
+      hr[r] = reinterpret_cast<const uint4*>(hbuf + ((size_t)t * KT + slot) * I)[c - p * hx];
+    }
   }
 
-// One thread per 32-element block: the decode of the FFN kernels, written out to memory.
-__global__ __launch_bounds__(kThreads) void debug_dequant_kernel(const uint4* __restrict__ codes,
-                                                                 const uint8_t* __restrict__ scales,
-                                                                 long n_blocks,
-                                                                 float* __restrict__ out) {
-  const long b = (long)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= n_blocks) return;
-  const uint4 c = codes[b];
-  const float s = ue8m0_to_f32(scales[b]);
+  // 2. this wave's first batch of weights. Steps s = p * nch + c (slot p, chunk c).
+  const int n_steps = nv * nch;
+  const int s_begin = wv * n_steps / kDCWaves;
+  const int s_end = (wv + 1) * n_steps / kDCWaves;
+  const size_t tbase = (size_t)(row0 / kTile) * kTile * KBI;  // tile-major packed layout
+  uint4 cd[kDCBatch];
+  uint32_t sd[kDCBatch];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int q = 0; q < kDCBatch; ++q) {
+      const int s = min(s0 + q, s_end - 1);
+      const int p = s / nch;
+      const int c = s - p * nch;
+      const uint8_t* base = packed + (size_t)s_sid[p] * stride;
+      const size_t w = tbase + ((4 * c + g < KBI) ? 64 * c + lane : 64 * c);
+      cd[q] = ld_stream(reinterpret_cast<const uint4*>(base + off_dc) + w);
+      sd[q] = ld_scale(base + off_ds + w);
+    }
+  };
+  if (s_begin < s_end) load_batch(s_begin);
+
+  // 3. h into LDS
+#pragma unroll
+  for (int r = 0; r < kHRounds; ++r) {
+    const int c = tid + r * kDCThreads;
+    if (r * kDCThreads < nwords && c < nwords) smem[c] = hr[r];
+  }
+  if (tid == 0) smem[KT * hx] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  const int zero_word = KT * hx;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int cur_p = (s_begin < s_end) ? s_begin / nch : 0;
+  for (int s0 = s_begin; s0 < s_end; s0 += kDCBatch) {
+#pragma unroll
+    for (int q = 0; q < kDCBatch; ++q) {
+      const int s = s0 + q;
+      if (s < s_end) {  // wave-uniform
+        const int p = s / nch;
+        const int c = s - p * nch;
+        if (p != cur_p) {  // wave-uniform: flush the finished slot
+          if (lane < kTile) red[wv][cur_p][lane] = acc[0];
+          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          cur_p = p;
+        }
+        const int blk = 4 * c + g;
+        const bool bv = blk < KBI;
+        const uint4 wd = bv ? cd[q] : make_uint4(0, 0, 0, 0);
+        const float fs = scale_operand(bv ? sd[q] : 127u);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int ai = (j16 == 0 && bv) ? (p * hx + 16 * c + 4 * g + m) : zero_word;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(smem[ai]),
+                                                       fp4x8_to_bf16(dword(wd, m), fs), acc, 0, 0, 0);
+        }
+      }
+    }
+    if (s0 + kDCBatch < s_end) load_batch(s0 + kDCBatch);
+  }
+  if (s_begin < s_end && lane < kTile) red[wv][cur_p][lane] = acc[0];
+  __syncthreads();
+  if (tid < kTile && row0 + tid < H) {
+    float yv = 0.f;
+#pragma unroll
+    for (int p = 0; p < KT; ++p) {
+      if (p < nv) {
+        float sp = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDCWaves; ++w) sp += red[w][p][tid];
+        yv += s_w[p] * sp;
+      }
+    }
+    y[(size_t)t * H + row0 + tid] = f32_to_bf16_rne(yv);
+  }
+}
+
+// One thread per (row, block) of one matrix: the FP4 decode with the ue8m0 scale applied
+// in fp32 (exact for every scale byte), written out row-major [rows x K].
+__global__ __launch_bounds__(256) void debug_dequant_kernel(const uint4* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int rows, int kb, float* __restrict__ out) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= (long)rows * kb) return;
+  const int row = (int)(b / kb);
+  const int blk = (int)(b - (long)row * kb);
+  const long v = (long)(row / 16) * 16 * kb + 64L * (blk / 4) + 16 * (blk % 4) + (row % 16);
+  const uint4 c = codes[v];
+  const float s = ue8m0_to_f32(scales[v]);
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float* o = out + b * kBlock;
 #define MOE_FP4_DQ_WORD(Q)                                                        \
@@ -349,34 +414,87 @@ __global__ __launch_bounds__(kThreads) void debug_dequant_kernel(const uint4* __
 #undef MOE_FP4_DQ_WORD
 }
 
-}  // namespace
-
-hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
-                                int matrix, float* out, hipStream_t s) {
-  const PackedLayout L = packed_layout(hidden, inter);
-  const size_t coff[3] = {L.gate_codes, L.up_codes, L.down_codes};
-  const size_t soff[3] = {L.gate_scales, L.up_scales, L.down_scales};
-  const uint8_t* base = packed + (size_t)expert * L.stride;
-  const long n_blocks = (long)hidden * inter / kBlock;
-  const long grid = (n_blocks + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                     reinterpret_cast<const uint4*>(base + coff[matrix]), base + soff[matrix],
-                     n_blocks, out);
-  return hipGetLastError();
+template <int PER>
+hipError_t gate_up_launch(const uint16_t* x, const int32_t* ids, const double* logits, int T, int k,
+                          int32_t* ids_out, float* w_out, const uint8_t* packed, int n_experts,
+                          int H, int I, uint16_t* hbuf, hipStream_t s) {
+  const PackedLayout L = packed_layout(H, I);
+  const long tiles_per_pair = (I + kTile - 1) / kTile;
+  const long blocks = (long)T * k * tiles_per_pair;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  const uint32_t lds = (uint32_t)((H / 8 + 1) * 16);
+  return launch_kernel(kKindGateUp, gate_up_kernel<PER>, dim3((unsigned)blocks), dim3(kGUThreads),
+                       lds, s, x, ids, logits, k, ids_out, w_out, packed, L.stride, L.m[0].codes,
+                       L.m[1].codes, L.m[0].scales, L.m[1].scales, n_experts, H, I,
+                       (int)tiles_per_pair, hbuf);
 }
 
-hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, int T, int k,
-                          const uint8_t* packed, int n_experts, int hidden, int inter,
-                          uint16_t* hbuf, hipStream_t s) {
-  const RowMap rm = choose_row_map(hidden / kBlock);
-  MOE_FP4_ROWMAP_SWITCH(gate_up_dispatch, x, ids, T, k, packed, n_experts, hidden, inter, hbuf, s)
+template <int KT>
+hipError_t down_launch(const int32_t* ids, const float* w, int T, const uint8_t* packed,
+                       int n_experts, int H, int I, const uint16_t* hbuf, uint16_t* y,
+                       hipStream_t s) {
+  const PackedLayout L = packed_layout(H, I);
+  const long tiles = (H + kTile - 1) / kTile;
+  const long blocks = (long)T * tiles;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  const uint32_t lds = (uint32_t)((size_t)KT * I * 2 + 16);
+  // allow more than 64 KB of LDS per workgroup (the device has 160 KB per CU)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(down_combine_kernel<KT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLdsH + 16));
+  if (attr != hipSuccess) return attr;
+  return launch_kernel(kKindDownCombine, down_combine_kernel<KT>, dim3((unsigned)blocks),
+                       dim3(kDCThreads), lds, s, ids, w, T, packed, L.stride, L.m[2].codes,
+                       L.m[2].scales, n_experts, H, I, (int)tiles, hbuf, y);
+}
+
+}  // namespace
+
+hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, const double* logits, int T,
+                          int k, int32_t* ids_out, float* w_out, const uint8_t* packed,
+                          int n_experts, int hidden, int inter, uint16_t* hbuf, hipStream_t s) {
+  if (!logits)
+    return gate_up_launch<0>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  const int per = (n_experts + 63) / 64;
+  if (per <= 2)
+    return gate_up_launch<2>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  if (per <= 4)
+    return gate_up_launch<4>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  if (per <= 6)
+    return gate_up_launch<6>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  if (per <= 8)
+    return gate_up_launch<8>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  if (per <= 16)
+    return gate_up_launch<16>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  return gate_up_launch<32>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
 }
 
 hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,
                                const uint8_t* packed, int n_experts, int hidden, int inter,
                                const uint16_t* hbuf, uint16_t* y, hipStream_t s) {
-  const RowMap rm = choose_row_map(inter / kBlock);
-  MOE_FP4_ROWMAP_SWITCH(down_dispatch, ids, w, T, k, packed, n_experts, hidden, inter, hbuf, y, s)
+  switch (k) {
+    case 1: return down_launch<1>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 2: return down_launch<2>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 3: return down_launch<3>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 4: return down_launch<4>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 5: return down_launch<5>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 6: return down_launch<6>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 7: return down_launch<7>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    case 8: return down_launch<8>(ids, w, T, packed, n_experts, hidden, inter, hbuf, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
+                                int matrix, float* out, hipStream_t s) {
+  const PackedLayout L = packed_layout(hidden, inter);
+  const MatLayout& M = L.m[matrix];
+  const uint8_t* base = packed + (size_t)expert * L.stride;
+  const long n_blocks = (long)M.rows * M.kb;
+  const long grid = (n_blocks + 255) / 256;
+  debug_dequant_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+      reinterpret_cast<const uint4*>(base + M.codes), base + M.scales, M.rows, M.kb, out);
+  return hipGetLastError();
 }
 
 }  // namespace moe_fp4

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace moe_fp4 {
@@ -68,6 +69,85 @@ __device__ __forceinline__ double group_sum_f64(double v) {
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
   return v;
+}
+
+// Wave-wide maximum of a uint32 (all 64 lanes active): a DPP butterfly inside each row of
+// 16 lanes, then the four row results through scalar registers. Every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Order-preserving map of an fp64 value to uint64 (larger value -> larger key; -0 and +0
+// map to the same key). NaN is not ordered meaningfully.
+__device__ __forceinline__ uint64_t f64_order_key(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v + 0.0);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double f64_from_order_key(uint64_t k) {
+  const uint64_t u = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+  return __longlong_as_double((long long)u);
+}
+
+// Top-k of one row of E logits by a whole wavefront (all 64 lanes active, wave-uniform
+// arguments). Lane l holds the order keys of logits l, l + 64, ... (at most PER per lane);
+// each of the k rounds takes the lane-local best (largest key; a lane's ids ascend, so the
+// first of equal keys has the lowest id), then the wave-wide best via three DPP reductions
+// (high key word, low key word, lowest id among equal keys), and its owner removes it.
+// On return every lane holds ids[j] (descending logit, ties by ascending id) and
+// w[j] = softmax over the k selected logits (fp64, rounded to fp32), for j < k.
+template <int PER, typename V>
+__device__ __forceinline__ void wave_topk(const V* __restrict__ row, int E, int k, int lane,
+                                          int (&ids)[8], float (&w)[8]) {
+  uint64_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + i * 64;
+    key[i] = (e < E) ? f64_order_key((double)row[e]) : 0ull;  // 0: empty slot
+  }
+  double v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ids[j] = 0;
+    v[j] = 0.0;
+    if (j < k) {
+      uint64_t bk = 0ull;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (key[i] > bk) {
+          bk = key[i];
+          bi = lane + i * 64;
+        }
+      }
+      const uint32_t hi = wave_max_u32((uint32_t)(bk >> 32));
+      const uint32_t lo = wave_max_u32(((uint32_t)(bk >> 32) == hi) ? (uint32_t)bk : 0u);
+      const uint64_t mk = ((uint64_t)hi << 32) | lo;
+      const uint32_t win = wave_min_u32(bk == mk ? (uint32_t)bi : 0xffffffffu);
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (lane + i * 64 == (int)win) key[i] = 0ull;
+      ids[j] = (int)win;
+      v[j] = f64_from_order_key(mk);
+    }
+  }
+  double ex[8];
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ex[j] = (j < k) ? exp(v[j] - v[0]) : 0.0;
+    sum += ex[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = (j < k) ? (float)(ex[j] / sum) : 0.f;
 }
 
 __device__ __forceinline__ float silu_f32(float z) {

@@ -3,6 +3,7 @@
 // conversion and the bf16 dot2 instruction.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -15,65 +16,76 @@ constexpr int kMaxDim = 16384;    // max hidden / inter
 constexpr int kMaxExpertsTopk = 2048;  // max experts for the top-k selection kernel
 constexpr int kMaxLdsH = 65536;   // bytes of LDS for the k staged h vectors of one token
 
+// Kernel kinds for timing (same values as MOE_FP4_KERNEL_* in the public header).
+enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp = 3,
+                  kKindDownCombine = 4 };
+
 // ----------------------------------------------------------------------------------------
-// Packed expert layout (the output of moe_fp4_pack). Per expert, at e * stride:
-//   codes  gate [I x H/2] | up [I x H/2] | down [H x I/2]
-//   scales gate [I x H/32] | up [I x H/32] | down [H x I/32]
-// stride = code bytes + scale bytes rounded up to 256.
+// Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
+// [I x H], up [I x H], down [H x I]; rows x K). Each matrix is stored tile-major: its rows
+// (padded to a multiple of 16 with zero codes and scale byte 127) form 16-row tiles, K
+// forms 128-element chunks (4 scale blocks), and for every (tile, chunk) the 16-byte code
+// blocks are laid out as [block-in-chunk g][row-in-tile j], so the 64 lanes of a
+// wavefront (lane = 16 g + j) read one contiguous 1 KB word per load. The last chunk of a
+// row holds only the blocks that exist (K need not be a multiple of 128); its words keep
+// the same [g][j] order. Scale bytes follow the same order, one byte per block: 64
+// contiguous bytes per (tile, chunk).
+//   code word  (tile, c, g, j) at  tile * 16 * KB + 64 c + 16 g + j   (16-byte units)
+//   scale byte (tile, c, g, j) at  tile * 16 * KB + 64 c + 16 g + j   (bytes)
+// with KB = K / 32. Codes of the three matrices come first, then their scales, each
+// region 256-byte aligned; the expert stride is a multiple of 256.
 // ----------------------------------------------------------------------------------------
-struct PackedLayout {
-  size_t gate_codes, up_codes, down_codes;   // byte offsets inside one expert
-  size_t gate_scales, up_scales, down_scales;
-  size_t stride;                             // bytes per expert
+struct MatLayout {
+  size_t codes;   // byte offset of the code region inside one expert
+  size_t scales;  // byte offset of the scale region
+  int rows;       // rows of the matrix
+  int tiles;      // 16-row tiles
+  int kb;         // scale blocks per row (K / 32)
 };
+
+struct PackedLayout {
+  MatLayout m[3];  // gate, up, down
+  size_t stride;   // bytes per expert
+};
+
+inline size_t align_up256(size_t v) { return (v + 255) / 256 * 256; }
 
 inline PackedLayout packed_layout(int hidden, int inter) {
   PackedLayout L;
-  const size_t hi = (size_t)hidden * (size_t)inter;
-  L.gate_codes = 0;
-  L.up_codes = hi / 2;
-  L.down_codes = hi;
-  L.gate_scales = 3 * hi / 2;
-  L.up_scales = L.gate_scales + hi / kBlock;
-  L.down_scales = L.up_scales + hi / kBlock;
-  const size_t bytes = L.down_scales + hi / kBlock;
-  L.stride = (bytes + 255) / 256 * 256;
+  const int rows[3] = {inter, inter, hidden};
+  const int kdim[3] = {hidden, hidden, inter};
+  size_t off = 0;
+  for (int i = 0; i < 3; ++i) {
+    L.m[i].rows = rows[i];
+    L.m[i].tiles = (rows[i] + 15) / 16;
+    L.m[i].kb = kdim[i] / kBlock;
+    L.m[i].codes = off;
+    off += align_up256((size_t)L.m[i].tiles * 16 * L.m[i].kb * 16);
+  }
+  for (int i = 0; i < 3; ++i) {
+    L.m[i].scales = off;
+    off += align_up256((size_t)L.m[i].tiles * 16 * L.m[i].kb);
+  }
+  L.stride = align_up256(off);
   return L;
 }
 
-// Lane mapping of a K-long row: LPR lanes share one row, lane li owns the 32-element
-// blocks li, li + LPR, ..., li + (BPL-1) * LPR. 64 / LPR rows are processed at once.
-struct RowMap {
-  int lpr;
-  int bpl;
-};
+// Kernel timing. When timing is enabled, timing_slot hands out a pair of events for one
+// launch of kernel `kind`; the launch passes them to hipExtLaunchKernel, which stamps them
+// with the dispatch's own start and end times.
+bool timing_slot(int kind, hipEvent_t* start, hipEvent_t* stop);
 
-// Pick (LPR, BPL) for kb = K / 32 blocks: the fewest idle lane slots, BPL <= 4 when
-// possible, else LPR = 64 with BPL <= 8. Returns bpl = 0 if K is too large.
-inline RowMap choose_row_map(int kb) {
-  RowMap best{0, 0};
-  double best_eff = -1.0;
-  const int lprs[4] = {64, 32, 16, 8};
-  for (int i = 0; i < 4; ++i) {
-    const int lpr = lprs[i];
-    const int bpl = (kb + lpr - 1) / lpr;
-    if (bpl > 4) continue;
-    const double eff = (double)kb / (double)(lpr * bpl);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = RowMap{lpr, bpl};
-    }
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                         uint32_t shmem, hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timing_slot(kind, &e0, &e1)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0, static_cast<KArgs>(args)...);
+  } else {
+    kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
   }
-  if (best.bpl == 0) {
-    const int bpl = (kb + 63) / 64;
-    if (bpl <= 8) best = RowMap{64, bpl};
-  }
-  return best;
+  return hipGetLastError();
 }
-
-// Timing hooks (no-ops unless timing is enabled).
-void timing_begin(int kind, hipStream_t s);
-void timing_end(int kind, hipStream_t s);
 
 // Kernel launchers. Each returns hipSuccess or the launch error.
 hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int n_experts, int hidden,
@@ -87,9 +99,11 @@ hipError_t launch_topk_f64(const double* logits, int T, int n_experts, int k, in
 hipError_t launch_topk_f32(const float* logits, int T, int n_experts, int k, int32_t* ids,
                            float* w, hipStream_t s);
 
-hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, int T, int k,
-                          const uint8_t* packed, int n_experts, int hidden, int inter,
-                          uint16_t* hbuf, hipStream_t s);
+// ids != nullptr: experts from ids. Otherwise from fp64 logits [T x n_experts] (top-k
+// selected in the kernel; ids_out / w_out [T x k] receive the selection).
+hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, const double* logits, int T,
+                          int k, int32_t* ids_out, float* w_out, const uint8_t* packed,
+                          int n_experts, int hidden, int inter, uint16_t* hbuf, hipStream_t s);
 
 hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,
                                const uint8_t* packed, int n_experts, int hidden, int inter,

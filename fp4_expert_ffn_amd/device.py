@@ -59,9 +59,11 @@ class MoeFp4Layer:
         self.device = packed.device
         self._ws = None
         self._rws = None
+        self._fws = None
 
-    def _workspace(self, T: int) -> torch.Tensor:
-        need = C.moe_fp4_workspace_bytes(T, self.k, self.n_experts, self.hidden, self.inter)
+    def _workspace(self, T: int, k: Optional[int] = None) -> torch.Tensor:
+        need = C.moe_fp4_workspace_bytes(T, self.k if k is None else k, self.n_experts,
+                                         self.hidden, self.inter)
         if self._ws is None or self._ws.numel() < max(need, 256):
             self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
         return self._ws
@@ -97,11 +99,35 @@ class MoeFp4Layer:
         k = ids.shape[1] if ids.dim() == 2 else self.k
         if y is None:
             y = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=self.device)
-        ws = self._workspace(T)
+        ws = self._workspace(T, k)
         C.moe_fp4_expert_ffn(x, ids, w, T, k, self.packed, self.n_experts, self.hidden, self.inter,
                              y, ws, stream=stream)
         return y
 
     def forward(self, x: torch.Tensor, stream=None):
+        """moe_fp4_route then moe_fp4_expert_ffn."""
         ids, w = self.route(x, stream=stream)
         return self.ffn(x, ids, w, stream=stream), ids, w
+
+    def _forward_workspace(self, T: int) -> torch.Tensor:
+        need = C.moe_fp4_moe_forward_workspace_bytes(T, self.k, self.n_experts, self.hidden,
+                                                     self.inter)
+        if self._fws is None or self._fws.numel() < max(need, 256):
+            self._fws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._fws
+
+    def forward_fused(self, x: torch.Tensor, ids: Optional[torch.Tensor] = None,
+                      w: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                      stream=None):
+        """moe_fp4_moe_forward: the same layer in one call (three kernel launches)."""
+        T = x.shape[0]
+        if ids is None:
+            ids = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+        if w is None:
+            w = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
+        if y is None:
+            y = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=self.device)
+        ws = self._forward_workspace(T)
+        C.moe_fp4_moe_forward(x, self.w_router, T, self.hidden, self.n_experts, self.k, self.packed,
+                              self.inter, ids, w, y, ws, stream=stream)
+        return y, ids, w

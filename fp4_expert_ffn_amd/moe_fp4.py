@@ -53,6 +53,8 @@ _SIGNATURES = {
     "moe_fp4_route_logits": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp4_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_expert_ffn": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_fp4_moe_forward_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_fp4_timing_enable": (_I, [_I]),
@@ -163,6 +165,21 @@ def moe_fp4_expert_ffn(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: i
     _check(lib().moe_fp4_expert_ffn(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(packed),
                                     n_experts, hidden, inter, _ptr(y), _ptr(workspace),
                                     workspace_bytes, _stream(stream)), "moe_fp4_expert_ffn")
+
+
+def moe_fp4_moe_forward_workspace_bytes(T: int, k: int, n_experts: int, hidden: int,
+                                        inter: int) -> int:
+    return lib().moe_fp4_moe_forward_workspace_bytes(T, k, n_experts, hidden, inter)
+
+
+def moe_fp4_moe_forward(x, w_router, T: int, hidden: int, n_experts: int, k: int, packed,
+                        inter: int, topk_ids, topk_w, y, workspace,
+                        workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_fp4_moe_forward(_ptr(x), _ptr(w_router), T, hidden, n_experts, k, _ptr(packed),
+                                     inter, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(workspace),
+                                     workspace_bytes, _stream(stream)), "moe_fp4_moe_forward")
 
 
 def moe_fp4_validate_ids(topk_ids, T: int, k: int, n_experts: int, bad_count, stream=None) -> None:

@@ -131,6 +131,26 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
                        int k, const void* packed, int n_experts, int hidden, int inter,
                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Whole routed-expert layer in one call: moe_fp4_route followed by moe_fp4_expert_ffn,
+ * with the top-k selection folded into the first FFN kernel (three kernel launches in all:
+ * router GEMV, gate/up/SiLU with selection, down + combine). Same results as the two calls
+ * in sequence: topk_ids / topk_w receive the routing (bit-identical to moe_fp4_route), y
+ * the layer output. Cutting launches per layer is the pages' own lesson ([A100-FP4],
+ * section 然后又发现每 token 启动 2000 次内核).
+ * ------------------------------------------------------------------------------------ */
+
+/* Workspace bytes moe_fp4_moe_forward needs. */
+size_t moe_fp4_moe_forward_workspace_bytes(int T, int k, int n_experts, int hidden, int inter);
+
+/* x [T x hidden] bf16; w_router [n_experts x hidden] bf16; packed: moe_fp4_pack output;
+ * outputs topk_ids int32 [T x k], topk_w fp32 [T x k], y [T x hidden] bf16.
+ * Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, HIP. */
+int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int hidden,
+                        int n_experts, int k, const void* packed, int inter, int32_t* topk_ids,
+                        float* topk_w, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Debug helper: counts the entries of topk_ids [T x k] outside [0, n_experts) into
  * *bad_count (a device int32 that this call overwrites). */
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,

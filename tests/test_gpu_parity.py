@@ -213,6 +213,25 @@ def test_layer_decode_full_size_route_and_ffn(dev, decode_layer):
             log(f"decode token {s}: normwise {err:.2e} cosine {cos:.7f}")
 
 
+def test_moe_forward_matches_route_then_ffn(dev, decode_layer):
+    """The one-call layer (selection folded into the gate/up kernel) gives bit-identical
+    ids, weights and outputs to moe_fp4_route followed by moe_fp4_expert_ffn, for batch 1
+    and for a batch of 5 tokens; and its ids match the oracle."""
+    _, D = _mods()
+    wl, layer = decode_layer
+    wr_bits = S.router_weights(wl, 0)
+    for T, step in ((1, 100), (1, 101), (5, 102)):
+        x_bits = S.activations(wl, 0, step, tokens=T)
+        x = D.upload_bf16(x_bits, dev)
+        y1, ids1, w1 = layer.forward(x)
+        y2, ids2, w2 = layer.forward_fused(x)
+        torch.cuda.synchronize()
+        assert torch.equal(ids1, ids2) and torch.equal(w1, w2), f"T={T}"
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"T={T}"
+        ids_ref, w_ref, _ = O.route(x_bits, wr_bits, wl.k)
+        check_route(ids2.cpu().numpy(), w2.cpu().numpy(), ids_ref, w_ref, f"fused T={T}")
+
+
 def test_layer_batched64_zipf_full_size(dev, decode_layer):
     """64 tokens per step through the 384-expert layer, Zipf(1.1)-skewed logits."""
     _, D = _mods()
@@ -256,6 +275,20 @@ def test_layer_prefill8192_sampled(dev, decode_layer):
 def small_layer(dev):
     wl = S.small_workload(512, 384, 12, 6, 1, wid=400)
     return wl, _layer(wl, dev)
+
+
+@pytest.mark.parametrize("T", [1, 3, 70])
+def test_moe_forward_small_layer(dev, small_layer, T):
+    _, D = _mods()
+    wl, layer = small_layer
+    wr_bits = S.router_weights(wl, 0)
+    x_bits = S.activations(wl, 0, 7, tokens=T)
+    y, ids, w = layer.forward_fused(D.upload_bf16(x_bits, dev))
+    torch.cuda.synchronize()
+    ids_ref, w_ref, _ = O.route(x_bits, wr_bits, wl.k)
+    check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"fused small T={T}")
+    ref = O.expert_ffn(x_bits, ids_ref, w_ref, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
+    check_ffn(D.bf16_bits(y), ref, f"fused small T={T}")
 
 
 def test_t0_is_a_no_op(dev, small_layer):
