@@ -37,9 +37,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=(), csrc: str = CSRC) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, "-I", csrc, *[f"-D{d}" for d in defines], "-c",
+           os.path.join(csrc, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -52,13 +53,14 @@ def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
 
 
 def build(verbose: bool = True, lib_path: str = LIB_PATH, build_dir: str = BUILD_DIR,
-          defines=()) -> str:
+          defines=(), csrc: str = CSRC) -> str:
     """Compile every source and link the shared library. `defines` (NAME=VALUE strings)
-    override the compile-time launch-shape constants."""
+    override the compile-time launch-shape constants; `csrc` builds another source tree
+    of the same file names."""
     os.makedirs(build_dir, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines, csrc), SOURCES))
     tmp = lib_path + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

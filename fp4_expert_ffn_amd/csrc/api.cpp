@@ -13,6 +13,7 @@ using namespace moe_fp4;
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool valid_dim(int d) { return d > 0 && d % kBlock == 0 && d <= kMaxDim; }
 
@@ -110,9 +111,12 @@ int moe_fp4_pack(const uint8_t* codes, const uint8_t* scales, int n_experts, int
                                             static_cast<uint8_t*>(packed), s)));
 }
 
+// Route workspace: a 4 KB synchronisation area (kept between calls), then fp64 logits.
+constexpr size_t kRouteSyncBytes = 4096;
+
 size_t moe_fp4_route_workspace_bytes(int T, int n_experts) {
   if (T < 0 || n_experts <= 0) return 0;
-  return align256((size_t)T * (size_t)n_experts * sizeof(double));
+  return kRouteSyncBytes + align256((size_t)T * (size_t)n_experts * sizeof(double));
 }
 
 static int check_topk_args(int T, int n_experts, int k) {
@@ -122,6 +126,18 @@ static int check_topk_args(int T, int n_experts, int k) {
   return MOE_FP4_OK;
 }
 
+static hipError_t route_impl(const uint16_t* x, const uint16_t* w_router, int T, int hidden,
+                             int n_experts, int k, int32_t* topk_ids, float* topk_w,
+                             void* workspace, hipStream_t s) {
+  uint32_t* sync = static_cast<uint32_t*>(workspace);
+  double* logits = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + kRouteSyncBytes);
+  if (T == 1 && (size_t)route_decode_sync_words(n_experts) * 4 <= kRouteSyncBytes)
+    return launch_route_decode(x, w_router, hidden, n_experts, k, sync, logits, topk_ids, topk_w, s);
+  hipError_t e = launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s);
+  if (e != hipSuccess) return e;
+  return launch_topk_f64(logits, T, n_experts, k, topk_ids, topk_w, s);
+}
+
 int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden, int n_experts,
                   int k, int32_t* topk_ids, float* topk_w, void* workspace,
                   size_t workspace_bytes, void* stream) {
@@ -129,16 +145,13 @@ int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden
   int st = check_topk_args(T, n_experts, k);
   if (st != MOE_FP4_OK) return st;
   if (!valid_dim(hidden)) return MOE_FP4_ERR_BAD_SHAPE;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w) ||
       !aligned16(workspace))
     return MOE_FP4_ERR_MISALIGNED;
   if (workspace_bytes < moe_fp4_route_workspace_bytes(T, n_experts)) return MOE_FP4_ERR_WORKSPACE;
   if (T == 0) return MOE_FP4_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  double* logits = static_cast<double*>(workspace);
-  hipError_t e = (launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s));
-  if (e != hipSuccess) return MOE_FP4_ERR_HIP;
-  return from_hip((launch_topk_f64(logits, T, n_experts, k, topk_ids, topk_w, s)));
+  return from_hip(route_impl(x, w_router, T, hidden, n_experts, k, topk_ids, topk_w, workspace,
+                             static_cast<hipStream_t>(stream)));
 }
 
 int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,
@@ -146,7 +159,7 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
   if (!logits || !topk_ids || !topk_w) return MOE_FP4_ERR_INVALID_ARG;
   int st = check_topk_args(T, n_experts, k);
   if (st != MOE_FP4_OK) return st;
-  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_FP4_ERR_MISALIGNED;
+  if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w)) return MOE_FP4_ERR_MISALIGNED;
   if (T == 0) return MOE_FP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip((launch_topk_f32(logits, T, n_experts, k, topk_ids, topk_w, s)));
@@ -154,33 +167,37 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
 
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
   (void)n_experts;
-  (void)hidden;
-  if (T < 0 || k < 1 || k > kMaxK || !valid_dim(inter)) return 0;
+  if (T < 0 || k < 1 || k > kMaxK || !valid_dim(hidden) || !valid_dim(inter)) return 0;
   // h for every (token, slot) pair, bf16
   return align256((size_t)T * (size_t)k * (size_t)inter * 2);
 }
+
+// Both FFN stages; the workspace holds h.
+static hipError_t ffn_impl(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
+                           int k, const uint8_t* pk, int n_experts, int hidden, int inter,
+                           uint16_t* y, void* workspace, hipStream_t s) {
+  uint16_t* hbuf = static_cast<uint16_t*>(workspace);
+  hipError_t e = launch_gate_up(x, topk_ids, T, k, pk, n_experts, hidden, inter, hbuf, s);
+  if (e != hipSuccess) return e;
+  return launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, hbuf, y, s);
+}
+
+static bool lds_fits(int k, int inter) { return (size_t)k * (size_t)inter * 2 <= (size_t)kMaxLdsH; }
 
 int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                        int k, const void* packed, int n_experts, int hidden, int inter,
                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !topk_ids || !topk_w || !packed || !y || !workspace) return MOE_FP4_ERR_INVALID_ARG;
   if (T < 0 || n_experts <= 0 || k < 1 || k > kMaxK || k > n_experts) return MOE_FP4_ERR_INVALID_ARG;
-  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
-  if ((size_t)k * (size_t)inter * 2 > (size_t)kMaxLdsH) return MOE_FP4_ERR_BAD_SHAPE;
-  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(packed) ||
+  if (!valid_dim(hidden) || !valid_dim(inter) || !lds_fits(k, inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned4(topk_ids) || !aligned4(topk_w) || !aligned16(packed) ||
       !aligned16(y) || !aligned16(workspace))
     return MOE_FP4_ERR_MISALIGNED;
   if (workspace_bytes < moe_fp4_workspace_bytes(T, k, n_experts, hidden, inter))
     return MOE_FP4_ERR_WORKSPACE;
   if (T == 0) return MOE_FP4_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint8_t* pk = static_cast<const uint8_t*>(packed);
-  uint16_t* hbuf = static_cast<uint16_t*>(workspace);
-  hipError_t e = launch_gate_up(x, topk_ids, nullptr, T, k, nullptr, nullptr, pk, n_experts,
-                                hidden, inter, hbuf, s);
-  if (e != hipSuccess) return MOE_FP4_ERR_HIP;
-  return from_hip((launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden,
-                                                    inter, hbuf, y, s)));
+  return from_hip(ffn_impl(x, topk_ids, topk_w, T, k, static_cast<const uint8_t*>(packed),
+                           n_experts, hidden, inter, y, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_fp4_moe_forward_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
@@ -198,32 +215,25 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
     return MOE_FP4_ERR_INVALID_ARG;
   int st = check_topk_args(T, n_experts, k);
   if (st != MOE_FP4_OK) return st;
-  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
-  if ((size_t)k * (size_t)inter * 2 > (size_t)kMaxLdsH) return MOE_FP4_ERR_BAD_SHAPE;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(packed) || !aligned16(topk_ids) ||
-      !aligned16(topk_w) || !aligned16(y) || !aligned16(workspace))
+  if (!valid_dim(hidden) || !valid_dim(inter) || !lds_fits(k, inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(packed) || !aligned4(topk_ids) ||
+      !aligned4(topk_w) || !aligned16(y) || !aligned16(workspace))
     return MOE_FP4_ERR_MISALIGNED;
   if (workspace_bytes < moe_fp4_moe_forward_workspace_bytes(T, k, n_experts, hidden, inter))
     return MOE_FP4_ERR_WORKSPACE;
   if (T == 0) return MOE_FP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint8_t* pk = static_cast<const uint8_t*>(packed);
-  double* logits = static_cast<double*>(workspace);
-  uint16_t* hbuf = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) +
-                                               moe_fp4_route_workspace_bytes(T, n_experts));
-  if (launch_router_gemv(x, w_router, T, hidden, n_experts, logits, s) != hipSuccess)
+  if (route_impl(x, w_router, T, hidden, n_experts, k, topk_ids, topk_w, workspace, s) != hipSuccess)
     return MOE_FP4_ERR_HIP;
-  if (launch_gate_up(x, nullptr, logits, T, k, topk_ids, topk_w, pk, n_experts, hidden, inter,
-                     hbuf, s) != hipSuccess)
-    return MOE_FP4_ERR_HIP;
-  return from_hip(launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, hbuf,
-                                      y, s));
+  void* ffn_ws = static_cast<uint8_t*>(workspace) + moe_fp4_route_workspace_bytes(T, n_experts);
+  return from_hip(ffn_impl(x, topk_ids, topk_w, T, k, static_cast<const uint8_t*>(packed),
+                           n_experts, hidden, inter, y, ffn_ws, s));
 }
 
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts, int32_t* bad_count,
                          void* stream) {
   if (!topk_ids || !bad_count || T < 0 || k < 1 || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;
-  if (!aligned16(topk_ids)) return MOE_FP4_ERR_MISALIGNED;
+  if (!aligned4(topk_ids)) return MOE_FP4_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(launch_validate_ids(topk_ids, T, k, n_experts, bad_count, s));
 }

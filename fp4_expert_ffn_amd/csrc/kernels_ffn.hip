@@ -37,10 +37,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define MOE_FP4_GU_BATCH 4      // 128-element chunks loaded per wave before use
 #endif
 #ifndef MOE_FP4_DC_WAVES
-#define MOE_FP4_DC_WAVES 8      // wavefronts per down/combine tile
+#define MOE_FP4_DC_WAVES 16     // wavefronts per down/combine tile
+#endif
+#ifndef MOE_FP4_GU_MIN_WAVES
+#define MOE_FP4_GU_MIN_WAVES 5  // wavefronts per SIMD the gate/up kernel must allow
 #endif
 #ifndef MOE_FP4_DC_BATCH
-#define MOE_FP4_DC_BATCH 18     // (expert, chunk) steps loaded per wave before use
+#define MOE_FP4_DC_BATCH 5      // (expert, chunk) steps loaded per wave before use
 #endif
 
 constexpr int kGUWaves = MOE_FP4_GU_WAVES;
@@ -49,6 +52,9 @@ constexpr int kGUBatch = MOE_FP4_GU_BATCH;
 constexpr int kDCWaves = MOE_FP4_DC_WAVES;
 constexpr int kDCThreads = kDCWaves * 64;
 constexpr int kDCBatch = MOE_FP4_DC_BATCH;
+// the down kernel stages a token's h vectors (at most kMaxLdsH bytes) in at most four
+// 16-byte words per thread
+static_assert(4 * kDCThreads * 16 >= 65536, "MOE_FP4_DC_WAVES must be at least 16");
 constexpr int kTile = 16;  // weight rows per tile (MFMA N)
 
 // Weight streams are read once per call: non-temporal loads keep them from displacing
@@ -86,26 +92,22 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int m) {
 // ---------------------------------------------------------------------------------------
 // Stage 1: gate/up/SiLU. Workgroup = one tile of 16 rows of gate and up of one pair; the
 // kGUWaves waves take equal shares of the K chunks, in batches of kGUBatch chunks.
-// PER = 0: the expert comes from ids. PER > 0: from fp64 router logits [T x E], the
-// first wave selecting the token's top-k itself (PER keys per lane); the tile with row 0
-// of slot 0 writes the token's ids and weights.
-// LDS: the token's x (H bf16) followed by one zero 16-byte word.
+// LDS: the token's x (H bf16) followed by four zero 16-byte words.
 // ---------------------------------------------------------------------------------------
-template <int PER>
-__global__ __launch_bounds__(kGUThreads) void gate_up_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, const double* __restrict__ logits,
-    int k, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-    const uint8_t* __restrict__ packed, size_t stride, size_t off_gc, size_t off_uc,
-    size_t off_gs, size_t off_us, int n_experts, int H, int I, int tiles_per_pair,
-    uint16_t* __restrict__ hbuf) {
+// The kernel is kept to MOE_FP4_GU_MIN_WAVES wavefronts per SIMD so that one launch's
+// tiles are resident together (no second round at the end).
+template <int XR>
+__global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(MOE_FP4_GU_MIN_WAVES)))
+void gate_up_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, int k,
+                    const uint8_t* __restrict__ packed, size_t stride, size_t off_gc,
+                    size_t off_uc, size_t off_gs, size_t off_us, int n_experts, int H, int I,
+                    int tiles_per_pair, uint16_t* __restrict__ hbuf) {
   extern __shared__ uint4 smem[];
   __shared__ float red_g[kGUWaves][kTile], red_u[kGUWaves][kTile];
-  __shared__ int s_e;
   const int tile = blockIdx.x;
   const int pair = tile / tiles_per_pair;
   const int row0 = (tile - pair * tiles_per_pair) * kTile;
   const int t = pair / k;
-  const int slot = pair - t * k;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -115,36 +117,9 @@ __global__ __launch_bounds__(kGUThreads) void gate_up_kernel(
   const int nch = (KB + 3) / 4;  // 128-element chunks of K
   const int nx = H / 8;          // 16-byte words of x
 
-  int e;
-  if constexpr (PER > 0) {
-    if (wv == 0) {
-      int sid[8];
-      float sw[8];
-      wave_topk<PER>(logits + (size_t)t * n_experts, n_experts, k, lane, sid, sw);
-      int ej = sid[0];
-#pragma unroll
-      for (int q = 1; q < 8; ++q)
-        if (q == slot) ej = sid[q];
-      if (lane == 0) s_e = ej;
-      if (slot == 0 && row0 == 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (q < k && lane == q) {
-            ids_out[(size_t)t * k + q] = sid[q];
-            w_out[(size_t)t * k + q] = sw[q];
-          }
-        }
-      }
-    }
-    __syncthreads();
-    e = s_e;
-  } else {
-    e = ids[pair];
-    if (e < 0 || e >= n_experts) return;  // whole workgroup
-  }
-
-  // 1. x into registers (indices clamped: every load is issued)
-  constexpr int kXRounds = kMaxDim / 8 / kGUThreads;
+  // 1. x into registers (XR rounds of the workgroup cover H; indices clamped, so every
+  // load is issued). x does not depend on the expert, so it goes first.
+  constexpr int kXRounds = XR;
   uint4 xr[kXRounds];
   const uint4* xv = reinterpret_cast<const uint4*>(x + (size_t)t * H);
 #pragma unroll
@@ -152,6 +127,9 @@ __global__ __launch_bounds__(kGUThreads) void gate_up_kernel(
     xr[r] = make_uint4(0, 0, 0, 0);
     if (r * kGUThreads < nx) xr[r] = xv[min(tid + r * kGUThreads, nx - 1)];
   }
+
+  const int e = ids[pair];
+  if (e < 0 || e >= n_experts) return;  // whole workgroup
 
   // 2. this wave's first batch of weights
   const int c_begin = wv * nch / kGUWaves;
@@ -185,26 +163,38 @@ __global__ __launch_bounds__(kGUThreads) void gate_up_kernel(
     const int i = tid + r * kGUThreads;
     if (r * kGUThreads < nx && i < nx) smem[i] = xr[r];
   }
-  if (tid == 0) smem[nx] = make_uint4(0, 0, 0, 0);
+  if (tid < 4) smem[nx + tid] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
+  // A operand from LDS: the lanes of row 0 (j == 0) read x words 16 c + 4 g + m, the other
+  // lanes the 4-word zero area; byte addresses, the 16 m offset folded into the reads.
+  const char* lds = reinterpret_cast<const char*>(smem);
+  const uint32_t zero_addr = (uint32_t)nx * 16u;
+  const uint32_t a_lane = (j == 0) ? (uint32_t)(64 * g) : zero_addr;
+  const uint32_t a_step = (j == 0) ? 256u : 0u;
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  auto mfma_chunk = [&](uint32_t a_addr, const uint4& wg, const uint4& wu, float fg, float fu) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(lds + a_addr + 16 * m));
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wg, m), fg), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wu, m), fu), accu, 0, 0, 0);
+    }
+  };
   for (int c0 = c_begin; c0 < c_end; c0 += kGUBatch) {
+    if (c0 + kGUBatch <= c_end && 4 * (c0 + kGUBatch) <= KB) {  // wave-uniform: all blocks exist
 #pragma unroll
-    for (int q = 0; q < kGUBatch; ++q) {
-      const int c = c0 + q;
-      const int blk = 4 * c + g;
-      const bool bv = (c < c_end) && (blk < KB);  // wave-uniform c, per-lane blk
-      const uint4 wg = bv ? cg[q] : make_uint4(0, 0, 0, 0);
-      const uint4 wu = bv ? cu[q] : make_uint4(0, 0, 0, 0);
-      const float fg = scale_operand(bv ? sg[q] : 127u);
-      const float fu = scale_operand(bv ? su[q] : 127u);
+      for (int q = 0; q < kGUBatch; ++q)
+        mfma_chunk(a_lane + (uint32_t)(c0 + q) * a_step, cg[q], cu[q], scale_operand(sg[q]),
+                   scale_operand(su[q]));
+    } else {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int ai = (j == 0 && bv) ? (16 * c + 4 * g + m) : nx;
-        const bf16x8_t a = as_bf16x8(smem[ai]);
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wg, m), fg), accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wu, m), fu), accu, 0, 0, 0);
+      for (int q = 0; q < kGUBatch; ++q) {
+        const int c = c0 + q;
+        const bool bv = (c < c_end) && (4 * c + g < KB);  // wave-uniform c, per-lane block
+        mfma_chunk(bv ? a_lane + (uint32_t)c * a_step : zero_addr,
+                   bv ? cg[q] : make_uint4(0, 0, 0, 0), bv ? cu[q] : make_uint4(0, 0, 0, 0),
+                   scale_operand(bv ? sg[q] : 127u), scale_operand(bv ? su[q] : 127u));
       }
     }
     if (c0 + kGUBatch < c_end) load_batch(c0 + kGUBatch);
@@ -229,15 +219,19 @@ __global__ __launch_bounds__(kGUThreads) void gate_up_kernel(
 // ---------------------------------------------------------------------------------------
 // Stage 2: down projection and weighted combine. Workgroup = one tile of 16 output rows of
 // one token. The token's valid slots are put in canonical order (ascending expert id, then
-// weight bits; invalid ids dropped) and the (slot, chunk) steps split evenly over the
-// waves; each wave keeps one accumulator for the slot it is on and stores it to LDS when
-// it moves on. The final sum over waves and slots runs in a fixed order, so permuting a
-// token's (id, weight) pairs gives bit-identical output.
-// Load order per thread: its share of the token's h vectors (into LDS), then its first
-// batch of down weights, so the LDS stores wait only for the h loads.
-// LDS: h of the KT slots (bf16, natural order) then one zero 16-byte word.
+// weight bits, then slot; invalid ids dropped) and the (slot, chunk) steps are split evenly
+// over the kDCWaves waves; each wave keeps one accumulator for the slot it is on and
+// stores it to LDS when it moves on. The final sum over waves and slots runs in a fixed
+// order, so permuting a token's (id, weight) pairs gives bit-identical output.
+// Load order per thread: its share of the token's k h vectors (natural slot order, so the
+// addresses need no routing data), then the ids, then its first batch of down weights,
+// then the LDS stores. Every load is issued (indices clamped to valid data) and every
+// store is unconditional (surplus words go to a dummy LDS word), so the stores wait for
+// the h loads only. Per-slot expert bases and slot numbers sit in one VGPR per lane and
+// are read with readlane at the wave-uniform slot index.
+// LDS: h of the KT slots (bf16, natural order) then four zero 16-byte words and a dummy.
 // ---------------------------------------------------------------------------------------
-template <int KT>
+template <int KT, int HR>
 __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int T,
     const uint8_t* __restrict__ packed, size_t stride, size_t off_dc, size_t off_ds,
@@ -256,15 +250,27 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
   const int g = lane >> 4;
   const int KBI = I / kBlock;
   const int nch = (KBI + 3) / 4;
-  const int hx = I / 8;  // 16-byte words per h vector
+  const int hx = I / 8;      // 16-byte words per h vector
+  const int hw = KT * hx;    // 16-byte words of the token's k h vectors
 
-  // canonical slot order: lane jj < KT of wave 0 ranks slot jj
+  // 1. the token's h vectors into registers (named registers: an array live across the
+  // table code below would be placed in private memory)
+  const uint4* hv = reinterpret_cast<const uint4*>(hbuf + (size_t)t * KT * I);
+  static_assert(HR >= 1 && HR <= 4, "h rounds");
+  uint4 hr0 = hv[min(tid, hw - 1)], hr1 = hr0, hr2 = hr0, hr3 = hr0;
+  if constexpr (HR > 1) hr1 = hv[min(tid + kDCThreads, hw - 1)];
+  if constexpr (HR > 2) hr2 = hv[min(tid + 2 * kDCThreads, hw - 1)];
+  if constexpr (HR > 3) hr3 = hv[min(tid + 3 * kDCThreads, hw - 1)];
+
+  // 2. canonical slot order: lane jj < KT of wave 0 ranks slot jj; lane 0 writes the table
+  // in rank order, entries past the valid slots pointing at expert 0 / slot 0 (used only
+  // by clamped loads whose results are discarded)
   if (tid < 64) {
     const int jj = tid;
     const int ej = (jj < KT) ? ids[(size_t)t * KT + jj] : -1;
     const uint32_t wj = (jj < KT) ? __float_as_uint(wts[(size_t)t * KT + jj]) : 0u;
-    const bool okj = ej >= 0 && ej < n_experts;
-    int rank = 0, nvl = 0;
+    const bool okj = jj < KT && ej >= 0 && ej < n_experts;
+    int rank = 0;
 #pragma unroll
     for (int i = 0; i < KT; ++i) {
       const int ei = __shfl(ej, i, 64);
@@ -272,94 +278,113 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
       const bool oki = ei >= 0 && ei < n_experts;
       const bool before = ei < ej || (ei == ej && (wi < wj || (wi == wj && i < jj)));
       rank += (oki && before) ? 1 : 0;
-      nvl += oki ? 1 : 0;
     }
-    if (jj < KT && okj) {
-      s_sid[rank] = ej;
-      s_slot[rank] = jj;
-      s_w[rank] = __uint_as_float(wj);
+    const int nvl = __popcll(__ballot(okj));
+#pragma unroll
+    for (int r = 0; r < KT; ++r) {
+      const int sr = __ffsll((long long)__ballot(okj && rank == r)) - 1;  // wave-uniform
+      const int src = sr < 0 ? 0 : sr;
+      const int er = __shfl(ej, src, 64);
+      const uint32_t wr = (uint32_t)__shfl((int)wj, src, 64);
+      if (lane == 0) {
+        s_sid[r] = sr < 0 ? 0 : er;
+        s_slot[r] = src;
+        s_w[r] = sr < 0 ? 0.f : __uint_as_float(wr);
+      }
     }
-    if (jj == 0) s_nv = nvl;
+    if (lane == 0) s_nv = nvl;
   }
   for (int i = tid; i < kDCWaves * KT * kTile; i += kDCThreads) (&red[0][0][0])[i] = 0.f;
   __syncthreads();
   const int nv = s_nv;
-  // The slot table is read from LDS with the (wave-uniform) slot index: a select chain over
-  // a register array would be turned back into an indexed private-memory access.
+  // lane p < KT: byte offset of the expert and natural slot of canonical position p. The
+  // offset is added to the kernel argument, so the loads stay global (not flat) loads.
+  const int pl = min(lane, KT - 1);
+  const uint64_t voff = (uint64_t)s_sid[pl] * stride;
+  const int vslot = s_slot[pl];
+  auto base_of = [&](int p) {  // p wave-uniform
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)voff, p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(voff >> 32), p);
+    return packed + (((uint64_t)hi << 32) | lo);
+  };
 
-  // 1. h of the valid slots into registers
-  constexpr int kHRounds = (kMaxLdsH / 16 + kDCThreads - 1) / kDCThreads;
-  const int nwords = nv * hx;
-  uint4 hr[kHRounds];
-#pragma unroll
-  for (int r = 0; r < kHRounds; ++r) {
-    hr[r] = make_uint4(0, 0, 0, 0);
-    if (r * kDCThreads < nwords) {
-      const int c = min(tid + r * kDCThreads, nwords - 1);
-      const int p = c / hx;
-      const int slot = s_slot[p];
-      hr[r] = reinterpret_cast<const uint4*>(hbuf + ((size_t)t * KT + slot) * I)[c - p * hx];
-    }
-  }
-
-  // 2. this wave's first batch of weights. Steps s = p * nch + c (slot p, chunk c).
+  // 3. this wave's first batch of weights. Steps s = p * nch + c (position p, chunk c) are
+  // walked with carried (p, c) counters, all wave-uniform. Steps past this wave's range
+  // repeat its last step (or step 0 when the token has no valid slot), so every load
+  // reads packed data of a real expert.
   const int n_steps = nv * nch;
   const int s_begin = wv * n_steps / kDCWaves;
   const int s_end = (wv + 1) * n_steps / kDCWaves;
   const size_t tbase = (size_t)(row0 / kTile) * kTile * KBI;  // tile-major packed layout
+  const int s_last = max(s_end - 1, 0);
+  const int p_first = min(s_begin, s_last) / nch;
+  const int c_first = min(s_begin, s_last) - p_first * nch;
+  const int p_last = s_last / nch;
+  const int c_last = s_last - p_last * nch;
   uint4 cd[kDCBatch];
   uint32_t sd[kDCBatch];
-  auto load_batch = [&](int s0) {
+  auto load_batch = [&](int s0, int p, int c) {  // (p, c) = coordinates of step s0
 #pragma unroll
     for (int q = 0; q < kDCBatch; ++q) {
-      const int s = min(s0 + q, s_end - 1);
-      const int p = s / nch;
-      const int c = s - p * nch;
-      const uint8_t* base = packed + (size_t)s_sid[p] * stride;
-      const size_t w = tbase + ((4 * c + g < KBI) ? 64 * c + lane : 64 * c);
-      cd[q] = ld_stream(reinterpret_cast<const uint4*>(base + off_dc) + w);
-      sd[q] = ld_scale(base + off_ds + w);
+      const bool in = s0 + q < s_end;
+      const uint8_t* b = base_of(in ? p : p_last);
+      const int cc = in ? c : c_last;
+      const size_t w = tbase + ((4 * cc + g < KBI) ? 64 * cc + lane : 64 * cc);
+      cd[q] = ld_stream(reinterpret_cast<const uint4*>(b + off_dc) + w);
+      sd[q] = ld_scale(b + off_ds + w);
+      if (++c == nch) {
+        c = 0;
+        ++p;
+      }
     }
   };
-  if (s_begin < s_end) load_batch(s_begin);
+  load_batch(s_begin, p_first, c_first);
 
-  // 3. h into LDS
-#pragma unroll
-  for (int r = 0; r < kHRounds; ++r) {
-    const int c = tid + r * kDCThreads;
-    if (r * kDCThreads < nwords && c < nwords) smem[c] = hr[r];
+  // 4. h into LDS
+  const int dummy = hw + 4;
+  {
+    const int c0 = tid, c1 = tid + kDCThreads, c2 = tid + 2 * kDCThreads, c3 = tid + 3 * kDCThreads;
+    smem[c0 < hw ? c0 : dummy] = hr0;
+    if constexpr (HR > 1) smem[c1 < hw ? c1 : dummy] = hr1;
+    if constexpr (HR > 2) smem[c2 < hw ? c2 : dummy] = hr2;
+    if constexpr (HR > 3) smem[c3 < hw ? c3 : dummy] = hr3;
   }
-  if (tid == 0) smem[KT * hx] = make_uint4(0, 0, 0, 0);
+  if (tid < 4) smem[hw + tid] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  const int zero_word = KT * hx;
+  const char* lds = reinterpret_cast<const char*>(smem);
+  const uint32_t zero_addr = (uint32_t)hw * 16u;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  int cur_p = (s_begin < s_end) ? s_begin / nch : 0;
+  int cur_p = p_first;
+  int p = p_first, c = c_first;
+  int hslot = __builtin_amdgcn_readlane(vslot, p_first) * hx;  // first h word of position p
   for (int s0 = s_begin; s0 < s_end; s0 += kDCBatch) {
 #pragma unroll
     for (int q = 0; q < kDCBatch; ++q) {
-      const int s = s0 + q;
-      if (s < s_end) {  // wave-uniform
-        const int p = s / nch;
-        const int c = s - p * nch;
+      if (s0 + q < s_end) {  // wave-uniform
         if (p != cur_p) {  // wave-uniform: flush the finished slot
           if (lane < kTile) red[wv][cur_p][lane] = acc[0];
           acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
           cur_p = p;
+          hslot = __builtin_amdgcn_readlane(vslot, p) * hx;
         }
-        const int blk = 4 * c + g;
-        const bool bv = blk < KBI;
+        const bool bv = 4 * c + g < KBI;
+        const uint32_t a_addr =
+            (j16 == 0 && bv) ? (uint32_t)(hslot + 16 * c + 4 * g) * 16u : zero_addr;
         const uint4 wd = bv ? cd[q] : make_uint4(0, 0, 0, 0);
         const float fs = scale_operand(bv ? sd[q] : 127u);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const int ai = (j16 == 0 && bv) ? (p * hx + 16 * c + 4 * g + m) : zero_word;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(smem[ai]),
-                                                       fp4x8_to_bf16(dword(wd, m), fs), acc, 0, 0, 0);
+          const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(lds + a_addr + 16 * m));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(dword(wd, m), fs), acc, 0, 0, 0);
+        }
+        if (++c == nch) {
+          c = 0;
+          ++p;
         }
       }
     }
-    if (s0 + kDCBatch < s_end) load_batch(s0 + kDCBatch);
+    if (s0 + kDCBatch < s_end) load_batch(s0 + kDCBatch, p, c);  // (p, c): step s0 + kDCBatch
   }
   if (s_begin < s_end && lane < kTile) red[wv][cur_p][lane] = acc[0];
   __syncthreads();
@@ -414,59 +439,66 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint4* __restr
 #undef MOE_FP4_DQ_WORD
 }
 
-template <int PER>
-hipError_t gate_up_launch(const uint16_t* x, const int32_t* ids, const double* logits, int T, int k,
-                          int32_t* ids_out, float* w_out, const uint8_t* packed, int n_experts,
-                          int H, int I, uint16_t* hbuf, hipStream_t s) {
+template <int XR>
+hipError_t gate_up_launch_xr(const uint16_t* x, const int32_t* ids, int T, int k,
+                             const uint8_t* packed, int n_experts, int H, int I, uint16_t* hbuf,
+                             hipStream_t s) {
   const PackedLayout L = packed_layout(H, I);
   const long tiles_per_pair = (I + kTile - 1) / kTile;
   const long blocks = (long)T * k * tiles_per_pair;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  const uint32_t lds = (uint32_t)((H / 8 + 1) * 16);
-  return launch_kernel(kKindGateUp, gate_up_kernel<PER>, dim3((unsigned)blocks), dim3(kGUThreads),
-                       lds, s, x, ids, logits, k, ids_out, w_out, packed, L.stride, L.m[0].codes,
-                       L.m[1].codes, L.m[0].scales, L.m[1].scales, n_experts, H, I,
-                       (int)tiles_per_pair, hbuf);
+  const uint32_t lds = (uint32_t)((H / 8 + 4) * 16);
+  return launch_kernel(kKindGateUp, gate_up_kernel<XR>, dim3((unsigned)blocks), dim3(kGUThreads),
+                       lds, s, x, ids, k, packed, L.stride, L.m[0].codes, L.m[1].codes,
+                       L.m[0].scales, L.m[1].scales, n_experts, H, I, (int)tiles_per_pair, hbuf);
+}
+
+template <int KT, int HR>
+hipError_t down_launch_hr(const int32_t* ids, const float* w, int T, const uint8_t* packed,
+                          int n_experts, int H, int I, const uint16_t* hbuf, uint16_t* y,
+                          hipStream_t s) {
+  const PackedLayout L = packed_layout(H, I);
+  const long tiles = H / kTile;
+  const long blocks = (long)T * tiles;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  const uint32_t lds = (uint32_t)(((size_t)KT * I / 8 + 5) * 16);
+  // allow more than 64 KB of LDS per workgroup (the device has 160 KB per CU)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(down_combine_kernel<KT, HR>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLdsH + 80));
+  if (attr != hipSuccess) return attr;
+  return launch_kernel(kKindDownCombine, down_combine_kernel<KT, HR>, dim3((unsigned)blocks),
+                       dim3(kDCThreads), lds, s, ids, w, T, packed, L.stride, L.m[2].codes,
+                       L.m[2].scales, n_experts, H, I, (int)tiles, hbuf, y);
 }
 
 template <int KT>
 hipError_t down_launch(const int32_t* ids, const float* w, int T, const uint8_t* packed,
                        int n_experts, int H, int I, const uint16_t* hbuf, uint16_t* y,
                        hipStream_t s) {
-  const PackedLayout L = packed_layout(H, I);
-  const long tiles = (H + kTile - 1) / kTile;
-  const long blocks = (long)T * tiles;
-  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  const uint32_t lds = (uint32_t)((size_t)KT * I * 2 + 16);
-  // allow more than 64 KB of LDS per workgroup (the device has 160 KB per CU)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(down_combine_kernel<KT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLdsH + 16));
-  if (attr != hipSuccess) return attr;
-  return launch_kernel(kKindDownCombine, down_combine_kernel<KT>, dim3((unsigned)blocks),
-                       dim3(kDCThreads), lds, s, ids, w, T, packed, L.stride, L.m[2].codes,
-                       L.m[2].scales, n_experts, H, I, (int)tiles, hbuf, y);
+  constexpr int kMaxRounds = (kMaxLdsH / 16 + kDCThreads - 1) / kDCThreads;
+  const int rounds = (KT * I / 8 + kDCThreads - 1) / kDCThreads;
+#define MOE_FP4_DC_LAUNCH(R) \
+  return down_launch_hr<KT, R>(ids, w, T, packed, n_experts, H, I, hbuf, y, s)
+  if (rounds <= 1) MOE_FP4_DC_LAUNCH(1);
+  if (rounds <= 2) MOE_FP4_DC_LAUNCH(2);
+  if (rounds <= 4) MOE_FP4_DC_LAUNCH(4);
+  MOE_FP4_DC_LAUNCH((kMaxRounds > 4 ? kMaxRounds : 4));
+#undef MOE_FP4_DC_LAUNCH
 }
 
 }  // namespace
 
-hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, const double* logits, int T,
-                          int k, int32_t* ids_out, float* w_out, const uint8_t* packed,
+hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, int T, int k, const uint8_t* packed,
                           int n_experts, int hidden, int inter, uint16_t* hbuf, hipStream_t s) {
-  if (!logits)
-    return gate_up_launch<0>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
-  const int per = (n_experts + 63) / 64;
-  if (per <= 2)
-    return gate_up_launch<2>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
-  if (per <= 4)
-    return gate_up_launch<4>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
-  if (per <= 6)
-    return gate_up_launch<6>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
-  if (per <= 8)
-    return gate_up_launch<8>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
-  if (per <= 16)
-    return gate_up_launch<16>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
-  return gate_up_launch<32>(x, ids, logits, T, k, ids_out, w_out, packed, n_experts, hidden, inter, hbuf, s);
+  const int rounds = (hidden / 8 + kGUThreads - 1) / kGUThreads;
+#define MOE_FP4_GU_LAUNCH(R) \
+  return gate_up_launch_xr<R>(x, ids, T, k, packed, n_experts, hidden, inter, hbuf, s)
+  if (rounds <= 1) MOE_FP4_GU_LAUNCH(1);
+  if (rounds <= 2) MOE_FP4_GU_LAUNCH(2);
+  if (rounds <= 4) MOE_FP4_GU_LAUNCH(4);
+  MOE_FP4_GU_LAUNCH(kMaxDim / 8 / kGUThreads);
+#undef MOE_FP4_GU_LAUNCH
 }
 
 hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,

@@ -78,6 +78,115 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const V* __restrict__ lo
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Batch-1 routing in one launch. Workgroup g computes the logits of experts
+// 12 g .. 12 g + 11 (two per wavefront, the x chunks shared by both rows), publishes them
+// and raises its flag; workgroup 0 then waits for every flag and selects the top-k.
+// Flags carry an epoch instead of being reset: every workgroup reads the epoch word at
+// start, flags are set to epoch + 1, and workgroup 0 stores epoch + 1 as the next call's
+// epoch once it has seen them all. No atomic read-modify-write is needed (contended
+// atomics across the eight XCDs cost tens of microseconds at this width), and the initial
+// contents of the synchronisation words do not matter. The wait is bounded: after
+// kSpinLimit polls workgroup 0 proceeds, so the kernel always ends.
+// ---------------------------------------------------------------------------------------
+constexpr int kRouteRowsPerWave = 2;
+constexpr int kRouteWaves = 6;
+constexpr int kRouteRowsPerWG = kRouteRowsPerWave * kRouteWaves;
+constexpr int kRouteThreads = kRouteWaves * 64;
+constexpr unsigned kSpinLimit = 1u << 22;
+
+template <int PER>
+__global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int H, int E, int k,
+    uint32_t* __restrict__ sync, double* __restrict__ logits, int32_t* __restrict__ ids,
+    float* __restrict__ w) {
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint32_t target = sync[0] + 1u;
+
+  // GEMV, fp64 accumulation of the exact bf16 x bf16 products (same order for every row)
+  const int row0 = g * kRouteRowsPerWG + wv * kRouteRowsPerWave;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int chunks = H / 8;
+  double acc[kRouteRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRouteRowsPerWave; ++r) acc[r] = 0.0;
+  constexpr int kBatch = 8;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kBatch) {
+    uint4 a[kBatch], b[kRouteRowsPerWave][kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + u * 64;
+      a[u] = (c < chunks) ? xv[c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < kRouteRowsPerWave; ++r) {
+        const int row = min(row0 + r, E - 1);
+        b[r][u] = (c < chunks) ? reinterpret_cast<const uint4*>(wr + (size_t)row * H)[c]
+                               : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t av[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+#pragma unroll
+      for (int r = 0; r < kRouteRowsPerWave; ++r) {
+        const uint32_t bv[4] = {b[r][u].x, b[r][u].y, b[r][u].z, b[r][u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float p0 = bf16_bits_to_f32(av[q] & 0xffffu) * bf16_bits_to_f32(bv[q] & 0xffffu);
+          const float p1 = bf16_bits_to_f32(av[q] >> 16) * bf16_bits_to_f32(bv[q] >> 16);
+          acc[r] += (double)p0;
+          acc[r] += (double)p1;
+        }
+      }
+    }
+  }
+  // The workgroup's logits go through LDS to wave 0, which stores them all and then
+  // raises the flag with a release: the release orders only the releasing wave's own
+  // stores, so no other wave of the workgroup may store logits.
+  __shared__ double s_logit[kRouteRowsPerWG];
+#pragma unroll
+  for (int r = 0; r < kRouteRowsPerWave; ++r) {
+    acc[r] = group_sum_f64<64>(acc[r]);
+    if (lane == 0) s_logit[wv * kRouteRowsPerWave + r] = acc[r];
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int row = g * kRouteRowsPerWG + lane;
+    if (lane < kRouteRowsPerWG && row < E) logits[row] = s_logit[lane];
+    if (lane == 0) __hip_atomic_store(&sync[1 + g], target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (g != 0) return;
+
+  for (int f = tid; f < G; f += kRouteThreads) {
+    unsigned n = 0;
+    // relaxed polls (an acquire per poll would invalidate this XCD's L2 each time), one
+    // acquire fence once the flag is seen
+    while (__hip_atomic_load(&sync[1 + f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++n > kSpinLimit) break;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+  if (wv == 0) {
+    int sid[8];
+    float sw[8];
+    wave_topk<PER>(logits, E, k, lane, sid, sw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k && lane == j) {
+        ids[j] = sid[j];
+        w[j] = sw[j];
+      }
+    }
+    if (lane == 0) sync[0] = target;
+  }
+}
+
 __global__ __launch_bounds__(1024) void validate_ids_kernel(const int32_t* __restrict__ ids,
                                                            long n, int n_experts,
                                                            int32_t* __restrict__ bad) {
@@ -120,6 +229,27 @@ hipError_t launch_topk(const V* logits, int T, int n_experts, int k, int32_t* id
   if (per <= 8) return launch_kernel(kKindTopk, topk_kernel<V, 8>, grid, block, 0, s, logits, T, n_experts, k, ids, w);
   if (per <= 16) return launch_kernel(kKindTopk, topk_kernel<V, 16>, grid, block, 0, s, logits, T, n_experts, k, ids, w);
   return launch_kernel(kKindTopk, topk_kernel<V, 32>, grid, block, 0, s, logits, T, n_experts, k, ids, w);
+}
+
+hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden, int n_experts,
+                               int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)((n_experts + kRouteRowsPerWG - 1) / kRouteRowsPerWG)), block(kRouteThreads);
+  const int per = (n_experts + 63) / 64;
+#define MOE_FP4_ROUTE_LAUNCH(P)                                                                  \
+  return launch_kernel(kKindRouteDecode, route_decode_kernel<P>, grid, block, 0, s, x, wr, hidden, \
+                       n_experts, k, sync, logits, ids, w)
+  if (per <= 2) MOE_FP4_ROUTE_LAUNCH(2);
+  if (per <= 4) MOE_FP4_ROUTE_LAUNCH(4);
+  if (per <= 6) MOE_FP4_ROUTE_LAUNCH(6);
+  if (per <= 8) MOE_FP4_ROUTE_LAUNCH(8);
+  if (per <= 16) MOE_FP4_ROUTE_LAUNCH(16);
+  MOE_FP4_ROUTE_LAUNCH(32);
+#undef MOE_FP4_ROUTE_LAUNCH
+}
+
+int route_decode_sync_words(int n_experts) {
+  return 1 + (n_experts + kRouteRowsPerWG - 1) / kRouteRowsPerWG;
 }
 
 hipError_t launch_topk_f64(const double* logits, int T, int n_experts, int k, int32_t* ids,

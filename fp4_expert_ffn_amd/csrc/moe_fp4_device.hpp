@@ -97,21 +97,70 @@ __device__ __forceinline__ double f64_from_order_key(uint64_t k) {
   return __longlong_as_double((long long)u);
 }
 
+// Softmax over the k selected logits v[0..k-1] (v[0] the largest, the same v on every
+// lane of the wavefront), fp64, summed in slot order, rounded to fp32: the one definition
+// of the router weights. Lane j < k evaluates slot j's exponential and quotient, so the
+// wavefront pays for one exp and one division instead of k of each; on return every lane
+// holds all k weights.
+__device__ __forceinline__ void topk_softmax_weights(const double (&v)[8], int k, int lane,
+                                                     float (&w)[8]) {
+  double vl = v[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) vl = (lane == j) ? v[j] : vl;
+  const double ex = (lane < k) ? exp(vl - v[0]) : 0.0;
+  const uint64_t exb = (uint64_t)__double_as_longlong(ex);
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)exb, j);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(exb >> 32), j);
+      sum += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+  }
+  const float wl = (float)(ex / sum);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    w[j] = (j < k) ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j)) : 0.f;
+}
+
+// (key, id) order of the selection: larger key first, equal keys by smaller id.
+__device__ __forceinline__ bool topk_before(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
 // Top-k of one row of E logits by a whole wavefront (all 64 lanes active, wave-uniform
-// arguments). Lane l holds the order keys of logits l, l + 64, ... (at most PER per lane);
-// each of the k rounds takes the lane-local best (largest key; a lane's ids ascend, so the
-// first of equal keys has the lowest id), then the wave-wide best via three DPP reductions
-// (high key word, low key word, lowest id among equal keys), and its owner removes it.
-// On return every lane holds ids[j] (descending logit, ties by ascending id) and
-// w[j] = softmax over the k selected logits (fp64, rounded to fp32), for j < k.
-template <int PER, typename V>
+// arguments). Lane l holds the order keys of logits l, l + 64, ... (at most PER per lane)
+// and sorts them once, best first, with an odd-even transposition network. Each of the k
+// rounds then looks only at the lanes' heads: a DPP maximum of the heads' high key words;
+// when a single lane holds it (the usual case) that lane's head is the winner, otherwise
+// the low words and then the ids decide among the tied lanes. The winning lane shifts its
+// list by one. On return every lane holds ids[j] (descending logit, ties by ascending
+// id) and w[j] = softmax over the k selected logits (fp64, rounded to fp32), for j < k.
+template <int PER, bool WEIGHTS = true, typename V>
 __device__ __forceinline__ void wave_topk(const V* __restrict__ row, int E, int k, int lane,
                                           int (&ids)[8], float (&w)[8]) {
   uint64_t key[PER];
+  int kid[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + i * 64;
     key[i] = (e < E) ? f64_order_key((double)row[e]) : 0ull;  // 0: empty slot
+    kid[i] = (e < E) ? e : 0x7fffffff;
+  }
+#pragma unroll
+  for (int pass = 0; pass < PER; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < PER; i += 2) {
+      if (topk_before(key[i + 1], kid[i + 1], key[i], kid[i])) {
+        const uint64_t tk = key[i];
+        key[i] = key[i + 1];
+        key[i + 1] = tk;
+        const int ti = kid[i];
+        kid[i] = kid[i + 1];
+        kid[i + 1] = ti;
+      }
+    }
   }
   double v[8];
 #pragma unroll
@@ -119,35 +168,39 @@ __device__ __forceinline__ void wave_topk(const V* __restrict__ row, int E, int 
     ids[j] = 0;
     v[j] = 0.0;
     if (j < k) {
-      uint64_t bk = 0ull;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (key[i] > bk) {
-          bk = key[i];
-          bi = lane + i * 64;
-        }
+      const uint32_t hk = (uint32_t)(key[0] >> 32);
+      const uint32_t hi = wave_max_u32(hk);
+      const unsigned long long tied = __ballot(hk == hi);
+      int wl;
+      uint64_t mk;
+      if (__popcll(tied) == 1) {  // wave-uniform
+        wl = __ffsll((long long)tied) - 1;
+        mk = ((uint64_t)hi << 32) | (uint32_t)__builtin_amdgcn_readlane((uint32_t)key[0], wl);
+      } else {
+        const uint32_t lo = wave_max_u32(hk == hi ? (uint32_t)key[0] : 0u);
+        mk = ((uint64_t)hi << 32) | lo;
+        const uint32_t mid = wave_min_u32(key[0] == mk ? (uint32_t)kid[0] : 0xffffffffu);
+        wl = (int)(mid & 63u);  // a lane's ids are congruent to the lane mod 64
       }
-      const uint32_t hi = wave_max_u32((uint32_t)(bk >> 32));
-      const uint32_t lo = wave_max_u32(((uint32_t)(bk >> 32) == hi) ? (uint32_t)bk : 0u);
-      const uint64_t mk = ((uint64_t)hi << 32) | lo;
-      const uint32_t win = wave_min_u32(bk == mk ? (uint32_t)bi : 0xffffffffu);
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (lane + i * 64 == (int)win) key[i] = 0ull;
-      ids[j] = (int)win;
+      ids[j] = __builtin_amdgcn_readlane(kid[0], wl);
       v[j] = f64_from_order_key(mk);
+      if (lane == wl) {
+#pragma unroll
+        for (int i = 0; i + 1 < PER; ++i) {
+          key[i] = key[i + 1];
+          kid[i] = kid[i + 1];
+        }
+        key[PER - 1] = 0ull;
+        kid[PER - 1] = 0x7fffffff;
+      }
     }
   }
-  double ex[8];
-  double sum = 0.0;
+  if constexpr (WEIGHTS) {
+    topk_softmax_weights(v, k, lane, w);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ex[j] = (j < k) ? exp(v[j] - v[0]) : 0.0;
-    sum += ex[j];
+    for (int j = 0; j < 8; ++j) w[j] = 0.f;
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = (j < k) ? (float)(ex[j] / sum) : 0.f;
 }
 
 __device__ __forceinline__ float silu_f32(float z) {

@@ -13,12 +13,12 @@ namespace moe_fp4 {
 constexpr int kBlock = 32;        // elements per ue8m0 scale block along K
 constexpr int kMaxK = 8;          // max experts per token
 constexpr int kMaxDim = 16384;    // max hidden / inter
-constexpr int kMaxExpertsTopk = 2048;  // max experts for the top-k selection kernel
 constexpr int kMaxLdsH = 65536;   // bytes of LDS for the k staged h vectors of one token
+constexpr int kMaxExpertsTopk = 2048;  // max experts for the top-k selection kernel
 
 // Kernel kinds for timing (same values as MOE_FP4_KERNEL_* in the public header).
 enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp = 3,
-                  kKindDownCombine = 4 };
+                  kKindDownCombine = 4, kKindRouteDecode = 5 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -94,15 +94,19 @@ hipError_t launch_pack(const uint8_t* codes, const uint8_t* scales, int n_expert
 hipError_t launch_router_gemv(const uint16_t* x, const uint16_t* wr, int T, int hidden,
                               int n_experts, double* logits, hipStream_t s);
 
+// Batch-1 routing in one launch (GEMV + top-k); sync: route_decode_sync_words(E) words
+// that persist between calls (their initial contents do not matter).
+hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden, int n_experts,
+                               int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
+                               hipStream_t s);
+int route_decode_sync_words(int n_experts);
+
 hipError_t launch_topk_f64(const double* logits, int T, int n_experts, int k, int32_t* ids,
                            float* w, hipStream_t s);
 hipError_t launch_topk_f32(const float* logits, int T, int n_experts, int k, int32_t* ids,
                            float* w, hipStream_t s);
 
-// ids != nullptr: experts from ids. Otherwise from fp64 logits [T x n_experts] (top-k
-// selected in the kernel; ids_out / w_out [T x k] receive the selection).
-hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, const double* logits, int T,
-                          int k, int32_t* ids_out, float* w_out, const uint8_t* packed,
+hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, int T, int k, const uint8_t* packed,
                           int n_experts, int hidden, int inter, uint16_t* hbuf, hipStream_t s);
 
 hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,

@@ -27,7 +27,7 @@ ERR_WORKSPACE = -4
 ERR_HIP = -5
 
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
-KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine")
+KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode")
 
 
 class MoeFp4Error(RuntimeError):

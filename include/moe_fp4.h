@@ -26,9 +26,11 @@
  *    Faults inside a kernel surface at the caller's next synchronisation.
  *  - T = 0 (no tokens) is a no-op that returns MOE_FP4_OK.
  *  - Shapes: hidden and inter must be positive multiples of 32 and at most 16384;
- *    1 <= k <= min(n_experts, 8); k * inter <= 32768 for moe_fp4_expert_ffn (the k h
- *    vectors of a token are staged in 64 KB of LDS); every device pointer must be
- *    16-byte aligned.
+ *    1 <= k <= min(n_experts, 8); k * inter <= 32768 for moe_fp4_expert_ffn and
+ *    moe_fp4_moe_forward (the k h vectors of a token are staged in 64 KB of LDS).
+ *  - Alignment: topk_ids, topk_w and the fp32 logits of moe_fp4_route_logits must be
+ *    4-byte aligned (so a row slice of a [T x k] array can be passed); every other device
+ *    pointer (activations, weights, packed experts, outputs, workspaces) 16-byte aligned.
  */
 #ifndef MOE_FP4_H
 #define MOE_FP4_H
@@ -43,7 +45,7 @@ extern "C" {
 #define MOE_FP4_OK 0
 #define MOE_FP4_ERR_INVALID_ARG (-1)   /* null pointer, negative size, k out of range */
 #define MOE_FP4_ERR_BAD_SHAPE (-2)     /* hidden or inter not a multiple of 32 / too large */
-#define MOE_FP4_ERR_MISALIGNED (-3)    /* a device pointer is not 16-byte aligned */
+#define MOE_FP4_ERR_MISALIGNED (-3)    /* a device pointer breaks the alignment rule above */
 #define MOE_FP4_ERR_WORKSPACE (-4)     /* workspace or packed buffer smaller than required */
 #define MOE_FP4_ERR_HIP (-5)           /* a HIP launch or runtime call failed */
 
@@ -98,7 +100,11 @@ size_t moe_fp4_route_workspace_bytes(int T, int n_experts);
 
 /* x [T x hidden] bf16, w_router [n_experts x hidden] bf16 (row-major), outputs
  * topk_ids int32 [T x k], topk_w fp32 [T x k]. workspace: device scratch of at least
- * moe_fp4_route_workspace_bytes(T, n_experts) bytes (contents on entry are ignored).
+ * moe_fp4_route_workspace_bytes(T, n_experts) bytes, owned by the caller. Its first 4 KB
+ * hold synchronisation words that a batch-1 call (T == 1: GEMV and selection in one
+ * launch) carries from call to call; their initial contents do not matter, the caller
+ * must not write them between calls, and calls that may run concurrently need distinct
+ * workspaces. The rest is scratch whose contents on entry are ignored.
  * Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, HIP. */
 int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden, int n_experts,
                   int k, int32_t* topk_ids, float* topk_w, void* workspace,
@@ -120,24 +126,28 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
  * h is rounded to bf16 before the down projection, y is rounded to bf16.
  * ------------------------------------------------------------------------------------ */
 
-/* Workspace bytes moe_fp4_expert_ffn needs. */
+/* Workspace bytes moe_fp4_expert_ffn needs: h of every (token, slot) pair (bf16).
+ * 0 for invalid arguments. */
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter);
 
 /* x [T x hidden] bf16; topk_ids int32 [T x k]; topk_w fp32 [T x k];
  * packed: the output of moe_fp4_pack for n_experts experts; y [T x hidden] bf16 (output,
- * may not alias x); workspace of at least moe_fp4_workspace_bytes(...) bytes.
+ * may not alias x); workspace of at least moe_fp4_workspace_bytes(...) bytes, owned by the
+ * caller, contents on entry ignored; calls that may run concurrently need distinct
+ * workspaces.
  * Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, WORKSPACE, HIP. */
 int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                        int k, const void* packed, int n_experts, int hidden, int inter,
                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
- * Whole routed-expert layer in one call: moe_fp4_route followed by moe_fp4_expert_ffn,
- * with the top-k selection folded into the first FFN kernel (three kernel launches in all:
- * router GEMV, gate/up/SiLU with selection, down + combine). Same results as the two calls
- * in sequence: topk_ids / topk_w receive the routing (bit-identical to moe_fp4_route), y
- * the layer output. Cutting launches per layer is the pages' own lesson ([A100-FP4],
- * section 然后又发现每 token 启动 2000 次内核).
+ * Whole routed-expert layer in one call: moe_fp4_route followed by moe_fp4_expert_ffn on
+ * one workspace (three kernel launches for a batch-1 call: router GEMV with selection,
+ * gate/up/SiLU, down + combine). Same results as the two calls in sequence: topk_ids /
+ * topk_w receive the routing (bit-identical to moe_fp4_route), y the layer output
+ * (bit-identical to moe_fp4_expert_ffn). Cutting launches per layer is the pages' own
+ * lesson ([A100-FP4], section 然后又发现每 token 启动 2000 次内核). The workspace's first
+ * 4 KB follow the rules given for moe_fp4_route.
  * ------------------------------------------------------------------------------------ */
 
 /* Workspace bytes moe_fp4_moe_forward needs. */
@@ -177,7 +187,8 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
 #define MOE_FP4_KERNEL_TOPK 2
 #define MOE_FP4_KERNEL_GATE_UP 3
 #define MOE_FP4_KERNEL_DOWN_COMBINE 4
-#define MOE_FP4_KERNEL_KINDS 5
+#define MOE_FP4_KERNEL_ROUTE_DECODE 5 /* batch-1 router GEMV + selection in one launch */
+#define MOE_FP4_KERNEL_KINDS 6
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

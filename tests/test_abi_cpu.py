@@ -14,7 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_fp4.h")
 
 A = 0x10000  # an aligned fake device address (never dereferenced)
-MIS = 0x10008  # misaligned
+MIS = 0x10008  # misaligned for 16-byte pointers
+MIS4 = 0x10002  # misaligned for 4-byte pointers (ids, weights, fp32 logits)
 
 
 def _declared_functions():
@@ -59,6 +60,7 @@ def test_workspace_sizes():
     assert C.moe_fp4_workspace_bytes(1, 6, 384, 4096, 2880) >= 6 * 2880 * 2
     assert C.moe_fp4_workspace_bytes(8192, 6, 384, 4096, 2880) >= 8192 * 6 * 2880 * 2
     assert C.moe_fp4_route_workspace_bytes(1, 384) >= 384 * 8
+    assert C.moe_fp4_workspace_bytes(1, 6, 384, 4010, 2880) == 0  # hidden not a multiple of 32
 
 
 def ffn(L, x=A, ids=A, w=A, T=1, k=6, packed=A, E=384, H=4096, I=2880, y=A, ws=A, wsb=1 << 20):
@@ -79,6 +81,9 @@ def test_expert_ffn_argument_checks(L):
     assert ffn(L, k=8, I=8192) == C.ERR_BAD_SHAPE          # k * inter > 32768
     assert ffn(L, x=MIS) == C.ERR_MISALIGNED
     assert ffn(L, packed=MIS) == C.ERR_MISALIGNED
+    assert ffn(L, ids=MIS4) == C.ERR_MISALIGNED
+    assert ffn(L, w=MIS4) == C.ERR_MISALIGNED
+    assert ffn(L, ids=A + 4, w=A + 12, wsb=8) == C.ERR_WORKSPACE
     assert ffn(L, wsb=100) == C.ERR_WORKSPACE
     # T = 0 is a no-op: OK without touching any pointer
     assert ffn(L, T=0, wsb=0) == C.OK
@@ -92,7 +97,11 @@ def test_route_argument_checks(L):
     assert route(k=7, E=6) == C.ERR_INVALID_ARG
     assert route(E=4096) == C.ERR_BAD_SHAPE
     assert route(H=31) == C.ERR_BAD_SHAPE
-    assert route(ids=MIS) == C.ERR_MISALIGNED
+    assert route(x=MIS) == C.ERR_MISALIGNED
+    assert route(ids=MIS4) == C.ERR_MISALIGNED
+    assert route(w=MIS4) == C.ERR_MISALIGNED
+    # ids / weights only need 4-byte alignment: the check passes and the workspace one fires
+    assert route(ids=A + 4, w=A + 8, wsb=8) == C.ERR_WORKSPACE
     assert route(wsb=8) == C.ERR_WORKSPACE
     assert route(T=0) == C.OK
     assert L.moe_fp4_route_logits(A, 0, 384, 6, A, A, None) == C.OK

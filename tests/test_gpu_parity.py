@@ -123,6 +123,29 @@ def test_route_ids_bit_exact_full_size(dev):
     check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, "route")
 
 
+@pytest.mark.parametrize("n_experts,k", [(384, 6), (20, 3), (64, 8), (200, 1)])
+def test_route_batch1_sequence(dev, n_experts, k):
+    """Batch-1 routing takes the one-launch path (its workspace keeps synchronisation words
+    from call to call): consecutive calls on one workspace with different tokens must each
+    match the oracle, including a token with exact ties among the top scores."""
+    C, D = _mods()
+    wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
+    wr_bits = S.router_weights(wl, 0)[:n_experts].copy()
+    wr_bits[n_experts - 1] = wr_bits[3]
+    layer = D.MoeFp4Layer(torch.empty(256, dtype=torch.uint8, device=dev), n_experts,
+                          wl.hidden, wl.inter, k, D.upload_bf16(wr_bits, dev))
+    for step in range(12):
+        x_bits = S.activations(wl, 0, 1000 + step)
+        if step == 5:
+            x_bits = wr_bits[3:4].copy()
+        ids_ref, w_ref, _ = O.route(x_bits, wr_bits, k)
+        ids, w = layer.route(D.upload_bf16(x_bits, dev))
+        torch.cuda.synchronize()
+        check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"step {step}")
+        if step == 5 and k >= 2:
+            assert list(ids_ref[0][:2]) == [3, n_experts - 1]
+
+
 @pytest.mark.parametrize("routing", ["zipf", "uniform", "ties"])
 def test_route_logits_bit_exact(dev, routing):
     C, D = _mods()
