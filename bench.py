@@ -43,6 +43,30 @@ def gate_up_bytes(hidden: int, inter: int) -> int:
     return n // 2 + n // 32
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_layer_hbm_traffic.md")
+KERNEL_SOURCES = {"gate_up_kernel": "kernels_ffn.hip", "down_combine_kernel": "kernels_ffn.hip",
+                  "route_decode_kernel": "kernels_route.hip"}
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the summary is
+    missing or the kernel's source has changed since the counters were taken."""
+    import hashlib
+
+    try:
+        lines = open(TRAFFIC_SUMMARY).read().splitlines()
+        src = os.path.join(ROOT, "fp4_expert_ffn_amd", "csrc", KERNEL_SOURCES[kernel])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, KeyError):
+        return None
+    for line in lines:
+        f = line.split()
+        if len(f) == 5 and f[0] == "traffic_bytes_per_launch" and f[1] == kernel and f[3] == "source":
+            return int(f[2]) if f[4] == digest else None
+    return None
+
+
 def cpu_baseline(wl, n_tokens: int, first_step: int):
     """Time the fp64 oracle (route + expert FFN) on the host for a bounded sample of the
     same workload: n_tokens tokens, one BLAS thread."""
@@ -81,6 +105,9 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="before the steps, run a plain elementwise copy of 256 MiB three times "
+                         "(a known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -109,6 +136,15 @@ def main() -> int:
     xs_bits = np.concatenate([S.activations(wl, 0, s) for s in range(n_x)])
     xs = D.upload_bf16(xs_bits, dev)
     log(f"setup done in {time.time() - t0:.1f} s")
+
+    if args.pmc_calibration:
+        # 64 Mi fp32 elements: 268,435,456 B read and 268,435,456 B written per launch
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ids = torch.empty((1, k), dtype=torch.int32, device=dev)
     w = torch.empty((1, k), dtype=torch.float32, device=dev)
@@ -186,7 +222,8 @@ def main() -> int:
             achieved = alg / (gu["avg_us"] * 1e-6) / 1e9
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": None, "kernel": "gate_up", "bytes_per_launch": alg,
+                        "traffic": measured_traffic("gate_up_kernel"), "kernel": "gate_up",
+                        "bytes_per_launch": alg,
                         "avg_launch_us": round(gu["avg_us"], 3)}
         log("kernels: " + json.dumps(kernels))
 
