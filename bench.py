@@ -102,7 +102,7 @@ def main() -> int:
     ap.add_argument("--api", choices=["fused", "split"], default="fused",
                     help="fused: one moe_fp4_moe_forward call; split: moe_fp4_route then "
                          "moe_fp4_expert_ffn (three kernel launches either way)")
-    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
     ap.add_argument("--pmc-calibration", action="store_true",
