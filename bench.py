@@ -96,6 +96,11 @@ def cpu_baseline(wl, n_tokens: int, first_step: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default="layer_decode_h4096_i2880_e384",
+                    choices=["layer_decode_h4096_i2880_e384", "batched64_zipf", "prefill8192_uniform",
+                             "prefill32768_uniform"],
+                    help="the batch-1 decode layer (default, the headline line), or one of the "
+                         "batched shapes run through the grouped GEMM path")
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=["graph", "stream"], default="graph")
@@ -114,6 +119,9 @@ def main() -> int:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build runs on a single MI355X).", file=sys.stderr)
         return 2
+
+    if args.workload != "layer_decode_h4096_i2880_e384":
+        return run_batched(args)
 
     import torch
 
@@ -252,6 +260,158 @@ def main() -> int:
         "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
         "hbm_frac_step": round(step_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_step": step_bytes,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 (the f8f6f4 MFMA runs at this rate with an FP8 operand)
+
+
+def run_batched(args) -> int:
+    """A batched step: top-k of the step's router logits (drawn directly, as the workload
+    defines them) then moe_fp4_expert_ffn, which takes the grouped GEMM path. Fresh logits
+    every step, so the experts read and their token counts change from step to step."""
+    import torch
+
+    from fp4_expert_ffn_amd import device as D
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    from synth import moe_inputs as S
+
+    C.lib()
+    dev = torch.device("cuda:0")
+    wl = S.WORKLOADS[args.workload]
+    H, I, E, k, T = wl.hidden, wl.inter, wl.n_experts, wl.k, wl.tokens
+    # bounded so one run stays within about a minute of GPU time
+    K = min(args.steps, 100 if T <= 64 else 10)
+    W = min(args.warmup, 10 if T <= 64 else 2)
+    log(f"{wl.name}: uploading {E} experts")
+    packed = D.upload_experts(S.expert_source(wl, 0), E, H, I, dev, chunk=32)
+    layer = D.MoeFp4Layer(packed, E, H, I, k)
+    n_lg = W + 2 * K
+    lgs = torch.stack([torch.from_numpy(S.router_logits(wl, 0, i)) for i in range(n_lg)]).to(dev)
+    xs = [D.upload_bf16(S.activations(wl, 0, i), dev) for i in range(2)]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    layer._workspace(T, k)
+
+    def step(i: int) -> None:
+        C.moe_fp4_route_logits(lgs[i], T, E, k, ids, w)
+        layer.ffn(xs[i % 2], ids, w, y)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if args.mode == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(W, W + K):
+                step(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(W, W + K):
+            step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed_s = max(gpu_ms / 1e3, 1e-9)
+
+    # distinct experts per step (outside the timed region)
+    distinct = []
+    for i in range(W, W + K):
+        C.moe_fp4_route_logits(lgs[i], T, E, k, ids, w)
+        distinct.append(int(torch.unique(ids).numel()))
+    d_avg = float(np.mean(distinct))
+    pairs = T * k
+    flops = pairs * 6.0 * H * I
+    step_bytes = d_avg * expert_bytes(H, I) + 2 * T * H * 2 + T * E * 4 + pairs * 8
+    tflops = flops * K / elapsed_s / 1e12
+    log(f"timed {K} steps ({args.mode}): {gpu_ms:.3f} ms -> {gpu_ms / K:.3f} ms/step, "
+        f"{tflops:.1f} TFLOP/s, {step_bytes * K / elapsed_s / 1e9:.0f} GB/s, {d_avg:.1f} experts/step")
+
+    kernels = {}
+    roofline = None
+    if not args.no_roofline_pass:
+        C.moe_fp4_timing_reset()
+        C.moe_fp4_timing_enable(True)
+        for i in range(W + K, W + 2 * K):
+            step(i)
+        torch.cuda.synchronize()
+        C.moe_fp4_timing_enable(False)
+        for kind, name in enumerate(C.KERNEL_NAMES):
+            n, ms = C.moe_fp4_timing_read(kind)
+            if n:
+                kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+        C.moe_fp4_timing_reset()
+        gu = kernels.get("grouped_gate_up")
+        if gu:
+            t_s = gu["avg_us"] * 1e-6
+            if wl.tokens >= 32768:  # enough tokens per expert for a matrix-core bound
+                achieved = pairs * 4.0 * H * I / t_s / 1e12
+                roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                            "traffic": None, "kernel": "grouped_gate_up",
+                            "flops_per_launch": pairs * 4.0 * H * I, "avg_launch_us": round(gu["avg_us"], 3)}
+            else:
+                Hp, Ip = (H + 127) // 128 * 128, (I + 127) // 128 * 128
+                alg = d_avg * gate_up_bytes(H, I) + T * Hp * 2 * (1 + 1 / 32) + pairs * Ip * 2 * (1 + 1 / 32)
+                achieved = alg / t_s / 1e9
+                roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "grouped_gate_up", "bytes_per_launch": round(alg),
+                            "avg_launch_us": round(gu["avg_us"], 3)}
+        log("kernels: " + json.dumps(kernels))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import moe_oracle as O
+
+        n_tok = min(args.cpu_tokens, 8)
+        lg = S.router_logits(wl, 0, W).astype(np.float64)[:n_tok]
+        x_bits = S.activations(wl, 0, W % 2)[:n_tok]
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ids_o, w_o = O.topk_softmax(lg, k)
+            O.expert_ffn(x_bits, ids_o, w_o, S.expert_source(wl, 0), E, H, I)
+            dt = time.perf_counter() - t0
+        cpu = {"value": n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_tok} tokens of one step (top-k + expert FFN, fp64 NumPy, 1 thread), {dt:.1f} s"}
+
+    out = {
+        "metric": "batched FP4 TFLOP/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(gpu_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8(hi+lo) x fp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
+                   "tokens": T, "routing": wl.routing, "launch": args.mode, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(T * K / elapsed_s, 1),
+        "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
+        "distinct_experts_per_step": d_avg,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

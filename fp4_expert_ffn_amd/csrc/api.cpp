@@ -1,5 +1,6 @@
 // C ABI of the routed FP4 expert FFN library: argument checks, workspace sizing, kernel
 // dispatch on the caller's stream, and the optional kernel timing hooks.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -165,31 +166,56 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
   return from_hip((launch_topk_f32(logits, T, n_experts, k, topk_ids, topk_w, s)));
 }
 
+// Token count from which the automatic path choice takes the grouped GEMM path.
+constexpr int kGroupedMinTokens = 16;
+
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
-  (void)n_experts;
-  if (T < 0 || k < 1 || k > kMaxK || !valid_dim(hidden) || !valid_dim(inter)) return 0;
-  // h for every (token, slot) pair, bf16
-  return align256((size_t)T * (size_t)k * (size_t)inter * 2);
+  if (T < 0 || k < 1 || k > kMaxK || n_experts <= 0 || !valid_dim(hidden) || !valid_dim(inter))
+    return 0;
+  if (T == 0) return 0;
+  // decode path: h for every (token, slot) pair, bf16; grouped path: see batched_layout
+  const size_t decode = align256((size_t)T * (size_t)k * (size_t)inter * 2);
+  const size_t grouped = batched_layout(T, k, n_experts, hidden, inter).bytes;
+  return std::max(decode, grouped);
 }
 
-// Both FFN stages; the workspace holds h.
+static bool lds_fits(int k, int inter) { return (size_t)k * (size_t)inter * 2 <= (size_t)kMaxLdsH; }
+
+// The FFN on a workspace of moe_fp4_workspace_bytes; path already validated.
 static hipError_t ffn_impl(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                            int k, const uint8_t* pk, int n_experts, int hidden, int inter,
-                           uint16_t* y, void* workspace, hipStream_t s) {
+                           uint16_t* y, void* workspace, int path, hipStream_t s) {
+  if (path == MOE_FP4_PATH_GROUPED)
+    return launch_batched_ffn(x, topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, y,
+                              workspace, s);
   uint16_t* hbuf = static_cast<uint16_t*>(workspace);
   hipError_t e = launch_gate_up(x, topk_ids, T, k, pk, n_experts, hidden, inter, hbuf, s);
   if (e != hipSuccess) return e;
   return launch_down_combine(topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, hbuf, y, s);
 }
 
-static bool lds_fits(int k, int inter) { return (size_t)k * (size_t)inter * 2 <= (size_t)kMaxLdsH; }
+// Resolves MOE_FP4_PATH_AUTO and checks the shape limits of the chosen path.
+static int choose_path(int path, int T, int k, int n_experts, int inter) {
+  if (path == MOE_FP4_PATH_AUTO) {
+    path = (T >= kGroupedMinTokens && n_experts <= kMaxExpertsTopk) ? MOE_FP4_PATH_GROUPED
+                                                                    : MOE_FP4_PATH_DECODE;
+    if (path == MOE_FP4_PATH_DECODE && !lds_fits(k, inter) && n_experts <= kMaxExpertsTopk)
+      path = MOE_FP4_PATH_GROUPED;
+  }
+  if (path == MOE_FP4_PATH_DECODE) return lds_fits(k, inter) ? path : MOE_FP4_ERR_BAD_SHAPE;
+  if (path == MOE_FP4_PATH_GROUPED) return n_experts <= kMaxExpertsTopk ? path : MOE_FP4_ERR_BAD_SHAPE;
+  return MOE_FP4_ERR_INVALID_ARG;
+}
 
-int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
-                       int k, const void* packed, int n_experts, int hidden, int inter,
-                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+int moe_fp4_expert_ffn_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
+                          int k, const void* packed, int n_experts, int hidden, int inter,
+                          uint16_t* y, void* workspace, size_t workspace_bytes, int path,
+                          void* stream) {
   if (!x || !topk_ids || !topk_w || !packed || !y || !workspace) return MOE_FP4_ERR_INVALID_ARG;
   if (T < 0 || n_experts <= 0 || k < 1 || k > kMaxK || k > n_experts) return MOE_FP4_ERR_INVALID_ARG;
-  if (!valid_dim(hidden) || !valid_dim(inter) || !lds_fits(k, inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  const int chosen = choose_path(path, T, k, n_experts, inter);
+  if (chosen < 0) return chosen;
   if (!aligned16(x) || !aligned4(topk_ids) || !aligned4(topk_w) || !aligned16(packed) ||
       !aligned16(y) || !aligned16(workspace))
     return MOE_FP4_ERR_MISALIGNED;
@@ -197,7 +223,15 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
     return MOE_FP4_ERR_WORKSPACE;
   if (T == 0) return MOE_FP4_OK;
   return from_hip(ffn_impl(x, topk_ids, topk_w, T, k, static_cast<const uint8_t*>(packed),
-                           n_experts, hidden, inter, y, workspace, static_cast<hipStream_t>(stream)));
+                           n_experts, hidden, inter, y, workspace, chosen,
+                           static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int k, const void* packed, int n_experts, int hidden, int inter,
+                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_fp4_expert_ffn_ex(x, topk_ids, topk_w, T, k, packed, n_experts, hidden, inter, y,
+                               workspace, workspace_bytes, MOE_FP4_PATH_AUTO, stream);
 }
 
 size_t moe_fp4_moe_forward_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
@@ -215,7 +249,9 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
     return MOE_FP4_ERR_INVALID_ARG;
   int st = check_topk_args(T, n_experts, k);
   if (st != MOE_FP4_OK) return st;
-  if (!valid_dim(hidden) || !valid_dim(inter) || !lds_fits(k, inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  const int chosen = choose_path(MOE_FP4_PATH_AUTO, T, k, n_experts, inter);
+  if (chosen < 0) return chosen;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(packed) || !aligned4(topk_ids) ||
       !aligned4(topk_w) || !aligned16(y) || !aligned16(workspace))
     return MOE_FP4_ERR_MISALIGNED;
@@ -227,7 +263,7 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
     return MOE_FP4_ERR_HIP;
   void* ffn_ws = static_cast<uint8_t*>(workspace) + moe_fp4_route_workspace_bytes(T, n_experts);
   return from_hip(ffn_impl(x, topk_ids, topk_w, T, k, static_cast<const uint8_t*>(packed),
-                           n_experts, hidden, inter, y, ffn_ws, s));
+                           n_experts, hidden, inter, y, ffn_ws, chosen, s));
 }
 
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts, int32_t* bad_count,

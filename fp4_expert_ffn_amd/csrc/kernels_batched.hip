@@ -1,0 +1,678 @@
+// Batched routed expert FFN: (token, slot) pairs grouped by expert, then a grouped GEMM on the
+// block-scaled matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4). Used where several tokens
+// share an expert, so each expert's FP4 weights are streamed once per 64 of its tokens
+// instead of once per token.
+//
+// 1. sort_kernel: histogram of the valid ids over experts, exclusive scan, scatter of pair
+//    indices into expert order (perm), and a table of 64-row M-blocks per expert. The order
+//    of pairs inside an expert's group is not fixed (LDS atomics), and nothing depends on
+//    it: every MFMA row is computed on its own, with the same K order.
+// 2. quant_x_kernel: x -> two-term MXFP8 (E4M3) hi + lo with one ue8m0 scale per 32 elements
+//    each. The pair reproduces bf16 inputs to about 2^-8 of the block maximum; one FP8 term
+//    alone does not meet the output tolerance. The scale exponent is the smallest X with
+//    max|v| <= 448 * 2^X, so no element overflows the E4M3 range.
+// 3. gemm_gate_up_kernel: per (M-block, 64 rows of I): g and u for 64 rows of gate and up,
+//    h = silu(g) * u, quantised in the epilogue to MXFP8 hi + lo (blocks of 32 along I).
+// 4. gemm_down_kernel: per (M-block, 64 rows of H): y_e = W_down h, times the pair's router
+//    weight, written fp32 per pair.
+// 5. combine_kernel: y[t] = sum of the token's valid pairs in canonical slot order (ascending
+//    expert id, then weight bits, then slot) -> bf16.
+//
+// Operand layout of the block-scaled MFMA (16 x 16 x 128), measured on gfx950:
+//  * B, FP4 (4 of the 8 operand dwords used): lane 16 g + j holds column j, K = 32 g + e for
+//    nibble e (low nibble first). One packed tile-major word (tile, chunk c, g, j) is exactly
+//    this operand for weight rows tile * 16 .. + 15 and K = 128 c .. 128 c + 127, so a
+//    wavefront reads its B operand as one contiguous 1 KB load.
+//  * A, FP8 (8 dwords): lane 16 g + r holds row r; byte e sits at K = 64 (e / 16) + 16 g + e % 16,
+//    i.e. two 16-byte pieces of the row at K offsets 16 g and 64 + 16 g.
+//  * Scales: lane (row or column, g) supplies the ue8m0 byte of K-block g (K = 32 g .. + 31)
+//    of its row / column (operand byte 0).
+//  * C: row i, column j at lane j + 16 (i / 4), element i % 4.
+#include <algorithm>
+
+#include "moe_fp4_device.hpp"
+#include "moe_fp4_internal.hpp"
+
+namespace moe_fp4 {
+
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Weight words are read once per M-block: non-temporal loads keep them out of the way of
+// the reused activation rows in the caches.
+__device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr int kBWaves = 4;
+constexpr int kBThreads = kBWaves * 64;
+constexpr int kBN = 16 * kBWaves;       // weight rows per workgroup
+constexpr int kMSub = kBlockRows / 16;  // 16-row MFMA subtiles per M-block
+constexpr int kAPitch = 272;            // LDS bytes per staged A row: hi 128 | lo 128 | pad 16
+constexpr int kSortThreads = 1024;
+
+// ---------------------------------------------------------------------------------------
+// MXFP8 (E4M3) encoding of one 32-element block, two terms.
+// ---------------------------------------------------------------------------------------
+// Smallest X with a <= 448 * 2^X (448 = 1.75 * 2^8, the largest E4M3 value), clamped to the
+// ue8m0 range; a == 0 gives -127.
+__device__ __forceinline__ int mx_exponent(float a) {
+  if (!(a > 0.f)) return -127;
+  const uint32_t b = __float_as_uint(a);
+  int E = (int)((b >> 23) & 0xff) - 127;
+  uint32_t man = b & 0x7fffffu;
+  if (E == -127) {  // subnormal: normalise
+    const int sh = __clz((int)man) - 8;
+    man = (man << sh) & 0x7fffffu;
+    E = -126 - sh;
+  }
+  // mantissa <= 1.75  <=>  man <= 0.75 * 2^23
+  int X = (man <= 0x600000u) ? E - 8 : E - 7;
+  return max(-127, min(127, X));
+}
+
+// v[0..31] (fp32) -> hi, lo E4M3 bytes (16-byte words h0,h1 / l0,l1 in element order) and
+// their scale bytes.
+__device__ __forceinline__ void mx8_encode_block(const float (&v)[32], uint4& h0, uint4& h1,
+                                                 uint4& l0, uint4& l1, uint32_t& sh,
+                                                 uint32_t& sl) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int X = mx_exponent(amax);
+  uint32_t hw[8];
+  float r[32];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    int w = 0;
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * d], -X), ldexpf(v[4 * d + 1], -X), w, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * d + 2], -X), ldexpf(v[4 * d + 3], -X), w, true);
+    hw[d] = (uint32_t)w;
+    // residual against the decoded hi value (exact in fp32)
+    r[4 * d + 0] = v[4 * d + 0] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 0), X);
+    r[4 * d + 1] = v[4 * d + 1] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 1), X);
+    r[4 * d + 2] = v[4 * d + 2] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 2), X);
+    r[4 * d + 3] = v[4 * d + 3] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 3), X);
+  }
+  float rmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) rmax = fmaxf(rmax, fabsf(r[i]));
+  const int Xl = mx_exponent(rmax);
+  uint32_t lw[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    int w = 0;
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[4 * d], -Xl), ldexpf(r[4 * d + 1], -Xl), w, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[4 * d + 2], -Xl), ldexpf(r[4 * d + 3], -Xl), w, true);
+    lw[d] = (uint32_t)w;
+  }
+  h0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  h1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+  l0 = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  l1 = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+  sh = (uint32_t)(X + 127);
+  sl = (uint32_t)(Xl + 127);
+}
+
+// ---------------------------------------------------------------------------------------
+// 1. sort by expert (one workgroup)
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf) {
+  // sbuf: kSortThreads ints of LDS
+  const int tid = threadIdx.x;
+  sbuf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kSortThreads; off <<= 1) {
+    const int add = (tid >= off) ? sbuf[tid - off] : 0;
+    __syncthreads();
+    sbuf[tid] += add;
+    __syncthreads();
+  }
+  const int inclusive = sbuf[tid];
+  __syncthreads();
+  return inclusive - v;
+}
+
+__global__ __launch_bounds__(kSortThreads) void sort_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ blk_expert, int32_t* __restrict__ blk_row0,
+    int32_t* __restrict__ blk_rows, int32_t* __restrict__ n_blocks) {
+  extern __shared__ int sm[];
+  int* cnt = sm;                // E
+  int* cur = sm + E;            // E
+  int* boff = sm + 2 * E;       // E
+  int* sbuf = sm + 3 * E;       // kSortThreads
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kSortThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // each thread owns experts [tid * per, tid * per + per)
+  const int per = (E + kSortThreads - 1) / kSortThreads;
+  int rows = 0, blks = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      rows += cnt[e];
+      blks += (cnt[e] + kBlockRows - 1) / kBlockRows;
+    }
+  }
+  int row_base = block_exclusive_scan(rows, sbuf);
+  int blk_base = block_exclusive_scan(blks, sbuf);
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      cur[e] = row_base;
+      boff[e] = blk_base;
+      offsets[e] = row_base;
+      const int n = cnt[e];
+      const int nb = (n + kBlockRows - 1) / kBlockRows;
+      for (int b = 0; b < nb; ++b) {
+        blk_expert[blk_base + b] = e;
+        blk_row0[blk_base + b] = row_base + b * kBlockRows;
+        blk_rows[blk_base + b] = min(kBlockRows, n - b * kBlockRows);
+      }
+      row_base += n;
+      blk_base += nb;
+    }
+  }
+  if (tid == kSortThreads - 1) {
+    offsets[E] = row_base;
+    n_blocks[0] = blk_base;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += kSortThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) perm[atomicAdd(&cur[e], 1)] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 2. x -> MXFP8 hi / lo, one thread per (token, 32-block); blocks past H are zero (scale
+//    byte 127)
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                      int Hp, uint8_t* __restrict__ qhi,
+                                                      uint8_t* __restrict__ qlo,
+                                                      uint8_t* __restrict__ shi,
+                                                      uint8_t* __restrict__ slo) {
+  const int nbk = Hp / kBlock;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)T * nbk) return;
+  const long t = idx / nbk;
+  const int b = (int)(idx - t * nbk);
+  uint4 h0 = make_uint4(0, 0, 0, 0), h1 = h0, l0 = h0, l1 = h0;
+  uint32_t sh = 127, sl = 127;
+  if (kBlock * b < H) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + t * H + kBlock * b);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = src[q];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * q + 2 * i] = bf16_bits_to_f32(ww[i] & 0xffffu);
+        v[8 * q + 2 * i + 1] = bf16_bits_to_f32(ww[i] >> 16);
+      }
+    }
+    mx8_encode_block(v, h0, h1, l0, l1, sh, sl);
+  }
+  uint4* dh = reinterpret_cast<uint4*>(qhi + t * Hp + kBlock * b);
+  uint4* dl = reinterpret_cast<uint4*>(qlo + t * Hp + kBlock * b);
+  dh[0] = h0;
+  dh[1] = h1;
+  dl[0] = l0;
+  dl[1] = l1;
+  shi[t * nbk + b] = (uint8_t)sh;
+  slo[t * nbk + b] = (uint8_t)sl;
+}
+
+// ---------------------------------------------------------------------------------------
+// Grouped GEMM core shared by both stages. A workgroup owns one M-block (up to kBlockRows
+// rows of one expert's group) and kBN weight rows (wave w: 16-row tile n0 / 16 + w of each of
+// its NMAT matrices). Per 128-element chunk of K:
+//  * the block's A rows (hi, lo, scales) are staged in one of two LDS buffers; each thread
+//    moves four 16-byte pieces and (threads < 2 * kBlockRows) one scale dword, loaded from
+//    global memory about one chunk ahead of their store;
+//  * each wave loads its B words (one 1 KB word per matrix) two chunks ahead;
+//  * 16-row subtiles past the block's rows are skipped (wave-uniform);
+//  * one barrier per chunk.
+// Every load is issued with a clamped chunk index, so the wait counts stay exact. The GEMM
+// kernels are held to 4 wavefronts per SIMD (at most 128 registers per lane; the two LDS
+// buffers of 17.9 KB each allow 4 workgroups per CU), so other workgroups' chunks cover
+// each wave's memory waits.
+// ---------------------------------------------------------------------------------------
+struct GemmCtx {
+  const uint8_t* ahi;
+  const uint8_t* alo;
+  const uint8_t* ashi;
+  const uint8_t* aslo;
+  long r0, r1, r2, r3;  // byte offsets of the A rows of this thread's four pieces
+  long sr;              // byte offset of the scale row of this thread's scale dword
+  int part;             // 16-byte piece of the row (0..7 hi, 8..15 lo), same for all four
+  int KB;               // K blocks of 32
+  int Kp;               // padded K (row pitch of the A data, bytes)
+};
+
+// The staged values travel in five separate registers (d0..d3, s): a struct or array
+// carried around the K loop is placed in private memory.
+__device__ __forceinline__ void stage_load(const GemmCtx& cx, int c, uint4& d0, uint4& d1,
+                                           uint4& d2, uint4& d3, uint32_t& sv) {
+  const long off = 128L * c + 16 * (cx.part & 7);
+  const uint8_t* base = cx.part < 8 ? cx.ahi : cx.alo;
+  d0 = *reinterpret_cast<const uint4*>(base + cx.r0 + off);
+  d1 = *reinterpret_cast<const uint4*>(base + cx.r1 + off);
+  d2 = *reinterpret_cast<const uint4*>(base + cx.r2 + off);
+  d3 = *reinterpret_cast<const uint4*>(base + cx.r3 + off);
+  const int tid = threadIdx.x;
+  const uint8_t* sb = (tid & 1) ? cx.aslo : cx.ashi;
+  sv = *reinterpret_cast<const uint32_t*>(sb + cx.sr + 4L * c);
+}
+
+// piece i of thread tid: q = tid + kBThreads i, row q / 16, part q % 16
+__device__ __forceinline__ void stage_store(uint8_t* lds, uint8_t* lds_s, uint4 d0, uint4 d1,
+                                            uint4 d2, uint4 d3, uint32_t sv) {
+  const int tid = threadIdx.x;
+  uint8_t* p = lds + (tid >> 4) * kAPitch + 16 * (tid & 15);
+  constexpr int kRowStep = (kBThreads / 16) * kAPitch;
+  *reinterpret_cast<uint4*>(p) = d0;
+  *reinterpret_cast<uint4*>(p + kRowStep) = d1;
+  *reinterpret_cast<uint4*>(p + 2 * kRowStep) = d2;
+  *reinterpret_cast<uint4*>(p + 3 * kRowStep) = d3;
+  if (tid < 2 * kBlockRows) *reinterpret_cast<uint32_t*>(lds_s + 4 * tid) = sv;
+}
+
+// A operand (hi or lo) of 16-row subtile m for this lane; halves of K-blocks past K are zero.
+__device__ __forceinline__ i32x8_t a_operand(const uint8_t* lds, int m, int lane, bool lo,
+                                             bool half0_ok, bool half1_ok) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint8_t* row = lds + (16 * m + r) * kAPitch + (lo ? 128 : 0);
+  uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
+  uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
+  if (!half0_ok) p0 = make_uint4(0, 0, 0, 0);
+  if (!half1_ok) p1 = make_uint4(0, 0, 0, 0);
+  return i32x8_t{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
+                 (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+}
+
+__device__ __forceinline__ i32x8_t b_operand(uint4 w) {
+  return i32x8_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+}
+
+// One matrix's B word for this lane: 16 code bytes and the scale byte (zero / 1 past K).
+struct BWord {
+  uint4 w;
+  uint32_t s;
+};
+
+__device__ __forceinline__ BWord load_b(const uint8_t* codes, const uint8_t* scales, int c,
+                                        int KB, bool wave_on) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const bool ok = wave_on && 4 * c + g < KB;
+  const long w = (4 * c + g < KB) ? 64L * c + lane : 64L * c;  // past K: any valid word
+  BWord b;
+  b.w = ld_nt16(codes + 16 * w);
+  b.s = scales[w];
+  if (!ok) {
+    b.w = make_uint4(0, 0, 0, 0);
+    b.s = 127u;
+  }
+  return b;
+}
+
+// acc[m][q] accumulates 16-row subtile m of matrix q (0: codes0 / scales0, 1: codes1 ...).
+template <int NMAT>
+__device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const uint8_t* codes0,
+                                            const uint8_t* scales0, const uint8_t* codes1,
+                                            const uint8_t* scales1, bool wave_on, int rows,
+                                            uint8_t* lds, uint8_t* lds_s,
+                                            f32x4_t (&acc)[kMSub][NMAT]) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int nch = (cx.KB + 3) / 4;
+  constexpr int kBuf = kBlockRows * kAPitch;
+  constexpr int kBufS = kBlockRows * 8;
+  uint4 d0, d1, d2, d3;
+  uint32_t sv;
+  stage_load(cx, 0, d0, d1, d2, d3, sv);
+  stage_store(lds, lds_s, d0, d1, d2, d3, sv);
+  stage_load(cx, min(1, nch - 1), d0, d1, d2, d3, sv);
+  BWord b0c = load_b(codes0, scales0, 0, cx.KB, wave_on);
+  BWord b0n = load_b(codes0, scales0, min(1, nch - 1), cx.KB, wave_on);
+  BWord b1c = b0c, b1n = b0n;
+  if constexpr (NMAT > 1) {
+    b1c = load_b(codes1, scales1, 0, cx.KB, wave_on);
+    b1n = load_b(codes1, scales1, min(1, nch - 1), cx.KB, wave_on);
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const uint8_t* A = lds + (c & 1) * kBuf;
+    const uint8_t* AS = lds_s + (c & 1) * kBufS;
+    // A halves of this lane: K-blocks 4 c + 2 h + g / 2; this lane's scale: K-block 4 c + g.
+    // Past K the data is zeroed and the scale forced to 1: padding scale bytes are never
+    // written, and a NaN scale (byte 255) would poison the product even with zero data.
+    const bool h0 = 4 * c + (g >> 1) < cx.KB;
+    const bool h1 = 4 * c + 2 + (g >> 1) < cx.KB;
+    const bool s_ok = 4 * c + g < cx.KB;
+    if (wave_on) {
+      const i32x8_t bq0 = b_operand(b0c.w);
+      const i32x8_t bq1 = b_operand(b1c.w);
+#pragma unroll
+      for (int m = 0; m < kMSub; ++m) {
+        if (16 * m < rows) {  // wave-uniform
+          const i32x8_t ahi = a_operand(A, m, lane, false, h0, h1);
+          const i32x8_t alo = a_operand(A, m, lane, true, h0, h1);
+          const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;
+          const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;
+          acc[m][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              ahi, bq0, acc[m][0], 0, 4, 0, sw_hi, 0, (int)b0c.s);
+          acc[m][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              alo, bq0, acc[m][0], 0, 4, 0, sw_lo, 0, (int)b0c.s);
+          if constexpr (NMAT > 1) {
+            acc[m][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                ahi, bq1, acc[m][1], 0, 4, 0, sw_hi, 0, (int)b1c.s);
+            acc[m][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                alo, bq1, acc[m][1], 0, 4, 0, sw_lo, 0, (int)b1c.s);
+          }
+        }
+      }
+    }
+    // chunk c + 1 into the other buffer (last read in iteration c - 1, before its barrier);
+    // then the loads of chunk c + 2 (clamped)
+    stage_store(lds + ((c + 1) & 1) * kBuf, lds_s + ((c + 1) & 1) * kBufS, d0, d1, d2, d3, sv);
+    const int cn = min(c + 2, nch - 1);
+    stage_load(cx, cn, d0, d1, d2, d3, sv);
+    b0c = b0n;
+    b0n = load_b(codes0, scales0, cn, cx.KB, wave_on);
+    if constexpr (NMAT > 1) {
+      b1c = b1n;
+      b1n = load_b(codes1, scales1, cn, cx.KB, wave_on);
+    }
+    __syncthreads();
+  }
+}
+
+// Fills the per-thread A row offsets. row_of(i) returns the A row (token or sorted position)
+// of block row i (clamped into the block by the caller).
+template <typename RowOf>
+__device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
+  const int tid = threadIdx.x;
+  constexpr int kRows = kBThreads / 16;  // rows covered by one piece index
+  cx.r0 = (long)row_of(tid >> 4) * cx.Kp;
+  cx.r1 = (long)row_of((tid >> 4) + kRows) * cx.Kp;
+  cx.r2 = (long)row_of((tid >> 4) + 2 * kRows) * cx.Kp;
+  cx.r3 = (long)row_of((tid >> 4) + 3 * kRows) * cx.Kp;
+  cx.part = tid & 15;
+  cx.sr = (long)row_of(min(tid >> 1, kBlockRows - 1)) * (cx.Kp / kBlock);
+}
+
+// ---------------------------------------------------------------------------------------
+// 3. gate / up / SiLU / h quantisation
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_gate_up_kernel(
+    const uint8_t* __restrict__ xhi, const uint8_t* __restrict__ xlo,
+    const uint8_t* __restrict__ xshi, const uint8_t* __restrict__ xslo, int Hp,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_expert,
+    const int32_t* __restrict__ blk_row0, const int32_t* __restrict__ blk_rows,
+    const int32_t* __restrict__ n_blocks, int k, const uint8_t* __restrict__ packed,
+    size_t stride, size_t off_gc, size_t off_uc, size_t off_gs, size_t off_us, int H, int I,
+    int n_tiles, uint8_t* __restrict__ hhi, uint8_t* __restrict__ hlo,
+    uint8_t* __restrict__ hshi, uint8_t* __restrict__ hslo, int Ip) {
+  __shared__ __align__(16) uint8_t lds[2 * kBlockRows * kAPitch];
+  __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
+  const int blk = blockIdx.x / n_tiles;
+  const int nt = blockIdx.x - blk * n_tiles;
+  if (blk >= n_blocks[0]) return;  // workgroup-uniform
+  const int e = blk_expert[blk];
+  const int row0 = blk_row0[blk];
+  const int rows = blk_rows[blk];
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int KB = H / kBlock;
+  const int tile = nt * kBWaves + wv;  // 16-row tile of gate / up
+  const bool wave_on = 16 * tile < I;
+
+  GemmCtx cx;
+  cx.ahi = xhi;
+  cx.alo = xlo;
+  cx.ashi = xshi;
+  cx.aslo = xslo;
+  cx.KB = KB;
+  cx.Kp = Hp;
+  gemm_ctx_rows(cx, [&](int i) { return perm[row0 + min(i, rows - 1)] / k; });
+
+  const uint8_t* base = packed + (size_t)e * stride;
+  const size_t tb = (size_t)min(tile, I / 16 - 1) * 16 * KB;  // tile-major word index
+  f32x4_t acc[kMSub][2];
+#pragma unroll
+  for (int m = 0; m < kMSub; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gemm_k_loop<2>(cx, base + off_gc + 16 * tb, base + off_gs + tb, base + off_uc + 16 * tb,
+                 base + off_us + tb, wave_on, rows, lds, lds_s, acc);
+
+  // epilogue: h (fp32) for the block's rows x 64 columns into LDS (the loop ended with a
+  // barrier), then per (row, 32-block) quantisation by one thread
+  float* htile = reinterpret_cast<float*>(lds);  // [kBlockRows][kBN + 1]
+  constexpr int kHP = kBN + 1;
+#pragma unroll
+  for (int m = 0; m < kMSub; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * m + 4 * (lane >> 4) + q;  // block row
+      const float gv = acc[m][0][q], uv = acc[m][1][q];
+      htile[i * kHP + 16 * wv + (lane & 15)] = silu_f32(gv) * uv;
+    }
+  __syncthreads();
+  if (tid < 2 * kBlockRows) {
+    const int r = tid >> 1, b = tid & 1;
+    const int col = nt * kBN + 32 * b;  // first I index of this 32-block
+    if (r < rows && col < I) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = htile[r * kHP + 32 * b + i];
+      uint4 h0, h1, l0, l1;
+      uint32_t sh, sl;
+      mx8_encode_block(v, h0, h1, l0, l1, sh, sl);
+      const long pos = row0 + r;
+      uint4* dh = reinterpret_cast<uint4*>(hhi + pos * Ip + col);
+      uint4* dl = reinterpret_cast<uint4*>(hlo + pos * Ip + col);
+      dh[0] = h0;
+      dh[1] = h1;
+      dl[0] = l0;
+      dl[1] = l1;
+      hshi[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sh;
+      hslo[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sl;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// 4. down projection, times the router weight, fp32 per pair
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_down_kernel(
+    const uint8_t* __restrict__ hhi, const uint8_t* __restrict__ hlo,
+    const uint8_t* __restrict__ hshi, const uint8_t* __restrict__ hslo, int Ip,
+    const int32_t* __restrict__ perm, const float* __restrict__ wts,
+    const int32_t* __restrict__ blk_expert, const int32_t* __restrict__ blk_row0,
+    const int32_t* __restrict__ blk_rows, const int32_t* __restrict__ n_blocks,
+    const uint8_t* __restrict__ packed, size_t stride, size_t off_dc, size_t off_ds, int H, int I,
+    int n_tiles, float* __restrict__ ypair) {
+  __shared__ __align__(16) uint8_t lds[2 * kBlockRows * kAPitch];
+  __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
+  const int blk = blockIdx.x / n_tiles;
+  const int nt = blockIdx.x - blk * n_tiles;
+  if (blk >= n_blocks[0]) return;  // workgroup-uniform
+  const int e = blk_expert[blk];
+  const int row0 = blk_row0[blk];
+  const int rows = blk_rows[blk];
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int KB = I / kBlock;
+  const int tile = nt * kBWaves + wv;  // 16-row tile of down (rows of H)
+  const bool wave_on = 16 * tile < H;
+
+  GemmCtx cx;
+  cx.ahi = hhi;
+  cx.alo = hlo;
+  cx.ashi = hshi;
+  cx.aslo = hslo;
+  cx.KB = KB;
+  cx.Kp = Ip;
+  gemm_ctx_rows(cx, [&](int i) { return row0 + min(i, rows - 1); });
+
+  const uint8_t* base = packed + (size_t)e * stride;
+  const size_t tb = (size_t)min(tile, H / 16 - 1) * 16 * KB;
+  f32x4_t acc[kMSub][1];
+#pragma unroll
+  for (int m = 0; m < kMSub; ++m) acc[m][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gemm_k_loop<1>(cx, base + off_dc + 16 * tb, base + off_ds + tb, nullptr, nullptr, wave_on,
+                 rows, lds, lds_s, acc);
+
+  if (!wave_on) return;
+  const int n = 16 * tile + (lane & 15);
+#pragma unroll
+  for (int m = 0; m < kMSub; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * m + 4 * (lane >> 4) + q;
+      if (i < rows) {
+        const int pair = perm[row0 + i];
+        ypair[(size_t)pair * H + n] = wts[pair] * acc[m][0][q];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// 5. combine: one workgroup per token
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ wts, int k,
+                                                      int n_experts, int H,
+                                                      const float* __restrict__ ypair,
+                                                      uint16_t* __restrict__ y) {
+  __shared__ int s_slot[kMaxK], s_nv;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int jj = tid;
+    const int ej = (jj < k) ? ids[(size_t)t * k + jj] : -1;
+    const uint32_t wj = (jj < k) ? __float_as_uint(wts[(size_t)t * k + jj]) : 0u;
+    const bool okj = jj < k && ej >= 0 && ej < n_experts;
+    int rank = 0;
+    for (int i = 0; i < k; ++i) {
+      const int ei = __shfl(ej, i, 64);
+      const uint32_t wi = (uint32_t)__shfl((int)wj, i, 64);
+      const bool oki = ei >= 0 && ei < n_experts;
+      const bool before = ei < ej || (ei == ej && (wi < wj || (wi == wj && i < jj)));
+      rank += (oki && before) ? 1 : 0;
+    }
+    const int nvl = __popcll(__ballot(okj));  // every lane of the wave votes
+    if (okj) s_slot[rank] = jj;
+    if (jj == 0) s_nv = nvl;
+  }
+  __syncthreads();
+  const int nv = s_nv;
+  for (int n = tid; n < H; n += 256) {
+    float acc = 0.f;
+    for (int p = 0; p < nv; ++p) acc += ypair[((size_t)t * k + s_slot[p]) * H + n];
+    y[(size_t)t * H + n] = f32_to_bf16_rne(acc);
+  }
+}
+
+}  // namespace
+
+BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter) {
+  BatchedLayout L{};
+  const size_t P = (size_t)T * (size_t)k;
+  const size_t Hp = (size_t)((hidden + 127) / 128) * 128;
+  const size_t Ip = (size_t)((inter + 127) / 128) * 128;
+  const size_t nb_max = (P + kBlockRows - 1) / kBlockRows + (size_t)n_experts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  L.offsets = take(((size_t)n_experts + 1) * 4);
+  L.perm = take(P * 4);
+  L.blk_expert = take(nb_max * 4);
+  L.blk_row0 = take(nb_max * 4);
+  L.blk_rows = take(nb_max * 4);
+  L.n_blocks = take(4);
+  L.xhi = take((size_t)T * Hp);
+  L.xlo = take((size_t)T * Hp);
+  L.xshi = take((size_t)T * Hp / kBlock);
+  L.xslo = take((size_t)T * Hp / kBlock);
+  L.hhi = take(P * Ip);
+  L.hlo = take(P * Ip);
+  L.hshi = take(P * Ip / kBlock);
+  L.hslo = take(P * Ip / kBlock);
+  L.ypair = take(P * (size_t)hidden * 4);
+  L.bytes = off;
+  L.nb_max = nb_max;
+  L.Hp = (int)Hp;
+  L.Ip = (int)Ip;
+  return L;
+}
+
+hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
+                              const uint8_t* packed, int n_experts, int hidden, int inter,
+                              uint16_t* y, void* workspace, hipStream_t s) {
+  const BatchedLayout B = batched_layout(T, k, n_experts, hidden, inter);
+  const PackedLayout L = packed_layout(hidden, inter);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + B.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + B.perm);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + B.blk_expert);
+  int32_t* brow0 = reinterpret_cast<int32_t*>(ws + B.blk_row0);
+  int32_t* brows = reinterpret_cast<int32_t*>(ws + B.blk_rows);
+  int32_t* nblk = reinterpret_cast<int32_t*>(ws + B.n_blocks);
+  const long P = (long)T * k;
+  if (P > 0x7fffffffL) return hipErrorInvalidValue;
+
+  const uint32_t sort_lds = (uint32_t)((3 * n_experts + kSortThreads) * sizeof(int));
+  hipError_t e = launch_kernel(kKindBatchedSort, sort_kernel, dim3(1), dim3(kSortThreads), sort_lds, s,
+                               ids, (int)P, n_experts, offsets, perm, bexp, brow0, brows, nblk);
+  if (e != hipSuccess) return e;
+
+  const long qn = (long)T * (B.Hp / kBlock);
+  e = launch_kernel(kKindBatchedQuant, quant_x_kernel, dim3((unsigned)((qn + 255) / 256)), dim3(256), 0,
+                    s, x, T, hidden, B.Hp, ws + B.xhi, ws + B.xlo, ws + B.xshi, ws + B.xslo);
+  if (e != hipSuccess) return e;
+
+  const int gu_tiles = (inter + kBN - 1) / kBN;
+  const long gu_grid = (long)B.nb_max * gu_tiles;
+  if (gu_grid > 0x7fffffffL) return hipErrorInvalidValue;
+  e = launch_kernel(kKindBatchedGateUp, gemm_gate_up_kernel, dim3((unsigned)gu_grid), dim3(kBThreads), 0,
+                    s, ws + B.xhi, ws + B.xlo, ws + B.xshi, ws + B.xslo, B.Hp, perm, bexp, brow0,
+                    brows, nblk, k, packed, L.stride, L.m[0].codes, L.m[1].codes, L.m[0].scales,
+                    L.m[1].scales, hidden, inter, gu_tiles, ws + B.hhi, ws + B.hlo, ws + B.hshi,
+                    ws + B.hslo, B.Ip);
+  if (e != hipSuccess) return e;
+
+  const int dn_tiles = (hidden + kBN - 1) / kBN;
+  const long dn_grid = (long)B.nb_max * dn_tiles;
+  if (dn_grid > 0x7fffffffL) return hipErrorInvalidValue;
+  float* ypair = reinterpret_cast<float*>(ws + B.ypair);
+  e = launch_kernel(kKindBatchedDown, gemm_down_kernel, dim3((unsigned)dn_grid), dim3(kBThreads), 0, s,
+                    ws + B.hhi, ws + B.hlo, ws + B.hshi, ws + B.hslo, B.Ip, perm, w, bexp, brow0,
+                    brows, nblk, packed, L.stride, L.m[2].codes, L.m[2].scales, hidden, inter,
+                    dn_tiles, ypair);
+  if (e != hipSuccess) return e;
+
+  return launch_kernel(kKindBatchedCombine, combine_kernel, dim3((unsigned)T), dim3(256), 0, s, ids,
+                       w, k, n_experts, hidden, ypair, y);
+}
+
+}  // namespace moe_fp4

@@ -18,7 +18,9 @@ constexpr int kMaxExpertsTopk = 2048;  // max experts for the top-k selection ke
 
 // Kernel kinds for timing (same values as MOE_FP4_KERNEL_* in the public header).
 enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp = 3,
-                  kKindDownCombine = 4, kKindRouteDecode = 5 };
+                  kKindDownCombine = 4, kKindRouteDecode = 5, kKindBatchedSort = 6,
+                  kKindBatchedQuant = 7, kKindBatchedGateUp = 8, kKindBatchedDown = 9,
+                  kKindBatchedCombine = 10 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -112,6 +114,29 @@ hipError_t launch_gate_up(const uint16_t* x, const int32_t* ids, int T, int k, c
 hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,
                                const uint8_t* packed, int n_experts, int hidden, int inter,
                                const uint16_t* hbuf, uint16_t* y, hipStream_t s);
+
+// ----------------------------------------------------------------------------------------
+// Batched path: pairs grouped by expert, grouped GEMM on the block-scaled matrix cores.
+// Workspace regions (byte offsets, 256-aligned) for T tokens:
+//   offsets [E+1], perm [T k], M-block table (expert, first row, rows) [nb_max each],
+//   n_blocks [1], x as MXFP8 hi / lo [T x Hp] + scales [T x Hp/32] each,
+//   h as MXFP8 hi / lo [T k x Ip] + scales each, per-pair weighted y_e fp32 [T k x H].
+// Hp, Ip: hidden, inter rounded up to 128.
+// ----------------------------------------------------------------------------------------
+constexpr int kBlockRows = 64;  // rows of one expert's group per GEMM workgroup
+
+struct BatchedLayout {
+  size_t offsets, perm, blk_expert, blk_row0, blk_rows, n_blocks;
+  size_t xhi, xlo, xshi, xslo, hhi, hlo, hshi, hslo, ypair;
+  size_t bytes, nb_max;
+  int Hp, Ip;
+};
+
+BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter);
+
+hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
+                              const uint8_t* packed, int n_experts, int hidden, int inter,
+                              uint16_t* y, void* workspace, hipStream_t s);
 
 hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
                                 int matrix, float* out, hipStream_t s);

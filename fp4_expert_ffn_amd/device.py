@@ -94,14 +94,19 @@ class MoeFp4Layer:
         return ids, w
 
     def ffn(self, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor,
-            y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+            y: Optional[torch.Tensor] = None, stream=None, path: Optional[int] = None) -> torch.Tensor:
+        """moe_fp4_expert_ffn (path None: automatic choice) or moe_fp4_expert_ffn_ex."""
         T = x.shape[0]
         k = ids.shape[1] if ids.dim() == 2 else self.k
         if y is None:
             y = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=self.device)
         ws = self._workspace(T, k)
-        C.moe_fp4_expert_ffn(x, ids, w, T, k, self.packed, self.n_experts, self.hidden, self.inter,
-                             y, ws, stream=stream)
+        if path is None:
+            C.moe_fp4_expert_ffn(x, ids, w, T, k, self.packed, self.n_experts, self.hidden,
+                                 self.inter, y, ws, stream=stream)
+        else:
+            C.moe_fp4_expert_ffn_ex(x, ids, w, T, k, self.packed, self.n_experts, self.hidden,
+                                    self.inter, y, ws, path, stream=stream)
         return y
 
     def forward(self, x: torch.Tensor, stream=None):

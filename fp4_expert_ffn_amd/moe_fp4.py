@@ -27,7 +27,8 @@ ERR_WORKSPACE = -4
 ERR_HIP = -5
 
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
-KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode")
+KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
+                "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine")
 
 
 class MoeFp4Error(RuntimeError):
@@ -53,6 +54,7 @@ _SIGNATURES = {
     "moe_fp4_route_logits": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp4_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_expert_ffn": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_fp4_expert_ffn_ex": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _I, _P]),
     "moe_fp4_moe_forward_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -165,6 +167,20 @@ def moe_fp4_expert_ffn(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: i
     _check(lib().moe_fp4_expert_ffn(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(packed),
                                     n_experts, hidden, inter, _ptr(y), _ptr(workspace),
                                     workspace_bytes, _stream(stream)), "moe_fp4_expert_ffn")
+
+
+PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
+
+
+def moe_fp4_expert_ffn_ex(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: int,
+                          hidden: int, inter: int, y, workspace, path: int,
+                          workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_fp4_expert_ffn_ex(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, k, _ptr(packed),
+                                       n_experts, hidden, inter, _ptr(y), _ptr(workspace),
+                                       workspace_bytes, path, _stream(stream)),
+           "moe_fp4_expert_ffn_ex")
 
 
 def moe_fp4_moe_forward_workspace_bytes(T: int, k: int, n_experts: int, hidden: int,

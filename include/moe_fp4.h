@@ -26,8 +26,8 @@
  *    Faults inside a kernel surface at the caller's next synchronisation.
  *  - T = 0 (no tokens) is a no-op that returns MOE_FP4_OK.
  *  - Shapes: hidden and inter must be positive multiples of 32 and at most 16384;
- *    1 <= k <= min(n_experts, 8); k * inter <= 32768 for moe_fp4_expert_ffn and
- *    moe_fp4_moe_forward (the k h vectors of a token are staged in 64 KB of LDS).
+ *    1 <= k <= min(n_experts, 8); the decode FFN path needs k * inter <= 32768 (the k h
+ *    vectors of a token are staged in 64 KB of LDS), the grouped path n_experts <= 2048.
  *  - Alignment: topk_ids, topk_w and the fp32 logits of moe_fp4_route_logits must be
  *    4-byte aligned (so a row slice of a [T x k] array can be passed); every other device
  *    pointer (activations, weights, packed experts, outputs, workspaces) 16-byte aligned.
@@ -126,8 +126,10 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
  * h is rounded to bf16 before the down projection, y is rounded to bf16.
  * ------------------------------------------------------------------------------------ */
 
-/* Workspace bytes moe_fp4_expert_ffn needs: h of every (token, slot) pair (bf16).
- * 0 for invalid arguments. */
+/* Workspace bytes moe_fp4_expert_ffn (any path) needs: the larger of h of every (token,
+ * slot) pair in bf16 (decode path) and the grouped path's sort tables, MXFP8 activations
+ * and per-pair fp32 outputs (about T * k * (hidden * 4 + 2 * inter) bytes). 0 for invalid
+ * arguments. */
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter);
 
 /* x [T x hidden] bf16; topk_ids int32 [T x k]; topk_w fp32 [T x k];
@@ -139,6 +141,28 @@ size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inte
 int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                        int k, const void* packed, int n_experts, int hidden, int inter,
                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same operation with an explicit choice of kernels ([A100-FP4], section
+ * 批处理不是「同时处理几个人」: tokens routed to the same expert can share one read of its
+ * weights, and weight reads are the cost that matters in an MoE layer).
+ *  MOE_FP4_PATH_DECODE: every (token, slot) pair streams its expert's weights (two
+ *    launches; best at batch 1; needs k * inter <= 32768).
+ *  MOE_FP4_PATH_GROUPED: pairs are grouped by expert on the device (no host readback) and
+ *    run through a grouped GEMM on the block-scaled FP4 matrix cores; the activations x and
+ *    h enter the matrix cores as two-term MXFP8 (E4M3 hi + lo, one ue8m0 scale per 32
+ *    elements each), accumulation is fp32, each pair's weighted output is combined per token
+ *    in canonical slot order (five launches; needs n_experts <= 2048).
+ *  MOE_FP4_PATH_AUTO: GROUPED from 16 tokens on, DECODE below.
+ * moe_fp4_expert_ffn is this call with MOE_FP4_PATH_AUTO. The workspace size covers every
+ * path. Errors: as moe_fp4_expert_ffn; an unknown path is INVALID_ARG, a shape the chosen
+ * path cannot take is BAD_SHAPE. */
+#define MOE_FP4_PATH_AUTO 0
+#define MOE_FP4_PATH_DECODE 1
+#define MOE_FP4_PATH_GROUPED 2
+int moe_fp4_expert_ffn_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
+                          int k, const void* packed, int n_experts, int hidden, int inter,
+                          uint16_t* y, void* workspace, size_t workspace_bytes, int path,
+                          void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Whole routed-expert layer in one call: moe_fp4_route followed by moe_fp4_expert_ffn on
@@ -188,7 +212,12 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
 #define MOE_FP4_KERNEL_GATE_UP 3
 #define MOE_FP4_KERNEL_DOWN_COMBINE 4
 #define MOE_FP4_KERNEL_ROUTE_DECODE 5 /* batch-1 router GEMV + selection in one launch */
-#define MOE_FP4_KERNEL_KINDS 6
+#define MOE_FP4_KERNEL_GROUPED_SORT 6
+#define MOE_FP4_KERNEL_GROUPED_QUANT 7
+#define MOE_FP4_KERNEL_GROUPED_GATE_UP 8
+#define MOE_FP4_KERNEL_GROUPED_DOWN 9
+#define MOE_FP4_KERNEL_GROUPED_COMBINE 10
+#define MOE_FP4_KERNEL_KINDS 11
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

@@ -78,7 +78,9 @@ def test_expert_ffn_argument_checks(L):
     assert ffn(L, H=4010) == C.ERR_BAD_SHAPE
     assert ffn(L, I=2881) == C.ERR_BAD_SHAPE
     assert ffn(L, H=16384 + 32) == C.ERR_BAD_SHAPE
-    assert ffn(L, k=8, I=8192) == C.ERR_BAD_SHAPE          # k * inter > 32768
+    # k * inter > 32768 does not fit the decode path's LDS: the automatic choice takes the
+    # grouped path (the argument checks pass and the workspace check fires)
+    assert ffn(L, k=8, I=8192, wsb=8) == C.ERR_WORKSPACE
     assert ffn(L, x=MIS) == C.ERR_MISALIGNED
     assert ffn(L, packed=MIS) == C.ERR_MISALIGNED
     assert ffn(L, ids=MIS4) == C.ERR_MISALIGNED
@@ -87,6 +89,22 @@ def test_expert_ffn_argument_checks(L):
     assert ffn(L, wsb=100) == C.ERR_WORKSPACE
     # T = 0 is a no-op: OK without touching any pointer
     assert ffn(L, T=0, wsb=0) == C.OK
+
+
+def test_expert_ffn_path_checks(L):
+    def ffn_ex(path, k=6, E=384, I=2880, wsb=1 << 40, T=1):
+        return L.moe_fp4_expert_ffn_ex(A, A, A, T, k, A, E, 4096, I, A, A, wsb, path, None)
+    assert ffn_ex(C.PATH_DECODE, k=8, I=8192) == C.ERR_BAD_SHAPE       # decode LDS limit
+    assert ffn_ex(C.PATH_GROUPED, E=4096, k=6) == C.ERR_BAD_SHAPE      # sort table limit
+    assert ffn_ex(7) == C.ERR_INVALID_ARG
+    assert ffn_ex(-1) == C.ERR_INVALID_ARG
+    for path in (C.PATH_AUTO, C.PATH_DECODE, C.PATH_GROUPED):
+        assert ffn_ex(path, wsb=8) == C.ERR_WORKSPACE
+        assert ffn_ex(path, T=0, wsb=0) == C.OK
+    # the workspace covers the grouped path: sort tables, MXFP8 x and h, fp32 per-pair y
+    need = C.moe_fp4_workspace_bytes(64, 6, 384, 4096, 2880)
+    assert need >= 64 * 6 * (4096 * 4 + 2 * 2944) + 64 * 2 * 4096
+    assert C.moe_fp4_workspace_bytes(0, 6, 384, 4096, 2880) == 0
 
 
 def test_route_argument_checks(L):

@@ -48,12 +48,16 @@ def _random_routing(rng, T, k, E, distinct=True):
     return ids, w
 
 
-def _run_ffn(layer, x_bits, ids, w, dev):
+DECODE, GROUPED = 1, 2  # moe_fp4_expert_ffn_ex paths
+PATHS = pytest.mark.parametrize("path", [DECODE, GROUPED], ids=["decode", "grouped"])
+
+
+def _run_ffn(layer, x_bits, ids, w, dev, path=None):
     _, D = _mods()
     x = D.upload_bf16(x_bits, dev)
     ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev)
     w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev)
-    y = layer.ffn(x, ids_d, w_d)
+    y = layer.ffn(x, ids_d, w_d, path=path)
     torch.cuda.synchronize()
     return D.bf16_bits(y)
 
@@ -183,7 +187,7 @@ def test_single_expert_h256_i128(dev):
 
 
 SMALL_SHAPES = [
-    # H, I, E, k, T: row maps (LPR, BPL) for K = H and K = I, ragged tails
+    # H, I, E, k, T: ragged K tails (K % 128 != 0), tiles of 16 rows, ragged token counts
     (64, 32, 4, 2, 3),
     (320, 96, 5, 3, 7),
     (512, 2880, 8, 6, 5),
@@ -192,20 +196,26 @@ SMALL_SHAPES = [
     (16384, 64, 3, 2, 2),
     (96, 16384, 3, 2, 2),
     (1024, 1024, 16, 8, 17),
+    # grouped-path shapes: H and I = 32 mod 64 (last 64-row tile half used), K padded to
+    # 128, one and several 64-row blocks per expert, a partial last block
+    (160, 96, 8, 3, 50),
+    (256, 128, 4, 2, 200),
+    (224, 2880, 6, 6, 40),
 ]
 
 
+@PATHS
 @pytest.mark.parametrize("H,I,E,k,T", SMALL_SHAPES)
-def test_ffn_small_shapes(dev, H, I, E, k, T):
+def test_ffn_small_shapes(dev, H, I, E, k, T, path):
     wl = S.small_workload(H, I, E, k, T, wid=300 + H % 97 + I % 89)
     layer = _layer(wl, dev)
     rng = np.random.default_rng(H * 7 + I)
     ids, w = _random_routing(rng, T, k, E)
     x_bits = S.activations(wl, 0, 0)
-    y = _run_ffn(layer, x_bits, ids, w, dev)
+    y = _run_ffn(layer, x_bits, ids, w, dev, path)
     ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), E, H, I)
-    err, cos = check_ffn(y, ref, f"H{H} I{I} E{E} k{k} T{T}")
-    log(f"H{H} I{I} E{E} k{k} T{T}: normwise {err:.2e} cosine {cos:.7f}")
+    err, cos = check_ffn(y, ref, f"path {path} H{H} I{I} E{E} k{k} T{T}")
+    log(f"path {path} H{H} I{I} E{E} k{k} T{T}: normwise {err:.2e} cosine {cos:.7f}")
 
 
 @pytest.fixture(scope="module")
@@ -243,7 +253,7 @@ def test_moe_forward_matches_route_then_ffn(dev, decode_layer):
     _, D = _mods()
     wl, layer = decode_layer
     wr_bits = S.router_weights(wl, 0)
-    for T, step in ((1, 100), (1, 101), (5, 102)):
+    for T, step in ((1, 100), (1, 101), (5, 102), (40, 103)):
         x_bits = S.activations(wl, 0, step, tokens=T)
         x = D.upload_bf16(x_bits, dev)
         y1, ids1, w1 = layer.forward(x)
@@ -266,12 +276,14 @@ def test_layer_batched64_zipf_full_size(dev, decode_layer):
     torch.cuda.synchronize()
     check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, "zipf64")
     x_bits = S.activations(wl, 0, 0)
-    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w)
-    torch.cuda.synchronize()
     # the layer holds the decode workload's experts
     ref = O.expert_ffn(x_bits, ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
-    err, cos = check_ffn(D.bf16_bits(y), ref, "zipf64")
-    log(f"batched64 zipf: {len(np.unique(ids_ref))} distinct experts, normwise {err:.2e} cosine {cos:.7f}")
+    for path in (DECODE, GROUPED):
+        y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w, path=path)
+        torch.cuda.synchronize()
+        err, cos = check_ffn(D.bf16_bits(y), ref, f"zipf64 path {path}")
+        log(f"batched64 zipf path {path}: {len(np.unique(ids_ref))} distinct experts, "
+            f"normwise {err:.2e} cosine {cos:.7f}")
 
 
 def test_layer_prefill8192_sampled(dev, decode_layer):
@@ -282,14 +294,17 @@ def test_layer_prefill8192_sampled(dev, decode_layer):
     lg = S.router_logits(wl, 0, 0)
     ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
     x_bits = S.activations(wl, 0, 0)
-    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w)
-    torch.cuda.synchronize()
     sample = np.sort(np.random.default_rng(55).choice(8192, size=24, replace=False))
     ids_ref, w_ref = O.topk_softmax(lg[sample].astype(np.float64), 6)
     check_route(ids.cpu().numpy()[sample], w.cpu().numpy()[sample], ids_ref, w_ref, "prefill")
     ref = O.expert_ffn(x_bits[sample], ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
-    err, cos = check_ffn(D.bf16_bits(y)[sample], ref, "prefill8192")
-    log(f"prefill8192 sample of 24: normwise {err:.2e} cosine {cos:.7f}")
+    for path in (DECODE, GROUPED):
+        y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w, path=path)
+        torch.cuda.synchronize()
+        yb = D.bf16_bits(y)
+        assert np.all(np.isfinite(O.bf16_to_f64(yb))), f"path {path}"
+        err, cos = check_ffn(yb[sample], ref, f"prefill8192 path {path}")
+        log(f"prefill8192 path {path}, sample of 24: normwise {err:.2e} cosine {cos:.7f}")
 
 
 # ------------------------------------------------------------------------------ edge cases
@@ -327,7 +342,8 @@ def test_t0_is_a_no_op(dev, small_layer):
     assert torch.all(y == 7)
 
 
-def test_invalid_and_duplicate_ids(dev, small_layer):
+@PATHS
+def test_invalid_and_duplicate_ids(dev, small_layer, path):
     C, D = _mods()
     wl, layer = small_layer
     E = wl.n_experts
@@ -336,9 +352,9 @@ def test_invalid_and_duplicate_ids(dev, small_layer):
                     [-5, -1, E, E + 1, 99, 2 ** 31 - 1]], np.int32)
     w = np.random.default_rng(9).random((3, 6)).astype(np.float32)
     x_bits = S.activations(wl, 0, 1, tokens=3)
-    y = _run_ffn(layer, x_bits, ids, w, dev)
+    y = _run_ffn(layer, x_bits, ids, w, dev, path)
     ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), E, wl.hidden, wl.inter)
-    check_ffn(y[:2], ref[:2], "invalid/duplicate ids")
+    check_ffn(y[:2], ref[:2], f"invalid/duplicate ids, path {path}")
     assert np.all(O.bf16_to_f64(y[2]) == 0.0)  # no valid id: exactly zero
     bad = torch.zeros(1, dtype=torch.int32, device=dev)
     C.moe_fp4_validate_ids(torch.from_numpy(ids).to(dev), 3, 6, E, bad)
@@ -346,44 +362,70 @@ def test_invalid_and_duplicate_ids(dev, small_layer):
     assert int(bad.item()) == int(np.sum((ids < 0) | (ids >= E)))
 
 
+@PATHS
 @pytest.mark.parametrize("k", [1, 8])
-def test_k_extremes(dev, small_layer, k):
+def test_k_extremes(dev, small_layer, k, path):
     wl, layer = small_layer
     rng = np.random.default_rng(10 + k)
     ids, w = _random_routing(rng, 5, k, wl.n_experts)
     x_bits = S.activations(wl, 0, 2, tokens=5)
-    y = _run_ffn(layer, x_bits, ids, w, dev)
+    y = _run_ffn(layer, x_bits, ids, w, dev, path)
     ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
-    check_ffn(y, ref, f"k={k}")
+    check_ffn(y, ref, f"k={k} path {path}")
 
 
-def test_slot_permutation_is_bit_identical(dev, small_layer):
+@PATHS
+def test_slot_permutation_is_bit_identical(dev, small_layer, path):
     wl, layer = small_layer
     rng = np.random.default_rng(11)
     T = 9
     ids, w = _random_routing(rng, T, 6, wl.n_experts)
     ids[0, 1] = ids[0, 0]  # a duplicate id with its own weight
     x_bits = S.activations(wl, 0, 3, tokens=T)
-    y0 = _run_ffn(layer, x_bits, ids, w, dev)
+    y0 = _run_ffn(layer, x_bits, ids, w, dev, path)
     for trial in range(3):
         perm = np.stack([rng.permutation(6) for _ in range(T)])
-        y1 = _run_ffn(layer, x_bits, np.take_along_axis(ids, perm, 1), np.take_along_axis(w, perm, 1), dev)
+        y1 = _run_ffn(layer, x_bits, np.take_along_axis(ids, perm, 1), np.take_along_axis(w, perm, 1),
+                      dev, path)
         assert np.array_equal(y0, y1), f"trial {trial}"
+    # and token order: the grouped path's per-expert grouping must not depend on it
+    tp = rng.permutation(T)
+    y2 = _run_ffn(layer, x_bits[tp], ids[tp], w[tp], dev, path)
+    assert np.array_equal(y0[tp], y2)
 
 
+@pytest.mark.parametrize("path", [None, DECODE, GROUPED], ids=["auto", "decode", "grouped"])
 @pytest.mark.parametrize("T", [1, 17, 64, 65, 300, 1024])
-def test_row_counts_and_repeat_determinism(dev, small_layer, T):
+def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
     """Same input five times: bit-identical outputs and no NaN/Inf, at token counts on both
     sides of 64."""
     wl, layer = small_layer
     rng = np.random.default_rng(T)
     ids, w = _random_routing(rng, T, 6, wl.n_experts)
     x_bits = S.activations(wl, 0, 4, tokens=T)
-    outs = [_run_ffn(layer, x_bits, ids, w, dev) for _ in range(5)]
+    outs = [_run_ffn(layer, x_bits, ids, w, dev, path) for _ in range(5)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     assert np.all(np.isfinite(O.bf16_to_f64(outs[0])))
     sample = np.unique(np.linspace(0, T - 1, min(T, 8)).astype(int))
     ref = O.expert_ffn(x_bits[sample], ids[sample], w[sample], S.expert_source(wl), wl.n_experts,
                        wl.hidden, wl.inter)
-    check_ffn(outs[0][sample], ref, f"T={T}")
+    check_ffn(outs[0][sample], ref, f"T={T} path {path}")
+
+
+def test_auto_path_choice(dev, small_layer):
+    """The automatic choice runs the decode kernels below 16 tokens and the grouped ones
+    from 16 on (read from the library's per-kernel launch counters)."""
+    C, D = _mods()
+    wl, layer = small_layer
+    for T, expect in ((15, "gate_up"), (16, "grouped_gate_up")):
+        rng = np.random.default_rng(T)
+        ids, w = _random_routing(rng, T, 6, wl.n_experts)
+        x_bits = S.activations(wl, 0, 5, tokens=T)
+        C.moe_fp4_timing_reset()
+        C.moe_fp4_timing_enable(True)
+        _run_ffn(layer, x_bits, ids, w, dev)
+        C.moe_fp4_timing_enable(False)
+        launched = {n for kind, n in enumerate(C.KERNEL_NAMES) if C.moe_fp4_timing_read(kind)[0]}
+        C.moe_fp4_timing_reset()
+        assert expect in launched and ("grouped_gate_up" if expect == "gate_up" else "gate_up") not in launched, (T, launched)
