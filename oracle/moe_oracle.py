@@ -306,7 +306,113 @@ def moe_layer(x_bits: np.ndarray, w_router_bits: np.ndarray, k: int, expert_sour
 
 
 # ---------------------------------------------------------------------------------------
-# 5. Layer chaining used by the multi-layer decode workload
+# 5. MX activation formats: the reading taken for activations that enter block-scaled
+#    matrix cores. DeepSeek quantises activations to FP8 with ue8m0 block scales
+#    ([8GB-GPU], RTX 50xx 上的三个从不抛错的 Bug names the act_quant step and its ue8m0 format);
+#    the pages give no block size or rounding, so this follows the OCP MX definition:
+#    blocks of 32 along K, one power-of-two scale 2^X per block, elements rounded to the
+#    nearest value of the element format with ties to the even code.
+# ---------------------------------------------------------------------------------------
+
+#: element formats: (exponent bits, mantissa bits, exponent bias, largest finite value)
+MX_FORMATS = {
+    "e4m3": (4, 3, 7, 448.0),  # FP8; the all-ones code is NaN, so 448 = 1.75 * 2^8 is the top
+    "e2m3": (2, 3, 1, 7.5),    # FP6
+    "e2m1": (2, 1, 1, 6.0),    # FP4 (the weight format)
+}
+
+
+def mx_grid(fmt: str) -> np.ndarray:
+    """Non-negative values of an element format in code order (code i -> grid[i]):
+    subnormals m / 2^mb * 2^(1 - bias), then normals (1 + m / 2^mb) * 2^(e - bias), up to
+    the largest finite value."""
+    eb, mb, bias, vmax = MX_FORMATS[fmt]
+    vals = [m / 2.0 ** mb * 2.0 ** (1 - bias) for m in range(2 ** mb)]
+    for e in range(1, 2 ** eb):
+        for m in range(2 ** mb):
+            vals.append((1.0 + m / 2.0 ** mb) * 2.0 ** (e - bias))
+    vals = [v for v in vals if v <= vmax]
+    return np.array(vals, dtype=np.float64)
+
+
+def mx_round(v: np.ndarray, fmt: str) -> np.ndarray:
+    """Round to the nearest value of the format, ties to the even code (|v| <= max)."""
+    grid = mx_grid(fmt)
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    if np.any(a > grid[-1]):
+        raise ValueError("value outside the format's range")
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, grid.size - 1)
+    lo = np.clip(hi - 1, 0, grid.size - 1)
+    d_hi = grid[hi] - a
+    d_lo = a - grid[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    q = np.where(pick_lo, grid[lo], grid[hi])
+    return np.copysign(q, v)
+
+
+def mx_scale_exponent(amax: float, vmax: float) -> int:
+    """Smallest integer X with amax <= vmax * 2^X, clamped to the ue8m0 range [-127, 127];
+    amax == 0 gives -127."""
+    if amax == 0.0:
+        return -127
+    x = math.frexp(amax)[1] - math.frexp(vmax)[1] - 1
+    while amax > math.ldexp(vmax, x):
+        x += 1
+    while x > -127 and amax <= math.ldexp(vmax, x - 1):
+        x -= 1
+    return max(-127, min(127, x))
+
+
+def mx_scale_exponents(amax: np.ndarray, vmax: float) -> np.ndarray:
+    """mx_scale_exponent for an array of block maxima (same rule, all blocks at once)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    x = np.frexp(amax)[1].astype(np.int64) - math.frexp(vmax)[1] - 1
+    for _ in range(3):  # x starts at most two below the answer
+        x = np.where(amax > np.ldexp(vmax, x), x + 1, x)
+    x = np.where(amax == 0.0, -127, x)
+    return np.clip(x, -127, 127)
+
+
+def mx_quantize(v: np.ndarray, fmt: str, terms: int = 1) -> np.ndarray:
+    """Dequantised value of v [..., K] (K a multiple of 32) after MX quantisation along
+    the last axis: one term q1 = 2^X round(v / 2^X), or two terms q1 + q2 where q2 is the
+    same quantisation of the residual v - q1 with its own block exponent."""
+    v = np.asarray(v, dtype=np.float64)
+    vmax = MX_FORMATS[fmt][3]
+    rem = v.reshape(-1, BLOCK).copy()
+    out = np.zeros_like(rem)
+    for _ in range(terms):
+        x = mx_scale_exponents(np.max(np.abs(rem), axis=1), vmax)[:, None]
+        q = np.ldexp(mx_round(np.ldexp(rem, -x), fmt), x)
+        out += q
+        rem -= q
+    return out.reshape(v.shape)
+
+
+def expert_ffn_mx(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, expert_source: ExpertSource,
+                  n_experts: int, hidden: int, inter: int, fmt: str, terms: int) -> np.ndarray:
+    """expert_ffn with the activations x and h replaced by their MX quantisation (fmt,
+    terms) before each projection: the numerics of a block-scaled matrix-core path, for
+    the activation-format study. fp64 otherwise."""
+    x = mx_quantize(bf16_to_f64(x_bits), fmt, terms)
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    y = np.zeros((x.shape[0], hidden), dtype=np.float64)
+    valid = (ids >= 0) & (ids < n_experts)
+    bufs: list = []
+    for e in np.unique(ids[valid]):
+        rows_t, slots = np.nonzero(ids == e)
+        wg, wu, wd = dequant_expert(*expert_source(int(e)), hidden, inter, bufs)
+        xe = x[rows_t]
+        h = silu(np.matmul(xe, wg.T)) * np.matmul(xe, wu.T)
+        ye = np.matmul(mx_quantize(h, fmt, terms), wd.T)
+        for r in range(rows_t.shape[0]):
+            y[rows_t[r]] += w[rows_t[r], slots[r]] * ye[r]
+    return y
+
+
+# ---------------------------------------------------------------------------------------
+# 6. Layer chaining used by the multi-layer decode workload
 # ---------------------------------------------------------------------------------------
 
 def residual_rmsnorm(r: np.ndarray, y: np.ndarray, eps: float = 1e-6):

@@ -1,0 +1,45 @@
+"""Activation-format study for the block-scaled matrix-core path (CPU, fp64 oracle).
+
+The grouped path feeds the activations x and h to v_mfma_scale_*_f8f6f4 as MX blocks. This
+study runs the oracle FFN at the real shape (hidden 4096, intermediate 2880, 6 experts per
+token) with x and h replaced by their MX quantisation and compares it with the exact
+oracle, per token, against the output tolerance (normwise max relative error 2e-2, cosine
+0.9995): one FP8 term is far from it, two terms (hi + lo) are well inside it. The grouped
+path uses two E4M3 terms.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synth import moe_inputs as S
+
+
+def _worst(y, ref):
+    errs = [O.normwise_rel_err(y[t], ref[t]) for t in range(ref.shape[0])]
+    coss = [O.cosine(y[t], ref[t]) for t in range(ref.shape[0])]
+    return max(errs), min(coss)
+
+
+def test_activation_format_study():
+    wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
+    x_bits = S.activations(wl, 0, 0, tokens=2)
+    rng = np.random.default_rng(12)
+    ids = np.stack([rng.permutation(wl.n_experts)[:6] for _ in range(2)]).astype(np.int32)
+    gen = S.expert_source(wl, 0)
+    blobs = {int(e): gen(int(e)) for e in np.unique(ids)}  # generated once, used four times
+    src = blobs.__getitem__
+    w = rng.random((2, 6)) + 0.05
+    ref = O.expert_ffn(x_bits, ids, w, src, wl.n_experts, wl.hidden, wl.inter)
+    res = {}
+    for fmt, terms in (("e4m3", 1), ("e4m3", 2), ("e2m3", 2)):
+        y = O.expert_ffn_mx(x_bits, ids, w, src, wl.n_experts, wl.hidden, wl.inter, fmt, terms)
+        res[(fmt, terms)] = _worst(y, ref)
+    err1, cos1 = res[("e4m3", 1)]
+    err2, cos2 = res[("e4m3", 2)]
+    err6, cos6 = res[("e2m3", 2)]
+    # two terms: inside the tolerance with a wide margin (the grouped path's choice)
+    assert err2 <= 5e-3 and cos2 >= 0.99999, res
+    assert err6 <= 1e-2 and cos6 >= 0.9999, res
+    # one FP8 term is an order of magnitude worse than two
+    assert err1 >= 5 * err2 and err1 >= 1e-2, res

@@ -347,3 +347,65 @@ def test_bf16_round_trip_and_rounding_against_torch():
     assert np.array_equal(O.bf16_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
     # the generator's fp32 -> bf16 rounding agrees with torch too
     assert np.array_equal(S.f32_to_bf16_bits(v), ref)
+
+
+# ------------------------------------------------------------------------- MX activations
+
+def test_mx_grids_match_the_format_definitions():
+    """Value counts and extremes of the element formats, and E2M1 equal to the weight
+    table (itself pinned to the pages' integer set above)."""
+    g8, g6, g4 = O.mx_grid("e4m3"), O.mx_grid("e2m3"), O.mx_grid("e2m1")
+    # E4M3: zero, 7 subnormals, 15 binades x 8 minus the NaN code
+    assert g8.size == 127 and g8[-1] == 448.0 and g8[1] == 2.0 ** -9
+    assert g6.size == 32 and g6[-1] == 7.5 and g6[1] == 0.125
+    assert np.array_equal(g4, O.e2m1_table()[:8])
+    for g in (g8, g6, g4):
+        assert np.all(np.diff(g) > 0)
+
+
+def test_mx_round_e4m3_matches_torch_float8():
+    """Round-to-nearest-even onto E4M3 against torch's float8_e4m3fn conversion (an
+    independent implementation), including exact midpoints between grid values."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    g = O.mx_grid("e4m3")
+    mids = (g[:-1] + g[1:]) / 2.0
+    vals = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-1, 1, 2000) * 2.0 ** -6,
+                           mids, -mids, g, -g]).astype(np.float32).astype(np.float64)
+    ref = torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.mx_round(vals, "e4m3"), ref)
+
+
+def test_mx_scale_exponent_is_the_smallest_fitting_power():
+    for n in (-20, -8, 0, 7):
+        top = np.ldexp(448.0, n)
+        assert O.mx_scale_exponent(top, 448.0) == n
+        assert O.mx_scale_exponent(np.nextafter(top, np.inf), 448.0) == n + 1
+    assert O.mx_scale_exponent(1.0, 448.0) == -8      # 448 * 2^-9 = 0.875 < 1 <= 1.75
+    assert O.mx_scale_exponent(1.76, 448.0) == -7
+    assert O.mx_scale_exponent(0.0, 448.0) == -127
+    assert O.mx_scale_exponent(6.0, 6.0) == 0 and O.mx_scale_exponent(6.5, 6.0) == 1
+
+
+def test_mx_two_terms_bound_and_one_term_exactness():
+    """Two E4M3 terms reproduce a block to within 2^-7 of its maximum; values already on
+    the scaled grid survive one term exactly."""
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((64, 128)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    q2 = O.mx_quantize(v, "e4m3", 2)
+    amax = np.abs(v).reshape(-1, 32).max(axis=1)
+    err = np.abs(q2 - v).reshape(-1, 32).max(axis=1)
+    assert np.all(err <= amax * 2.0 ** -7)
+    q1 = O.mx_quantize(v, "e4m3", 1)
+    assert np.array_equal(O.mx_quantize(q1, "e4m3", 1), q1)
+    # a whole block of zeros stays zero
+    assert np.all(O.mx_quantize(np.zeros((1, 32)), "e4m3", 2) == 0.0)
+
+
+def test_mx_scale_exponents_vector_form_matches_scalar_rule():
+    rng = np.random.default_rng(7)
+    a = np.concatenate([np.ldexp(rng.uniform(0.5, 1.0, 500), rng.integers(-140, 120, 500)),
+                        np.ldexp(448.0, np.arange(-20, 20)), [0.0, 448.0, 449.0, 1.75]])
+    for vmax in (448.0, 7.5, 6.0):
+        vec = O.mx_scale_exponents(a, vmax)
+        assert [O.mx_scale_exponent(float(v), vmax) for v in a] == list(vec)
