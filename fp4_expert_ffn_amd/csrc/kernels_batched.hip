@@ -11,9 +11,9 @@
 //    each. The pair reproduces bf16 inputs to about 2^-8 of the block maximum; one FP8 term
 //    alone does not meet the output tolerance. The scale exponent is the smallest X with
 //    max|v| <= 448 * 2^X, so no element overflows the E4M3 range.
-// 3. gemm_gate_up_kernel: per (M-block, 64 rows of I): g and u for 64 rows of gate and up,
+// 3. gemm_gate_up_kernel: per (M-block, 128 rows of I): g and u for 128 rows of gate and up,
 //    h = silu(g) * u, quantised in the epilogue to MXFP8 hi + lo (blocks of 32 along I).
-// 4. gemm_down_kernel: per (M-block, 64 rows of H): y_e = W_down h, times the pair's router
+// 4. gemm_down_kernel: per (M-block, 128 rows of H): y_e = W_down h, times the pair's router
 //    weight, written fp32 per pair.
 // 5. combine_kernel: y[t] = sum of the token's valid pairs in canonical slot order (ascending
 //    expert id, then weight bits, then slot) -> bf16.
@@ -50,7 +50,8 @@ __device__ __forceinline__ uint4 ld_nt16(const uint8_t* p) {
 
 constexpr int kBWaves = 4;
 constexpr int kBThreads = kBWaves * 64;
-constexpr int kBN = 16 * kBWaves;       // weight rows per workgroup
+constexpr int kNS = 2;                  // 16-row weight tiles per wave (per matrix)
+constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
 constexpr int kMSub = kBlockRows / 16;  // 16-row MFMA subtiles per M-block
 constexpr int kAPitch = 272;            // LDS bytes per staged A row: hi 128 | lo 128 | pad 16
 constexpr int kSortThreads = 1024;
@@ -237,18 +238,20 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------------------------------
 // Grouped GEMM core shared by both stages. A workgroup owns one M-block (up to kBlockRows
-// rows of one expert's group) and kBN weight rows (wave w: 16-row tile n0 / 16 + w of each of
-// its NMAT matrices). Per 128-element chunk of K:
+// rows of one expert's group) and kBN weight rows: wave w takes kNS = 2 consecutive 16-row
+// tiles of each of its matrices, so every A operand read from LDS feeds 2 (down) or 4
+// (gate and up) pairs of MFMAs. Per 128-element chunk of K:
 //  * the block's A rows (hi, lo, scales) are staged in one of two LDS buffers; each thread
 //    moves four 16-byte pieces and (threads < 2 * kBlockRows) one scale dword, loaded from
 //    global memory about one chunk ahead of their store;
-//  * each wave loads its B words (one 1 KB word per matrix) two chunks ahead;
+//  * each wave loads its B words (one 1 KB word per tile) two chunks ahead;
 //  * 16-row subtiles past the block's rows are skipped (wave-uniform);
 //  * one barrier per chunk.
 // Every load is issued with a clamped chunk index, so the wait counts stay exact. The GEMM
-// kernels are held to 4 wavefronts per SIMD (at most 128 registers per lane; the two LDS
-// buffers of 17.9 KB each allow 4 workgroups per CU), so other workgroups' chunks cover
-// each wave's memory waits.
+// kernels are held to 2 (gate/up: 4 B words and 64 accumulators per lane) and 4 (down)
+// wavefronts per SIMD (at most 256 / 128 registers per lane; the two LDS buffers of 17.9 KB
+// each allow 4 workgroups per CU), so other workgroups' chunks cover each wave's memory
+// waits.
 // ---------------------------------------------------------------------------------------
 struct GemmCtx {
   const uint8_t* ahi;
@@ -307,17 +310,18 @@ __device__ __forceinline__ i32x8_t b_operand(uint4 w) {
   return i32x8_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
 }
 
-// One matrix's B word for this lane: 16 code bytes and the scale byte (zero / 1 past K).
+// One B word for this lane: 16 code bytes and the scale byte (zero / 1 past K or past the
+// matrix rows).
 struct BWord {
   uint4 w;
   uint32_t s;
 };
 
 __device__ __forceinline__ BWord load_b(const uint8_t* codes, const uint8_t* scales, int c,
-                                        int KB, bool wave_on) {
+                                        int KB, bool on) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const bool ok = wave_on && 4 * c + g < KB;
+  const bool ok = on && 4 * c + g < KB;
   const long w = (4 * c + g < KB) ? 64L * c + lane : 64L * c;  // past K: any valid word
   BWord b;
   b.w = ld_nt16(codes + 16 * w);
@@ -329,13 +333,48 @@ __device__ __forceinline__ BWord load_b(const uint8_t* codes, const uint8_t* sca
   return b;
 }
 
-// acc[m][q] accumulates 16-row subtile m of matrix q (0: codes0 / scales0, 1: codes1 ...).
-template <int NMAT>
-__device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const uint8_t* codes0,
-                                            const uint8_t* scales0, const uint8_t* codes1,
-                                            const uint8_t* scales1, bool wave_on, int rows,
-                                            uint8_t* lds, uint8_t* lds_s,
-                                            f32x4_t (&acc)[kMSub][NMAT]) {
+// The B words of one wave: NB = (matrices) x kNS tiles, word q = matrix * kNS + tile. Named
+// members (an array carried around the K loop would be placed in private memory).
+struct BPtrs {
+  const uint8_t *c0, *c1, *c2, *c3;  // code base of word q (tile-major word 0)
+  const uint8_t *s0, *s1, *s2, *s3;  // scale base of word q
+  bool on0, on1, on2, on3;           // tile q lies inside its matrix
+};
+
+template <int NB>
+struct BSet {
+  BWord w0, w1, w2, w3;
+};
+
+template <int NB>
+__device__ __forceinline__ BSet<NB> load_bset(const BPtrs& p, int c, int KB) {
+  BSet<NB> r;
+  r.w0 = load_b(p.c0, p.s0, c, KB, p.on0);
+  r.w1 = r.w0;
+  r.w2 = r.w0;
+  r.w3 = r.w0;
+  if constexpr (NB > 1) r.w1 = load_b(p.c1, p.s1, c, KB, p.on1);
+  if constexpr (NB > 2) r.w2 = load_b(p.c2, p.s2, c, KB, p.on2);
+  if constexpr (NB > 3) r.w3 = load_b(p.c3, p.s3, c, KB, p.on3);
+  return r;
+}
+
+// acc[m][q] accumulates 16-row subtile m against B word q.
+template <int NB>
+struct Acc {
+  f32x4_t a[kMSub][NB];
+};
+
+__device__ __forceinline__ void mfma2(f32x4_t& acc, const i32x8_t& ahi, const i32x8_t& alo,
+                                      const BWord& b, int sw_hi, int sw_lo) {
+  const i32x8_t bq = b_operand(b.w);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bq, acc, 0, 4, 0, sw_hi, 0, (int)b.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, (int)b.s);
+}
+
+template <int NB>
+__device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, int rows,
+                                            uint8_t* lds, uint8_t* lds_s, Acc<NB>& acc) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int r = lane & 15;
@@ -347,13 +386,9 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const uint8_t* co
   stage_load(cx, 0, d0, d1, d2, d3, sv);
   stage_store(lds, lds_s, d0, d1, d2, d3, sv);
   stage_load(cx, min(1, nch - 1), d0, d1, d2, d3, sv);
-  BWord b0c = load_b(codes0, scales0, 0, cx.KB, wave_on);
-  BWord b0n = load_b(codes0, scales0, min(1, nch - 1), cx.KB, wave_on);
-  BWord b1c = b0c, b1n = b0n;
-  if constexpr (NMAT > 1) {
-    b1c = load_b(codes1, scales1, 0, cx.KB, wave_on);
-    b1n = load_b(codes1, scales1, min(1, nch - 1), cx.KB, wave_on);
-  }
+  BSet<NB> bcur = load_bset<NB>(bp, 0, cx.KB);
+  BSet<NB> bnxt = load_bset<NB>(bp, min(1, nch - 1), cx.KB);
+  const bool any_on = bp.on0;  // tile 0 of matrix 0 is the wave's first tile
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const uint8_t* A = lds + (c & 1) * kBuf;
@@ -364,9 +399,7 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const uint8_t* co
     const bool h0 = 4 * c + (g >> 1) < cx.KB;
     const bool h1 = 4 * c + 2 + (g >> 1) < cx.KB;
     const bool s_ok = 4 * c + g < cx.KB;
-    if (wave_on) {
-      const i32x8_t bq0 = b_operand(b0c.w);
-      const i32x8_t bq1 = b_operand(b1c.w);
+    if (any_on) {
 #pragma unroll
       for (int m = 0; m < kMSub; ++m) {
         if (16 * m < rows) {  // wave-uniform
@@ -374,16 +407,10 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const uint8_t* co
           const i32x8_t alo = a_operand(A, m, lane, true, h0, h1);
           const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;
           const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;
-          acc[m][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              ahi, bq0, acc[m][0], 0, 4, 0, sw_hi, 0, (int)b0c.s);
-          acc[m][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              alo, bq0, acc[m][0], 0, 4, 0, sw_lo, 0, (int)b0c.s);
-          if constexpr (NMAT > 1) {
-            acc[m][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                ahi, bq1, acc[m][1], 0, 4, 0, sw_hi, 0, (int)b1c.s);
-            acc[m][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                alo, bq1, acc[m][1], 0, 4, 0, sw_lo, 0, (int)b1c.s);
-          }
+          mfma2(acc.a[m][0], ahi, alo, bcur.w0, sw_hi, sw_lo);
+          if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, bcur.w1, sw_hi, sw_lo);
+          if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, bcur.w2, sw_hi, sw_lo);
+          if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, bcur.w3, sw_hi, sw_lo);
         }
       }
     }
@@ -392,12 +419,8 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const uint8_t* co
     stage_store(lds + ((c + 1) & 1) * kBuf, lds_s + ((c + 1) & 1) * kBufS, d0, d1, d2, d3, sv);
     const int cn = min(c + 2, nch - 1);
     stage_load(cx, cn, d0, d1, d2, d3, sv);
-    b0c = b0n;
-    b0n = load_b(codes0, scales0, cn, cx.KB, wave_on);
-    if constexpr (NMAT > 1) {
-      b1c = b1n;
-      b1n = load_b(codes1, scales1, cn, cx.KB, wave_on);
-    }
+    bcur = bnxt;
+    bnxt = load_bset<NB>(bp, cn, cx.KB);
     __syncthreads();
   }
 }
@@ -419,7 +442,7 @@ __device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
 // ---------------------------------------------------------------------------------------
 // 3. gate / up / SiLU / h quantisation
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_gate_up_kernel(
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_gate_up_kernel(
     const uint8_t* __restrict__ xhi, const uint8_t* __restrict__ xlo,
     const uint8_t* __restrict__ xshi, const uint8_t* __restrict__ xslo, int Hp,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_expert,
@@ -440,8 +463,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   const int wv = tid >> 6;
   const int lane = tid & 63;
   const int KB = H / kBlock;
-  const int tile = nt * kBWaves + wv;  // 16-row tile of gate / up
-  const bool wave_on = 16 * tile < I;
+  const int tile0 = (nt * kBWaves + wv) * kNS;  // first 16-row tile of gate / up of this wave
 
   GemmCtx cx;
   cx.ahi = xhi;
@@ -453,28 +475,45 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   gemm_ctx_rows(cx, [&](int i) { return perm[row0 + min(i, rows - 1)] / k; });
 
   const uint8_t* base = packed + (size_t)e * stride;
-  const size_t tb = (size_t)min(tile, I / 16 - 1) * 16 * KB;  // tile-major word index
-  f32x4_t acc[kMSub][2];
+  const int nt16 = I / 16;
+  const size_t tb0 = (size_t)min(tile0, nt16 - 1) * 16 * KB;  // tile-major word index
+  const size_t tb1 = (size_t)min(tile0 + 1, nt16 - 1) * 16 * KB;
+  BPtrs bp;
+  bp.c0 = base + off_gc + 16 * tb0;  // word 0: gate tile0, 1: gate tile0+1, 2: up tile0, 3: up tile0+1
+  bp.c1 = base + off_gc + 16 * tb1;
+  bp.c2 = base + off_uc + 16 * tb0;
+  bp.c3 = base + off_uc + 16 * tb1;
+  bp.s0 = base + off_gs + tb0;
+  bp.s1 = base + off_gs + tb1;
+  bp.s2 = base + off_us + tb0;
+  bp.s3 = base + off_us + tb1;
+  bp.on0 = bp.on2 = tile0 < nt16;
+  bp.on1 = bp.on3 = tile0 + 1 < nt16;
+  Acc<4> acc;
 #pragma unroll
-  for (int m = 0; m < kMSub; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<2>(cx, base + off_gc + 16 * tb, base + off_gs + tb, base + off_uc + 16 * tb,
-                 base + off_us + tb, wave_on, rows, lds, lds_s, acc);
+  for (int m = 0; m < kMSub; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gemm_k_loop<4>(cx, bp, rows, lds, lds_s, acc);
 
-  // epilogue: h (fp32) for the block's rows x 64 columns into LDS (the loop ended with a
+  // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
   float* htile = reinterpret_cast<float*>(lds);  // [kBlockRows][kBN + 1]
   constexpr int kHP = kBN + 1;
+  static_assert(kBlockRows * kHP * 4 <= 2 * kBlockRows * kAPitch, "h tile fits the A buffers");
 #pragma unroll
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 16 * m + 4 * (lane >> 4) + q;  // block row
-      const float gv = acc[m][0][q], uv = acc[m][1][q];
-      htile[i * kHP + 16 * wv + (lane & 15)] = silu_f32(gv) * uv;
+      const int col = 32 * wv + (lane & 15);        // tile tile0 (cols +0..15), tile0+1 (+16..31)
+      htile[i * kHP + col] = silu_f32(acc.a[m][0][q]) * acc.a[m][2][q];
+      htile[i * kHP + col + 16] = silu_f32(acc.a[m][1][q]) * acc.a[m][3][q];
     }
   __syncthreads();
-  if (tid < 2 * kBlockRows) {
-    const int r = tid >> 1, b = tid & 1;
+  static_assert(kBlockRows * (kBN / 32) == kBThreads, "one (row, 32-block) per thread");
+  {
+    const int r = tid / (kBN / 32), b = tid % (kBN / 32);
     const int col = nt * kBN + 32 * b;  // first I index of this 32-block
     if (r < rows && col < I) {
       float v[32];
@@ -519,8 +558,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   const int wv = tid >> 6;
   const int lane = tid & 63;
   const int KB = I / kBlock;
-  const int tile = nt * kBWaves + wv;  // 16-row tile of down (rows of H)
-  const bool wave_on = 16 * tile < H;
+  const int tile0 = (nt * kBWaves + wv) * kNS;  // first 16-row tile of down (rows of H)
 
   GemmCtx cx;
   cx.ahi = hhi;
@@ -532,25 +570,41 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   gemm_ctx_rows(cx, [&](int i) { return row0 + min(i, rows - 1); });
 
   const uint8_t* base = packed + (size_t)e * stride;
-  const size_t tb = (size_t)min(tile, H / 16 - 1) * 16 * KB;
-  f32x4_t acc[kMSub][1];
+  const int nt16 = H / 16;
+  const size_t tb0 = (size_t)min(tile0, nt16 - 1) * 16 * KB;
+  const size_t tb1 = (size_t)min(tile0 + 1, nt16 - 1) * 16 * KB;
+  BPtrs bp;
+  bp.c0 = base + off_dc + 16 * tb0;
+  bp.c1 = base + off_dc + 16 * tb1;
+  bp.c2 = bp.c3 = bp.c0;
+  bp.s0 = base + off_ds + tb0;
+  bp.s1 = base + off_ds + tb1;
+  bp.s2 = bp.s3 = bp.s0;
+  bp.on0 = tile0 < nt16;
+  bp.on1 = tile0 + 1 < nt16;
+  bp.on2 = bp.on3 = false;
+  Acc<2> acc;
 #pragma unroll
-  for (int m = 0; m < kMSub; ++m) acc[m][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<1>(cx, base + off_dc + 16 * tb, base + off_ds + tb, nullptr, nullptr, wave_on,
-                 rows, lds, lds_s, acc);
+  for (int m = 0; m < kMSub; ++m) acc.a[m][0] = acc.a[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gemm_k_loop<2>(cx, bp, rows, lds, lds_s, acc);
 
-  if (!wave_on) return;
-  const int n = 16 * tile + (lane & 15);
 #pragma unroll
-  for (int m = 0; m < kMSub; ++m)
+  for (int s2 = 0; s2 < kNS; ++s2) {
+    const int tile = tile0 + s2;
+    if (tile < nt16) {
+      const int n = 16 * tile + (lane & 15);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = 16 * m + 4 * (lane >> 4) + q;
-      if (i < rows) {
-        const int pair = perm[row0 + i];
-        ypair[(size_t)pair * H + n] = wts[pair] * acc[m][0][q];
-      }
+      for (int m = 0; m < kMSub; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * m + 4 * (lane >> 4) + q;
+          if (i < rows) {
+            const int pair = perm[row0 + i];
+            ypair[(size_t)pair * H + n] = wts[pair] * acc.a[m][s2][q];
+          }
+        }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
