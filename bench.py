@@ -98,7 +98,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="layer_decode_h4096_i2880_e384",
                     choices=["layer_decode_h4096_i2880_e384", "batched64_zipf", "prefill8192_uniform",
-                             "prefill32768_uniform"],
+                             "prefill32768_uniform", "stack16_decode", "expert_h256_i128"],
                     help="the batch-1 decode layer (default, the headline line), or one of the "
                          "batched shapes run through the grouped GEMM path")
     ap.add_argument("--steps", type=int, default=500)
@@ -120,6 +120,10 @@ def main() -> int:
               "(this build runs on a single MI355X).", file=sys.stderr)
         return 2
 
+    if args.workload == "stack16_decode":
+        return run_stack(args)
+    if args.workload == "expert_h256_i128":
+        return run_single_expert(args)
     if args.workload != "layer_decode_h4096_i2880_e384":
         return run_batched(args)
 
@@ -264,6 +268,168 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_stack(args) -> int:
+    """16 chained MoE layers at batch 1 (about 116 GB of FP4 experts resident): per token,
+    the residual starts as the token's x; every layer routes x (one-launch routing), runs
+    the expert FFN, then residual += y and x = RMSNorm(residual) feed the next layer."""
+    import torch
+
+    from fp4_expert_ffn_amd import device as D
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    from synth import moe_inputs as S
+
+    C.lib()
+    dev = torch.device("cuda:0")
+    wl = S.WORKLOADS["stack16_decode"]
+    H, I, E, k, L = wl.hidden, wl.inter, wl.n_experts, wl.k, wl.layers
+    K, W = min(args.steps, 200), min(args.warmup, 10)
+    stride = C.moe_fp4_packed_expert_stride(H, I)
+    log(f"{wl.name}: generating and packing {L} x {E} experts on the device "
+        f"({L * E * expert_bytes(H, I) / 1e9:.1f} GB)")
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        packed = torch.empty(stride * E, dtype=torch.uint8, device=dev)
+        for e0 in range(0, E, 32):
+            e1 = min(E, e0 + 32)
+            codes, scales = S.device_expert_blobs(wl, l, e0, e1, dev)
+            C.moe_fp4_pack(codes, scales, e1 - e0, H, I, packed.data_ptr() + e0 * stride,
+                           (e1 - e0) * stride)
+            del codes, scales
+        wr = D.upload_bf16(S.router_weights(wl, l), dev)
+        layers.append(D.MoeFp4Layer(packed, E, H, I, k, wr))
+    torch.cuda.synchronize()
+    xs = D.upload_bf16(np.concatenate([S.activations(wl, 0, t) for t in range(W + 2 * K)]), dev)
+    log(f"setup done in {time.time() - t0:.1f} s")
+    ws = layers[0]._forward_workspace(1)
+    for lay in layers:
+        lay._fws = ws  # one workspace for the whole stack (stream-ordered)
+    r = torch.empty((1, H), dtype=torch.float32, device=dev)
+    xa = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+    xb = torch.empty_like(xa)
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    w = torch.empty((1, k), dtype=torch.float32, device=dev)
+    y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+
+    def step(t: int) -> None:
+        x = xs[t:t + 1]
+        C.moe_fp4_residual_init(x, r, 1, H)
+        for l, lay in enumerate(layers):
+            lay.forward_fused(x, ids, w, y)
+            xn = xa if l % 2 == 0 else xb
+            C.moe_fp4_residual_rmsnorm(r, y, xn, 1, H, 1e-6)
+            x = xn
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    graph = None
+    if args.mode == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for t in range(W, W + K):
+                step(t)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for t in range(W, W + K):
+            step(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed_s = max(gpu_ms / 1e3, 1e-9)
+    token_bytes = L * (k * expert_bytes(H, I) + E * H * 2 + 2 * H * 2)
+    log(f"timed {K} tokens x {L} layers ({args.mode}): {gpu_ms:.3f} ms -> {K / elapsed_s:.1f} tokens/s, "
+        f"{token_bytes * K / elapsed_s / 1e9:.0f} GB/s")
+    kernels = {}
+    if not args.no_roofline_pass:
+        C.moe_fp4_timing_reset()
+        C.moe_fp4_timing_enable(True)
+        for t in range(W + K, W + 2 * K):
+            step(t)
+        torch.cuda.synchronize()
+        C.moe_fp4_timing_enable(False)
+        for kind, name in enumerate(C.KERNEL_NAMES):
+            n, ms = C.moe_fp4_timing_read(kind)
+            if n:
+                kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+        C.moe_fp4_timing_reset()
+        log("kernels: " + json.dumps(kernels))
+    out = {
+        "metric": "16-layer MoE decode tokens/s at batch 1 (+ achieved HBM GB/s)",
+        "value": round(K / elapsed_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(gpu_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "hidden": H, "intermediate": I, "experts": E,
+                   "top_k": k, "batch_tokens": 1, "launch": args.mode, "parallelism": "none (1 GPU)"},
+        "algorithmic_gbps": round(token_bytes * K / elapsed_s / 1e9, 1),
+        "hbm_frac_step": round(token_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_step": token_bytes,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_single_expert(args) -> int:
+    """One SwiGLU expert at batch 1 (hidden 256, intermediate 128): microseconds per
+    moe_fp4_expert_ffn call, stream-launched (launch latency bound, weights in L2)."""
+    import torch
+
+    from fp4_expert_ffn_amd import device as D
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    from synth import moe_inputs as S
+
+    C.lib()
+    dev = torch.device("cuda:0")
+    wl = S.WORKLOADS["expert_h256_i128"]
+    H, I = wl.hidden, wl.inter
+    K, W = min(args.steps, 2000), min(args.warmup, 100)
+    packed = D.upload_experts(S.expert_source(wl, 0), 1, H, I, dev)
+    layer = D.MoeFp4Layer(packed, 1, H, I, 1)
+    x = D.upload_bf16(S.activations(wl, 0, 0), dev)
+    ids = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    w = torch.ones((1, 1), dtype=torch.float32, device=dev)
+    y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+    layer._workspace(1, 1)
+    for _ in range(W):
+        layer.ffn(x, ids, w, y)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(K):
+        layer.ffn(x, ids, w, y)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / K
+    log(f"single expert H{H} I{I}: {us:.2f} us per call (two kernel launches)")
+    out = {"metric": "single-expert FFN call latency", "value": round(us, 3), "unit": "us/call",
+           "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(us / 1e3, 6),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": wl.name, "hidden": H, "intermediate": I,
+                                            "launch": "stream"}}
     print(json.dumps(out), flush=True)
     return 0
 

@@ -167,7 +167,7 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
 }
 
 // Token count from which the automatic path choice takes the grouped GEMM path.
-constexpr int kGroupedMinTokens = 16;
+constexpr int kGroupedMinTokens = 24;
 
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter) {
   if (T < 0 || k < 1 || k > kMaxK || n_experts <= 0 || !valid_dim(hidden) || !valid_dim(inter))
@@ -264,6 +264,23 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
   void* ffn_ws = static_cast<uint8_t*>(workspace) + moe_fp4_route_workspace_bytes(T, n_experts);
   return from_hip(ffn_impl(x, topk_ids, topk_w, T, k, static_cast<const uint8_t*>(packed),
                            n_experts, hidden, inter, y, ffn_ws, chosen, s));
+}
+
+int moe_fp4_residual_init(const uint16_t* x, float* residual, int T, int hidden, void* stream) {
+  if (!x || !residual || T < 0 || hidden <= 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!aligned4(residual) || (reinterpret_cast<uintptr_t>(x) & 1u)) return MOE_FP4_ERR_MISALIGNED;
+  if (T == 0) return MOE_FP4_OK;
+  return from_hip(launch_residual_init(x, residual, T, hidden, static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_residual_rmsnorm(float* residual, const uint16_t* y, uint16_t* x_out, int T,
+                             int hidden, float eps, void* stream) {
+  if (!residual || !y || !x_out || T < 0 || hidden <= 0 || !(eps >= 0.f)) return MOE_FP4_ERR_INVALID_ARG;
+  if (hidden % 8 != 0 || hidden > kMaxDim) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(residual) || !aligned16(y) || !aligned16(x_out)) return MOE_FP4_ERR_MISALIGNED;
+  if (T == 0) return MOE_FP4_OK;
+  return from_hip(launch_residual_rmsnorm(residual, y, x_out, T, hidden, eps,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts, int32_t* bad_count,

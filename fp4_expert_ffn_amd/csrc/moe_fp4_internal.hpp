@@ -20,7 +20,7 @@ constexpr int kMaxExpertsTopk = 2048;  // max experts for the top-k selection ke
 enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp = 3,
                   kKindDownCombine = 4, kKindRouteDecode = 5, kKindBatchedSort = 6,
                   kKindBatchedQuant = 7, kKindBatchedGateUp = 8, kKindBatchedDown = 9,
-                  kKindBatchedCombine = 10 };
+                  kKindBatchedCombine = 10, kKindNorm = 11 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -137,6 +137,11 @@ BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter)
 hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
                               const uint8_t* packed, int n_experts, int hidden, int inter,
                               uint16_t* y, void* workspace, hipStream_t s);
+
+// Layer chaining helpers (multi-layer decode harness).
+hipError_t launch_residual_init(const uint16_t* x, float* r, int T, int hidden, hipStream_t s);
+hipError_t launch_residual_rmsnorm(float* r, const uint16_t* y, uint16_t* x, int T, int hidden,
+                                   float eps, hipStream_t s);
 
 hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
                                 int matrix, float* out, hipStream_t s);

@@ -28,7 +28,8 @@ ERR_HIP = -5
 
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
 KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
-                "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine")
+                "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine",
+                "norm")
 
 
 class MoeFp4Error(RuntimeError):
@@ -55,6 +56,8 @@ _SIGNATURES = {
     "moe_fp4_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_expert_ffn": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_fp4_expert_ffn_ex": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _I, _P]),
+    "moe_fp4_residual_init": (_I, [_P, _P, _I, _I, _P]),
+    "moe_fp4_residual_rmsnorm": (_I, [_P, _P, _P, _I, _I, ctypes.c_float, _P]),
     "moe_fp4_moe_forward_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -170,6 +173,17 @@ def moe_fp4_expert_ffn(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: i
 
 
 PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
+
+
+def moe_fp4_residual_init(x, residual, T: int, hidden: int, stream=None) -> None:
+    _check(lib().moe_fp4_residual_init(_ptr(x), _ptr(residual), T, hidden, _stream(stream)),
+           "moe_fp4_residual_init")
+
+
+def moe_fp4_residual_rmsnorm(residual, y, x_out, T: int, hidden: int, eps: float = 1e-6,
+                             stream=None) -> None:
+    _check(lib().moe_fp4_residual_rmsnorm(_ptr(residual), _ptr(y), _ptr(x_out), T, hidden, eps,
+                                          _stream(stream)), "moe_fp4_residual_rmsnorm")
 
 
 def moe_fp4_expert_ffn_ex(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: int,

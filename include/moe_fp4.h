@@ -152,7 +152,8 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
  *    h enter the matrix cores as two-term MXFP8 (E4M3 hi + lo, one ue8m0 scale per 32
  *    elements each), accumulation is fp32, each pair's weighted output is combined per token
  *    in canonical slot order (five launches; needs n_experts <= 2048).
- *  MOE_FP4_PATH_AUTO: GROUPED from 16 tokens on, DECODE below.
+ *  MOE_FP4_PATH_AUTO: GROUPED from 24 tokens on, DECODE below (the measured crossover on
+ *    the 384-expert layer with uniform routing lies between 16 and 24 tokens).
  * moe_fp4_expert_ffn is this call with MOE_FP4_PATH_AUTO. The workspace size covers every
  * path. Errors: as moe_fp4_expert_ffn; an unknown path is INVALID_ARG, a shape the chosen
  * path cannot take is BAD_SHAPE. */
@@ -184,6 +185,23 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
                         int n_experts, int k, const void* packed, int inter, int32_t* topk_ids,
                         float* topk_w, uint16_t* y, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Layer chaining, for stacks of MoE layers (a harness step of the multi-layer decode
+ * workload: RMSNorm is among the per-layer kernels of a decode step, [A100-FP4], section
+ * 然后又发现每 token 启动 2000 次内核; residual and unit gain are the plain reading).
+ * moe_fp4_residual_init:    residual [T x hidden] fp32 = x [T x hidden] bf16.
+ * moe_fp4_residual_rmsnorm: residual += y (bf16, fp32 add), then
+ *                           x_out = bf16_rne(residual / sqrt(mean(residual^2) + eps)),
+ *                           the mean of squares accumulated in fp64; residual is updated
+ *                           in place, x_out may not alias y.
+ * moe_fp4_residual_rmsnorm needs hidden % 8 == 0 and hidden <= 16384 (BAD_SHAPE) and
+ * 16-byte aligned arrays; moe_fp4_residual_init needs residual 4-byte and x 2-byte
+ * alignment. Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, HIP.
+ * ------------------------------------------------------------------------------------ */
+int moe_fp4_residual_init(const uint16_t* x, float* residual, int T, int hidden, void* stream);
+int moe_fp4_residual_rmsnorm(float* residual, const uint16_t* y, uint16_t* x_out, int T,
+                             int hidden, float eps, void* stream);
 
 /* Debug helper: counts the entries of topk_ids [T x k] outside [0, n_experts) into
  * *bad_count (a device int32 that this call overwrites). */
@@ -217,7 +235,8 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
 #define MOE_FP4_KERNEL_GROUPED_GATE_UP 8
 #define MOE_FP4_KERNEL_GROUPED_DOWN 9
 #define MOE_FP4_KERNEL_GROUPED_COMBINE 10
-#define MOE_FP4_KERNEL_KINDS 11
+#define MOE_FP4_KERNEL_NORM 11 /* residual init and residual + RMSNorm */
+#define MOE_FP4_KERNEL_KINDS 12
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

@@ -148,6 +148,24 @@ def random_codes(rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
     return rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
 
 
+def device_expert_blobs(wl: Workload, layer: int, e0: int, e1: int, device, root: int = 0):
+    """Codes [e1 - e0, 3 H I / 2] and scales [e1 - e0, 3 H I / 32] (uint8, canonical layout)
+    of experts e0 .. e1 - 1 drawn on the device with torch's counter-based Philox
+    generator, seeded by (root, workload, layer, e0): the distributions of expert_blob
+    (uniform code bytes, scale bytes uniform in [scale_lo, scale_hi]) for stacks too large
+    to generate on the host. A different generator than expert_blob, so the values differ."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([root, wl.wid, layer, e0, 99]).generate_state(1)[0]))
+    n = e1 - e0
+    codes = torch.randint(0, 256, (n, wl.expert_code_bytes), dtype=torch.uint8, device=device,
+                          generator=g)
+    scales = torch.randint(wl.scale_lo, wl.scale_hi + 1, (n, wl.expert_scale_bytes),
+                           dtype=torch.uint8, device=device, generator=g)
+    return codes, scales
+
+
 def small_workload(hidden: int, inter: int, n_experts: int, k: int, tokens: int,
                    wid: int = 100, **kw) -> Workload:
     """A reduced-size workload with the same value distributions, for parity tests."""

@@ -149,3 +149,19 @@ def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         C.moe_fp4_expert_ffn(torch.zeros(4), A, A, 1, 6, A, 384, 4096, 2880, A, A, 1 << 20, stream=0)
+
+
+def test_residual_helpers_argument_checks(L):
+    assert L.moe_fp4_residual_init(None, A, 1, 64, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_residual_init(A, A, -1, 64, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_residual_init(A, A + 2, 1, 64, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_residual_init(A, A, 0, 64, None) == C.OK
+    f = L.moe_fp4_residual_rmsnorm
+    assert f(A, None, A, 1, 64, 1e-6, None) == C.ERR_INVALID_ARG
+    assert f(A, A, A, 1, 0, 1e-6, None) == C.ERR_INVALID_ARG
+    assert f(A, A, A, 1, 64, -1.0, None) == C.ERR_INVALID_ARG
+    assert f(A + 4, A, A, 1, 64, 1e-6, None) == C.ERR_MISALIGNED
+    assert f(A, A + 2, A, 1, 64, 1e-6, None) == C.ERR_MISALIGNED
+    assert f(A, A, A, 1, 60, 1e-6, None) == C.ERR_BAD_SHAPE
+    assert f(A, A, A, 1, 16384 + 8, 1e-6, None) == C.ERR_BAD_SHAPE
+    assert f(A, A, A, 0, 64, 1e-6, None) == C.OK

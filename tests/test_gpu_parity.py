@@ -253,7 +253,7 @@ def test_moe_forward_matches_route_then_ffn(dev, decode_layer):
     _, D = _mods()
     wl, layer = decode_layer
     wr_bits = S.router_weights(wl, 0)
-    for T, step in ((1, 100), (1, 101), (5, 102), (40, 103)):
+    for T, step in ((1, 100), (1, 101), (5, 102), (40, 103)):  # 40: grouped path
         x_bits = S.activations(wl, 0, step, tokens=T)
         x = D.upload_bf16(x_bits, dev)
         y1, ids1, w1 = layer.forward(x)
@@ -414,11 +414,11 @@ def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
 
 
 def test_auto_path_choice(dev, small_layer):
-    """The automatic choice runs the decode kernels below 16 tokens and the grouped ones
-    from 16 on (read from the library's per-kernel launch counters)."""
+    """The automatic choice runs the decode kernels below 24 tokens and the grouped ones
+    from 24 on (read from the library's per-kernel launch counters)."""
     C, D = _mods()
     wl, layer = small_layer
-    for T, expect in ((15, "gate_up"), (16, "grouped_gate_up")):
+    for T, expect in ((23, "gate_up"), (24, "grouped_gate_up")):
         rng = np.random.default_rng(T)
         ids, w = _random_routing(rng, T, 6, wl.n_experts)
         x_bits = S.activations(wl, 0, 5, tokens=T)
@@ -429,3 +429,63 @@ def test_auto_path_choice(dev, small_layer):
         launched = {n for kind, n in enumerate(C.KERNEL_NAMES) if C.moe_fp4_timing_read(kind)[0]}
         C.moe_fp4_timing_reset()
         assert expect in launched and ("grouped_gate_up" if expect == "gate_up" else "gate_up") not in launched, (T, launched)
+
+
+# ------------------------------------------------------------------------------ layer chain
+
+@pytest.mark.parametrize("H", [4096, 320, 96])
+def test_residual_rmsnorm_matches_oracle(dev, H):
+    """r += y in fp32 (exactly the fp64 sum rounded to fp32) and x = bf16(r / rms): at most
+    one bf16 unit in the last place from the oracle (the rounding of the normalised value
+    can differ where the fp64 quotient lies within an ulp of a rounding boundary)."""
+    C, D = _mods()
+    rng = np.random.default_rng(H)
+    T = 5
+    x0 = O.f64_to_bf16_bits(rng.standard_normal((T, H)))
+    y = O.f64_to_bf16_bits(rng.standard_normal((T, H)) * 3.0)
+    r = torch.empty((T, H), dtype=torch.float32, device=dev)
+    C.moe_fp4_residual_init(D.upload_bf16(x0, dev), r, T, H)
+    xo = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    C.moe_fp4_residual_rmsnorm(r, D.upload_bf16(y, dev), xo, T, H, 1e-6)
+    torch.cuda.synchronize()
+    r_ref, x_ref = O.residual_rmsnorm(O.bf16_to_f64(x0), O.bf16_to_f64(y))
+    assert np.array_equal(r.cpu().numpy(), r_ref.astype(np.float32))
+    xg = O.bf16_to_f64(D.bf16_bits(xo))
+    xr = O.bf16_to_f64(x_ref)
+    ulp = np.abs(xr) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(xg - xr) <= ulp), np.max(np.abs(xg - xr) / ulp)
+    assert np.mean(xg == xr) > 0.99
+
+
+def test_layer_stack_teacher_forced(dev):
+    """Four chained layers at batch 1: every layer's routing (bit-exact), FFN (tolerance)
+    and residual + RMSNorm (within one bf16 ulp) checked against the oracle on the GPU's own
+    input to that layer."""
+    C, D = _mods()
+    base = S.small_workload(512, 384, 16, 4, 1, wid=500)
+    layers = [_layer(base, dev, layer=l) for l in range(4)]
+    H = base.hidden
+    x_bits = S.activations(base, 0, 0)
+    x = D.upload_bf16(x_bits, dev)
+    r = torch.empty((1, H), dtype=torch.float32, device=dev)
+    C.moe_fp4_residual_init(x, r, 1, H)
+    for tok in range(3):
+        for l, layer in enumerate(layers):
+            x_in = D.bf16_bits(x)
+            r_in = r.cpu().numpy().astype(np.float64)
+            y, ids, w = layer.forward_fused(x)
+            xn = torch.empty_like(x)
+            C.moe_fp4_residual_rmsnorm(r, y, xn, 1, H, 1e-6)
+            torch.cuda.synchronize()
+            ids_ref, w_ref, _ = O.route(x_in, S.router_weights(base, l), base.k)
+            check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"token {tok} layer {l}")
+            ref = O.expert_ffn(x_in, ids_ref, w_ref, S.expert_source(base, l), base.n_experts, H,
+                               base.inter)
+            yb = D.bf16_bits(y)
+            check_ffn(yb, ref, f"token {tok} layer {l}")
+            _, x_ref = O.residual_rmsnorm(r_in, O.bf16_to_f64(yb))
+            xg, xr = O.bf16_to_f64(D.bf16_bits(xn)), O.bf16_to_f64(x_ref)
+            assert np.all(np.abs(xg - xr) <= np.abs(xr) * 2.0 ** -7 + 1e-30), (tok, l)
+            x = xn
+        x = D.upload_bf16(S.activations(base, 0, tok + 1), dev)  # next token: fresh input
+        C.moe_fp4_residual_init(x, r, 1, H)
