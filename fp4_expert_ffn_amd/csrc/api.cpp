@@ -6,7 +6,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/moe_fp4.h"
+#include "moe_fp4.h"
 #include "moe_fp4_internal.hpp"
 
 using namespace moe_fp4;

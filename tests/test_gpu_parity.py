@@ -247,9 +247,9 @@ def test_layer_decode_full_size_route_and_ffn(dev, decode_layer):
 
 
 def test_moe_forward_matches_route_then_ffn(dev, decode_layer):
-    """The one-call layer (selection folded into the gate/up kernel) gives bit-identical
-    ids, weights and outputs to moe_fp4_route followed by moe_fp4_expert_ffn, for batch 1
-    and for a batch of 5 tokens; and its ids match the oracle."""
+    """The one-call layer gives bit-identical ids, weights and outputs to moe_fp4_route
+    followed by moe_fp4_expert_ffn, for batch 1, a batch of 5 tokens (decode path) and 40
+    tokens (grouped path); and its ids match the oracle."""
     _, D = _mods()
     wl, layer = decode_layer
     wr_bits = S.router_weights(wl, 0)
