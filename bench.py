@@ -93,6 +93,71 @@ def cpu_baseline(wl, n_tokens: int, first_step: int):
                       f"(route + expert FFN, fp64 NumPy, 1 thread), {dt:.1f} s"}
 
 
+def measure_peaks(torch, C, dev) -> dict:
+    """What this chip sustains, measured with the library's two probe kernels: a streaming
+    read of 4 GiB with the expert kernels' 16-byte non-temporal loads, and a loop of the
+    block-scaled 16x16x128 matrix-core operation with FP4 x FP4 and FP8 x FP4 operands."""
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        C.moe_fp4_debug_stream_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    C.moe_fp4_timing_reset()
+    C.moe_fp4_timing_enable(True)
+    for _ in range(10):
+        C.moe_fp4_debug_stream_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    C.moe_fp4_timing_enable(False)
+    n, ms = C.moe_fp4_timing_read(C.KERNEL_NAMES.index("probe_stream"))
+    out["hbm_stream_read_gbs"] = round(nbytes * n / (ms * 1e-3) / 1e9, 1)
+    del buf
+    n_wg, iters = 1024, 2000  # 4 wavefronts per SIMD on 256 CUs
+    flops = n_wg * 4 * iters * C.PROBE_MFMA_CHAINS * 2.0 * 16 * 16 * 128
+    for fmt, key in ((4, "mfma_fp4xfp4_tflops"), (0, "mfma_fp8xfp4_tflops")):
+        C.moe_fp4_debug_mfma_loop(fmt, n_wg, iters, sink)
+        torch.cuda.synchronize()
+        C.moe_fp4_timing_reset()
+        C.moe_fp4_timing_enable(True)
+        for _ in range(5):
+            C.moe_fp4_debug_mfma_loop(fmt, n_wg, iters, sink)
+        torch.cuda.synchronize()
+        C.moe_fp4_timing_enable(False)
+        n, ms = C.moe_fp4_timing_read(C.KERNEL_NAMES.index("probe_mfma"))
+        out[key] = round(flops * n / (ms * 1e-3) / 1e12, 1)
+    C.moe_fp4_timing_reset()
+    log("measured peaks: " + json.dumps(out))
+    return out
+
+
+def step_percentiles(torch, step, indices) -> dict:
+    """Per-step GPU time (us) of stream-launched steps, each bracketed by its own events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in indices]
+    torch.cuda.synchronize()
+    for (a, b), i in zip(evs, indices):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"p10": round(float(np.percentile(us, 10)), 2), "p50": round(float(np.median(us)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "n": len(us),
+            "how": "stream launches, one event pair per step"}
+
+
+def with_measured_peak(roofline, peaks):
+    if roofline is None or not peaks:
+        return roofline
+    key = {"GB/s": "hbm_stream_read_gbs", "TFLOP/s": "mfma_fp8xfp4_tflops"}[roofline["unit"]]
+    mp = peaks.get(key)
+    if mp:
+        roofline["measured_peak"] = mp
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / mp, 4)
+    return roofline
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +175,8 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak probes (streaming read, matrix-core loop)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="before the steps, run a plain elementwise copy of 256 MiB three times "
                          "(a known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -239,6 +306,11 @@ def main() -> int:
                         "avg_launch_us": round(gu["avg_us"], 3)}
         log("kernels: " + json.dumps(kernels))
 
+    pct = step_percentiles(torch, step, range(W + K, W + 2 * K))
+    log(f"per-step us (stream): {json.dumps(pct)}")
+    peaks = None if args.no_peaks else measure_peaks(torch, C, dev)
+    roofline = with_measured_peak(roofline, peaks)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
@@ -264,7 +336,9 @@ def main() -> int:
         "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
         "hbm_frac_step": round(step_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_step": step_bytes,
+        "step_us": pct,
         "kernels": kernels,
+        "measured_peaks": peaks,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -543,6 +617,11 @@ def run_batched(args) -> int:
                             "avg_launch_us": round(gu["avg_us"], 3)}
         log("kernels: " + json.dumps(kernels))
 
+    pct = step_percentiles(torch, step, range(W + K, W + 2 * K))
+    log(f"per-step us (stream): {json.dumps(pct)}")
+    peaks = None if args.no_peaks else measure_peaks(torch, C, dev)
+    roofline = with_measured_peak(roofline, peaks)
+
     cpu = None
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
@@ -578,7 +657,9 @@ def run_batched(args) -> int:
         "tokens_per_s": round(T * K / elapsed_s, 1),
         "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
         "distinct_experts_per_step": d_avg,
+        "step_us": pct,
         "kernels": kernels,
+        "measured_peaks": peaks,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

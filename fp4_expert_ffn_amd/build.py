@@ -20,7 +20,7 @@ LIB_NAME = "libmoe_fp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["api.cpp", "kernels_pack.hip", "kernels_route.hip", "kernels_ffn.hip",
-           "kernels_batched.hip", "kernels_norm.hip"]
+           "kernels_batched.hip", "kernels_norm.hip", "kernels_probe.hip"]
 
 # Packed-fp32 VALU ops are switched off for the device code: the compiler otherwise forms
 # them from ordinary float code, and this library does not rely on them.
@@ -29,6 +29,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+
+# Per-source extra flags. The matrix-core probe keeps its accumulators in ordinary VGPRs:
+# in the accumulation-register form the compiler rotates independent accumulators through
+# register moves every iteration, which chains the operations and understates the peak.
+EXTRA_FLAGS = {"kernels_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -40,7 +45,7 @@ def hipcc() -> str:
 
 def _compile(src: str, build_dir: str = BUILD_DIR, defines=(), csrc: str = CSRC) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-I", csrc, *[f"-D{d}" for d in defines], "-c",
+    cmd = [hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", csrc, *[f"-D{d}" for d in defines], "-c",
            os.path.join(csrc, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]

@@ -302,6 +302,24 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
                                        matrix, out, s));
 }
 
+int moe_fp4_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned4(sink)) return MOE_FP4_ERR_MISALIGNED;
+  return from_hip(launch_probe_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_debug_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32_t* sink,
+                            void* stream) {
+  static_assert(MOE_FP4_PROBE_MFMA_CHAINS > 0, "chains");
+  if (!sink || (fmt_a != 0 && fmt_a != 4)) return MOE_FP4_ERR_INVALID_ARG;
+  if (n_workgroups < 1 || n_workgroups > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return MOE_FP4_ERR_INVALID_ARG;
+  if (!aligned4(sink)) return MOE_FP4_ERR_MISALIGNED;
+  if (probe_mfma_chains() != MOE_FP4_PROBE_MFMA_CHAINS) return MOE_FP4_ERR_INVALID_ARG;
+  return from_hip(launch_probe_mfma_loop(fmt_a, n_workgroups, iters, sink,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int moe_fp4_timing_enable(int enable) {
   timing().enabled = enable != 0;
   return MOE_FP4_OK;

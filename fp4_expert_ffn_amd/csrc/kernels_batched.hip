@@ -439,6 +439,33 @@ __device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
   cx.sr = (long)row_of(min(tid >> 1, kBlockRows - 1)) * (cx.Kp / kBlock);
 }
 
+// Workgroup -> (row block, column tile). The dispatcher hands workgroups to the eight XCDs
+// in turn (b mod 8) and each XCD has its own L2, so the logical index gives every XCD one
+// contiguous range of the n_blocks x n_tiles items (sized from the actual block count, so
+// the XCDs get equal shares). Inside a range the row blocks run fastest within groups of
+// kColGroup column tiles: the row blocks of one expert, which are consecutive blocks, read
+// the same weight tile close together in time on one XCD (the later reads hit its L2), and
+// each row block's activations are reused by the group's tiles. Returns false for the
+// workgroups past the items (the grid is nb_max x n_tiles rounded up to a multiple of 8).
+constexpr int kXcds = 8;
+constexpr int kColGroup = 4;
+
+__device__ __forceinline__ bool map_block_tile(int b, int nb, int n_tiles, int& blk, int& nt) {
+  const long G = (long)nb * n_tiles;
+  const long per = (G + kXcds - 1) / kXcds;
+  const int j = b / kXcds;
+  if (j >= per) return false;
+  const long L = (long)(b - j * kXcds) * per + j;
+  if (L >= G) return false;
+  const long span = (long)nb * kColGroup;
+  const int cg = (int)(L / span);
+  const int r = (int)(L - cg * span);
+  const int cols = min(kColGroup, n_tiles - cg * kColGroup);
+  blk = r / cols;
+  nt = cg * kColGroup + (r - blk * cols);
+  return true;
+}
+
 // ---------------------------------------------------------------------------------------
 // 3. gate / up / SiLU / h quantisation
 // ---------------------------------------------------------------------------------------
@@ -453,9 +480,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     uint8_t* __restrict__ hshi, uint8_t* __restrict__ hslo, int Ip) {
   __shared__ __align__(16) uint8_t lds[2 * kBlockRows * kAPitch];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
-  const int blk = blockIdx.x / n_tiles;
-  const int nt = blockIdx.x - blk * n_tiles;
-  if (blk >= n_blocks[0]) return;  // workgroup-uniform
+  int blk, nt;
+  if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk, nt)) return;  // workgroup-uniform
   const int e = blk_expert[blk];
   const int row0 = blk_row0[blk];
   const int rows = blk_rows[blk];
@@ -548,9 +574,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     int n_tiles, float* __restrict__ ypair) {
   __shared__ __align__(16) uint8_t lds[2 * kBlockRows * kAPitch];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
-  const int blk = blockIdx.x / n_tiles;
-  const int nt = blockIdx.x - blk * n_tiles;
-  if (blk >= n_blocks[0]) return;  // workgroup-uniform
+  int blk, nt;
+  if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk, nt)) return;  // workgroup-uniform
   const int e = blk_expert[blk];
   const int row0 = blk_row0[blk];
   const int rows = blk_rows[blk];
@@ -706,7 +731,8 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
   if (e != hipSuccess) return e;
 
   const int gu_tiles = (inter + kBN - 1) / kBN;
-  const long gu_grid = (long)B.nb_max * gu_tiles;
+  static_assert(kXcds == 8, "grid rounding below");
+  const long gu_grid = ((long)B.nb_max * gu_tiles + 7) / 8 * 8;  // a multiple of the XCD count
   if (gu_grid > 0x7fffffffL) return hipErrorInvalidValue;
   e = launch_kernel(kKindBatchedGateUp, gemm_gate_up_kernel, dim3((unsigned)gu_grid), dim3(kBThreads), 0,
                     s, ws + B.xhi, ws + B.xlo, ws + B.xshi, ws + B.xslo, B.Hp, perm, bexp, brow0,
@@ -716,7 +742,7 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
   if (e != hipSuccess) return e;
 
   const int dn_tiles = (hidden + kBN - 1) / kBN;
-  const long dn_grid = (long)B.nb_max * dn_tiles;
+  const long dn_grid = ((long)B.nb_max * dn_tiles + 7) / 8 * 8;
   if (dn_grid > 0x7fffffffL) return hipErrorInvalidValue;
   float* ypair = reinterpret_cast<float*>(ws + B.ypair);
   e = launch_kernel(kKindBatchedDown, gemm_down_kernel, dim3((unsigned)dn_grid), dim3(kBThreads), 0, s,

@@ -20,7 +20,8 @@ constexpr int kMaxExpertsTopk = 2048;  // max experts for the top-k selection ke
 enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp = 3,
                   kKindDownCombine = 4, kKindRouteDecode = 5, kKindBatchedSort = 6,
                   kKindBatchedQuant = 7, kKindBatchedGateUp = 8, kKindBatchedDown = 9,
-                  kKindBatchedCombine = 10, kKindNorm = 11 };
+                  kKindBatchedCombine = 10, kKindNorm = 11,
+                  kKindProbeStream = 12, kKindProbeMfma = 13 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -142,6 +143,14 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
 hipError_t launch_residual_init(const uint16_t* x, float* r, int T, int hidden, hipStream_t s);
 hipError_t launch_residual_rmsnorm(float* r, const uint16_t* y, uint16_t* x, int T, int hidden,
                                    float eps, hipStream_t s);
+
+// Measurement kernels: a streaming read of `bytes` bytes, and n_workgroups x 4 wavefronts
+// each issuing iters x probe_mfma_chains() block-scaled 16x16x128 MFMAs (B FP4, A FP4 when
+// fmt_a == 4 else FP8 E4M3).
+hipError_t launch_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32_t* sink,
+                                  hipStream_t s);
+int probe_mfma_chains();
 
 hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
                                 int matrix, float* out, hipStream_t s);

@@ -29,7 +29,8 @@ ERR_HIP = -5
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
 KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
                 "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine",
-                "norm")
+                "norm", "probe_stream", "probe_mfma")
+PROBE_MFMA_CHAINS = 8  # independent block-scaled MFMAs per wavefront per loop iteration
 
 
 class MoeFp4Error(RuntimeError):
@@ -62,6 +63,8 @@ _SIGNATURES = {
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_fp4_debug_stream_read": (_I, [_P, _Z, _P, _P]),
+    "moe_fp4_debug_mfma_loop": (_I, [_I, _I, _I, _P, _P]),
     "moe_fp4_timing_enable": (_I, [_I]),
     "moe_fp4_timing_reset": (_I, []),
     "moe_fp4_timing_read": (_I, [_I, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_double)]),
@@ -221,6 +224,16 @@ def moe_fp4_debug_dequant(packed, n_experts: int, hidden: int, inter: int, exper
                           matrix: int, out, stream=None) -> None:
     _check(lib().moe_fp4_debug_dequant(_ptr(packed), n_experts, hidden, inter, expert, matrix,
                                        _ptr(out), _stream(stream)), "moe_fp4_debug_dequant")
+
+
+def moe_fp4_debug_stream_read(src, nbytes: int, sink, stream=None) -> None:
+    _check(lib().moe_fp4_debug_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "moe_fp4_debug_stream_read")
+
+
+def moe_fp4_debug_mfma_loop(fmt_a: int, n_workgroups: int, iters: int, sink, stream=None) -> None:
+    _check(lib().moe_fp4_debug_mfma_loop(fmt_a, n_workgroups, iters, _ptr(sink), _stream(stream)),
+           "moe_fp4_debug_mfma_loop")
 
 
 def moe_fp4_timing_enable(enable: bool) -> None:

@@ -216,6 +216,26 @@ int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,
 int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int inter, int expert,
                           int matrix, float* out, void* stream);
 
+/* Measurement helper (not on the FFN path): reads `bytes` bytes at src with 16-byte
+ * non-temporal loads, the load form of the expert kernels, over a grid of up to 2048
+ * workgroups; for the measured HBM streaming peak. src: device, 16-byte aligned; bytes a
+ * positive multiple of 16. sink: one device uint32 that the kernel writes only when the
+ * XOR of everything read equals a fixed constant (it keeps the loads; the contents of sink
+ * carry no meaning). Errors: INVALID_ARG (null pointer, bytes 0 or not a multiple of 16),
+ * MISALIGNED, HIP. */
+int moe_fp4_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/* Measurement helper (not on the FFN path): n_workgroups workgroups of four wavefronts,
+ * each wavefront issuing iters x MOE_FP4_PROBE_MFMA_CHAINS independent block-scaled
+ * 16x16x128 matrix-core operations (v_mfma_scale_f32_16x16x128_f8f6f4; 2 x 16 x 16 x 128
+ * flops each) with B in FP4 E2M1 and A in FP4 E2M1 (fmt_a = 4) or FP8 E4M3 (fmt_a = 0),
+ * operands held in registers; for the measured matrix-core peak. sink as above.
+ * Errors: INVALID_ARG (null sink, fmt_a not 0 or 4, n_workgroups or iters outside
+ * [1, 1 << 20]), HIP. */
+#define MOE_FP4_PROBE_MFMA_CHAINS 8
+int moe_fp4_debug_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32_t* sink,
+                            void* stream);
+
 /* ------------------------------------------------------------------------------------
  * Built-in kernel timing, for measurement. When enabled, every kernel the library
  * launches is bracketed by a pair of HIP events on the launch stream (host-side event
@@ -236,7 +256,9 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
 #define MOE_FP4_KERNEL_GROUPED_DOWN 9
 #define MOE_FP4_KERNEL_GROUPED_COMBINE 10
 #define MOE_FP4_KERNEL_NORM 11 /* residual init and residual + RMSNorm */
-#define MOE_FP4_KERNEL_KINDS 12
+#define MOE_FP4_KERNEL_PROBE_STREAM 12 /* moe_fp4_debug_stream_read */
+#define MOE_FP4_KERNEL_PROBE_MFMA 13   /* moe_fp4_debug_mfma_loop */
+#define MOE_FP4_KERNEL_KINDS 14
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

@@ -165,3 +165,22 @@ def test_residual_helpers_argument_checks(L):
     assert f(A, A, A, 1, 60, 1e-6, None) == C.ERR_BAD_SHAPE
     assert f(A, A, A, 1, 16384 + 8, 1e-6, None) == C.ERR_BAD_SHAPE
     assert f(A, A, A, 0, 64, 1e-6, None) == C.OK
+
+
+def test_probe_helpers_argument_checks(L):
+    f = L.moe_fp4_debug_stream_read
+    assert f(None, 1024, A, None) == C.ERR_INVALID_ARG
+    assert f(A, 1024, None, None) == C.ERR_INVALID_ARG
+    assert f(A, 0, A, None) == C.ERR_INVALID_ARG
+    assert f(A, 1000, A, None) == C.ERR_INVALID_ARG
+    assert f(MIS, 1024, A, None) == C.ERR_MISALIGNED
+    assert f(A, 1024, MIS4, None) == C.ERR_MISALIGNED
+    g = L.moe_fp4_debug_mfma_loop
+    assert g(4, 1, 1, None, None) == C.ERR_INVALID_ARG
+    assert g(2, 1, 1, A, None) == C.ERR_INVALID_ARG
+    assert g(4, 0, 1, A, None) == C.ERR_INVALID_ARG
+    assert g(0, 1, 0, A, None) == C.ERR_INVALID_ARG
+    assert g(0, 1, (1 << 20) + 1, A, None) == C.ERR_INVALID_ARG
+    assert g(4, 1, 1, MIS4, None) == C.ERR_MISALIGNED
+    assert C.PROBE_MFMA_CHAINS == 8
+    assert len(C.KERNEL_NAMES) == 14
