@@ -43,27 +43,35 @@ def gate_up_bytes(hidden: int, inter: int) -> int:
     return n // 2 + n // 32
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_layer_hbm_traffic.md")
+TRAFFIC_SUMMARIES = [os.path.join(ROOT, "profiles", "decode_layer_hbm_traffic.md"),
+                     os.path.join(ROOT, "profiles", "grouped_hbm_traffic.md")]
 KERNEL_SOURCES = {"gate_up_kernel": "kernels_ffn.hip", "down_combine_kernel": "kernels_ffn.hip",
-                  "route_decode_kernel": "kernels_route.hip"}
+                  "route_decode_kernel": "kernels_route.hip",
+                  "gemm_gate_up_kernel": "kernels_batched.hip", "gemm_down_kernel": "kernels_batched.hip"}
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the summary is
-    missing or the kernel's source has changed since the counters were taken."""
+def measured_traffic(kernel: str, workload: str = ""):
+    """HBM bytes per launch of `kernel` (on `workload`, for the grouped kernels) from the
+    committed rocprofv3 counter summaries (FETCH_SIZE + WRITE_SIZE, calibrated on a plain
+    copy), or None when there is no entry or the kernel's source has changed since the
+    counters were taken."""
     import hashlib
 
+    key = f"{kernel}@{workload}" if workload else kernel
     try:
-        lines = open(TRAFFIC_SUMMARY).read().splitlines()
         src = os.path.join(ROOT, "fp4_expert_ffn_amd", "csrc", KERNEL_SOURCES[kernel])
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     except (OSError, KeyError):
         return None
-    for line in lines:
-        f = line.split()
-        if len(f) == 5 and f[0] == "traffic_bytes_per_launch" and f[1] == kernel and f[3] == "source":
-            return int(f[2]) if f[4] == digest else None
+    for path in TRAFFIC_SUMMARIES:
+        try:
+            lines = open(path).read().splitlines()
+        except OSError:
+            continue
+        for line in lines:
+            f = line.split()
+            if len(f) == 5 and f[0] == "traffic_bytes_per_launch" and f[1] == key and f[3] == "source":
+                return int(f[2]) if f[4] == digest else None
     return None
 
 
@@ -612,7 +620,8 @@ def run_batched(args) -> int:
                 alg = d_avg * gate_up_bytes(H, I) + T * Hp * 2 * (1 + 1 / 32) + pairs * Ip * 2 * (1 + 1 / 32)
                 achieved = alg / t_s / 1e9
                 roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic("gemm_gate_up_kernel", wl.name),
                             "kernel": "grouped_gate_up", "bytes_per_launch": round(alg),
                             "avg_launch_us": round(gu["avg_us"], 3)}
         log("kernels: " + json.dumps(kernels))
