@@ -409,3 +409,32 @@ def test_mx_scale_exponents_vector_form_matches_scalar_rule():
     for vmax in (448.0, 7.5, 6.0):
         vec = O.mx_scale_exponents(a, vmax)
         assert [O.mx_scale_exponent(float(v), vmax) for v in a] == list(vec)
+
+
+# --------------------------------------------------------------------------- layer chaining
+
+def test_residual_rmsnorm_hand_derived_cases():
+    """Hand-derived values of the residual update and the unit-gain RMSNorm:
+    - a constant row c normalises to c / |c| = 1 (eps = 1e-6 is far below bf16 resolution);
+    - the row pattern [3, 4, 0, 0] has mean square 25 / 4, so RMS 2.5 and normalised values
+      1.2 and 1.6, whose bf16 encodings are 0x3F9A (1.203125) and 0x3FCD (1.6015625);
+    - scaling the residual by 2^10 leaves x unchanged; the residual update is an exact sum."""
+    r = np.zeros((2, 64))
+    y = np.full((2, 64), 5.0)
+    y[1] = -5.0
+    r2, x = O.residual_rmsnorm(r, y)
+    assert np.array_equal(r2, y)
+    assert np.all(x[0] == 0x3F80) and np.all(x[1] == 0xBF80)
+
+    pat = np.tile(np.array([3.0, 4.0, 0.0, 0.0]), 16)[None, :]
+    r2, x = O.residual_rmsnorm(np.zeros_like(pat), pat)
+    assert x.tolist()[0][:4] == [0x3F9A, 0x3FCD, 0, 0]
+    assert np.array_equal(x[0].reshape(16, 4), np.tile(x[0][:4], (16, 1)))
+
+    _, x_big = O.residual_rmsnorm(np.zeros_like(pat), pat * 1024.0)
+    assert np.array_equal(x_big, x)
+
+    a = np.array([[1.5, -2.25, 0.0, 8.0]])
+    b = np.array([[0.25, 2.25, -1.0, 0.5]])
+    r2, _ = O.residual_rmsnorm(a, b)
+    assert r2.tolist() == [[1.75, 0.0, -1.0, 8.5]]
