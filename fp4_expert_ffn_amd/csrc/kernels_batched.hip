@@ -293,15 +293,29 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, uint8_t* lds_s, uint4 
   if (tid < 2 * kBlockRows) *reinterpret_cast<uint32_t*>(lds_s + 4 * tid) = sv;
 }
 
-// A operand (hi or lo) of 16-row subtile m for this lane; halves of K-blocks past K are zero.
+// A operand (hi or lo) of 16-row subtile m for this lane; halves of K-blocks past K are
+// zeroed with the lane masks m0 / m1 (all ones or zero: a select, not a branch, so the
+// LDS reads of one subtile can be scheduled under the previous subtile's MFMAs).
 __device__ __forceinline__ i32x8_t a_operand(const uint8_t* lds, int m, int lane, bool lo,
-                                             bool half0_ok, bool half1_ok) {
+                                             uint32_t m0, uint32_t m1) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint8_t* row = lds + (16 * m + r) * kAPitch + (lo ? 128 : 0);
+  const uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
+  const uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
+  return i32x8_t{(int)(p0.x & m0), (int)(p0.y & m0), (int)(p0.z & m0), (int)(p0.w & m0),
+                 (int)(p1.x & m1), (int)(p1.y & m1), (int)(p1.z & m1), (int)(p1.w & m1)};
+}
+
+// The same with branches (zeroing only when a mask is clear): fewer live registers, which
+// down's budget needs; its LDS reads wait inside the branches.
+__device__ __forceinline__ i32x8_t a_operand_br(const uint8_t* lds, int m, int lane, bool lo,
+                                                uint32_t m0, uint32_t m1) {
   const int r = lane & 15, g = lane >> 4;
   const uint8_t* row = lds + (16 * m + r) * kAPitch + (lo ? 128 : 0);
   uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
   uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-  if (!half0_ok) p0 = make_uint4(0, 0, 0, 0);
-  if (!half1_ok) p1 = make_uint4(0, 0, 0, 0);
+  if (!m0) p0 = make_uint4(0, 0, 0, 0);
+  if (!m1) p1 = make_uint4(0, 0, 0, 0);
   return i32x8_t{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
                  (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
 }
@@ -372,7 +386,11 @@ __device__ __forceinline__ void mfma2(f32x4_t& acc, const i32x8_t& ahi, const i3
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, (int)b.s);
 }
 
-template <int NB>
+// PAIR: the K loop runs two chunks per trip with two B sets used alternately and reloaded
+// in place (gate/up, which has the registers for it; measured 6-9 % faster). Without PAIR
+// one B set rotates (current = next), a register copy that waits for the next set's loads,
+// and the smaller register budget of down keeps it spill-free.
+template <int NB, bool PAIR>
 __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, int rows,
                                             uint8_t* lds, uint8_t* lds_s, Acc<NB>& acc) {
   const int lane = threadIdx.x & 63;
@@ -386,43 +404,68 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   stage_load(cx, 0, d0, d1, d2, d3, sv);
   stage_store(lds, lds_s, d0, d1, d2, d3, sv);
   stage_load(cx, min(1, nch - 1), d0, d1, d2, d3, sv);
-  BSet<NB> bcur = load_bset<NB>(bp, 0, cx.KB);
-  BSet<NB> bnxt = load_bset<NB>(bp, min(1, nch - 1), cx.KB);
+  // two B sets: chunk c uses b0 (PAIR: even chunks) or the rotated pair b0 <- b1
+  BSet<NB> b0 = load_bset<NB>(bp, 0, cx.KB);
+  BSet<NB> b1 = load_bset<NB>(bp, min(1, nch - 1), cx.KB);
   const bool any_on = bp.on0;  // tile 0 of matrix 0 is the wave's first tile
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const uint8_t* A = lds + (c & 1) * kBuf;
-    const uint8_t* AS = lds_s + (c & 1) * kBufS;
-    // A halves of this lane: K-blocks 4 c + 2 h + g / 2; this lane's scale: K-block 4 c + g.
-    // Past K the data is zeroed and the scale forced to 1: padding scale bytes are never
-    // written, and a NaN scale (byte 255) would poison the product even with zero data.
-    const bool h0 = 4 * c + (g >> 1) < cx.KB;
-    const bool h1 = 4 * c + 2 + (g >> 1) < cx.KB;
-    const bool s_ok = 4 * c + g < cx.KB;
-    if (any_on) {
-#pragma unroll
-      for (int m = 0; m < kMSub; ++m) {
-        if (16 * m < rows) {  // wave-uniform
-          const i32x8_t ahi = a_operand(A, m, lane, false, h0, h1);
-          const i32x8_t alo = a_operand(A, m, lane, true, h0, h1);
-          const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;
-          const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;
-          mfma2(acc.a[m][0], ahi, alo, bcur.w0, sw_hi, sw_lo);
-          if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, bcur.w1, sw_hi, sw_lo);
-          if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, bcur.w2, sw_hi, sw_lo);
-          if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, bcur.w3, sw_hi, sw_lo);
-        }
-      }
-    }
-    // chunk c + 1 into the other buffer (last read in iteration c - 1, before its barrier);
-    // then the loads of chunk c + 2 (clamped)
-    stage_store(lds + ((c + 1) & 1) * kBuf, lds_s + ((c + 1) & 1) * kBufS, d0, d1, d2, d3, sv);
-    const int cn = min(c + 2, nch - 1);
-    stage_load(cx, cn, d0, d1, d2, d3, sv);
-    bcur = bnxt;
-    bnxt = load_bset<NB>(bp, cn, cx.KB);
-    __syncthreads();
+  // One chunk C with B set BS: MFMAs on the A buffer of C, then A of C + 1 into the other
+  // buffer (last read in chunk C - 1, before its barrier), the A loads of C + 2, the B loads
+  // of C + 2 into BS (clamped), one barrier. A halves of this lane: K-blocks
+  // 4 C + 2 h + g / 2; its scale: K-block 4 C + g. Past K the data is zeroed and the scale
+  // forced to 1: padding scale bytes are never written, and a NaN scale (byte 255) would
+  // poison the product even with zero data.
+#define MOE_FP4_KSTEP(C, BS)                                                                     \
+  {                                                                                             \
+    const uint8_t* A = lds + ((C) & 1) * kBuf;                                                  \
+    const uint8_t* AS = lds_s + ((C) & 1) * kBufS;                                              \
+    const uint32_t h0 = 4 * (C) + (g >> 1) < cx.KB ? ~0u : 0u;                                  \
+    const uint32_t h1 = 4 * (C) + 2 + (g >> 1) < cx.KB ? ~0u : 0u;                              \
+    const bool s_ok = 4 * (C) + g < cx.KB;                                                      \
+    if (any_on) {                                                                               \
+      _Pragma("unroll") for (int m = 0; m < kMSub; ++m) {                                       \
+        if (16 * m < rows) { /* wave-uniform */                                                 \
+          const i32x8_t ahi = PAIR ? a_operand(A, m, lane, false, h0, h1)                       \
+                                   : a_operand_br(A, m, lane, false, h0, h1);                   \
+          const i32x8_t alo = PAIR ? a_operand(A, m, lane, true, h0, h1)                        \
+                                   : a_operand_br(A, m, lane, true, h0, h1);                    \
+          const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;                         \
+          const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;                     \
+          mfma2(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo);                                    \
+          if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo);              \
+          if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo);              \
+          if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo);              \
+        }                                                                                       \
+      }                                                                                         \
+    }                                                                                           \
+    stage_store(lds + (((C) + 1) & 1) * kBuf, lds_s + (((C) + 1) & 1) * kBufS, d0, d1, d2, d3,  \
+                sv);                                                                            \
+    const int cn = min((C) + 2, nch - 1);                                                       \
+    stage_load(cx, cn, d0, d1, d2, d3, sv);                                                     \
+    if constexpr (PAIR) {                                                                       \
+      /* the A loads go out before the B loads, so the next LDS store waits for A only */       \
+      __builtin_amdgcn_sched_barrier(0);                                                        \
+      BS = load_bset<NB>(bp, cn, cx.KB);                                                        \
+    } else {                                                                                    \
+      b0 = b1;                                                                                  \
+      b1 = load_bset<NB>(bp, cn, cx.KB);                                                        \
+    }                                                                                           \
+    __syncthreads();                                                                            \
   }
+  // the pair loop has no condition inside, so both B sets keep their registers across the
+  // back edge (a conditional second step makes the compiler copy them, which waits for
+  // their loads); an odd last chunk runs after it
+  if constexpr (PAIR) {
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
+      MOE_FP4_KSTEP(c, b0)
+      MOE_FP4_KSTEP(c + 1, b1)
+    }
+    if (c < nch) MOE_FP4_KSTEP(c, b0)
+  } else {
+    for (int c = 0; c < nch; ++c) MOE_FP4_KSTEP(c, b0)
+  }
+#undef MOE_FP4_KSTEP
 }
 
 // Fills the per-thread A row offsets. row_of(i) returns the A row (token or sorted position)
@@ -520,7 +563,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<4>(cx, bp, rows, lds, lds_s, acc);
+  gemm_k_loop<4, true>(cx, bp, rows, lds, lds_s, acc);
 
   // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
@@ -611,7 +654,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   Acc<2> acc;
 #pragma unroll
   for (int m = 0; m < kMSub; ++m) acc.a[m][0] = acc.a[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<2>(cx, bp, rows, lds, lds_s, acc);
+  gemm_k_loop<2, false>(cx, bp, rows, lds, lds_s, acc);
 
 #pragma unroll
   for (int s2 = 0; s2 < kNS; ++s2) {
