@@ -693,8 +693,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     const bool okj = jj < k && ej >= 0 && ej < n_experts;
     int rank = 0;
     for (int i = 0; i < k; ++i) {
-      const int ei = __shfl(ej, i, 64);
-      const uint32_t wi = (uint32_t)__shfl((int)wj, i, 64);
+      const int ei = __builtin_amdgcn_readlane(ej, i);
+      const uint32_t wi = (uint32_t)__builtin_amdgcn_readlane((int)wj, i);
       const bool oki = ei >= 0 && ei < n_experts;
       const bool before = ei < ej || (ei == ej && (wi < wj || (wi == wj && i < jj)));
       rank += (oki && before) ? 1 : 0;

@@ -223,11 +223,11 @@ void gate_up_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ 
 // over the kDCWaves waves; each wave keeps one accumulator for the slot it is on and
 // stores it to LDS when it moves on. The final sum over waves and slots runs in a fixed
 // order, so permuting a token's (id, weight) pairs gives bit-identical output.
-// Load order per thread: its share of the token's k h vectors (natural slot order, so the
-// addresses need no routing data), then the ids, then its first batch of down weights,
-// then the LDS stores. Every load is issued (indices clamped to valid data) and every
-// store is unconditional (surplus words go to a dummy LDS word), so the stores wait for
-// the h loads only. Per-slot expert bases and slot numbers sit in one VGPR per lane and
+// Load order per thread: wave 0 first loads the token's ids and weights; every thread then
+// loads its share of the token's k h vectors (natural slot order, so the addresses need no
+// routing data), then its first batch of down weights, then does the LDS stores. Every
+// load is issued (indices clamped to valid data) and every store is unconditional (surplus
+// words go to a dummy LDS word), so the stores wait for the h loads only. Per-slot expert bases and slot numbers sit in one VGPR per lane and
 // are read with readlane at the wave-uniform slot index.
 // LDS: h of the KT slots (bf16, natural order) then four zero 16-byte words and a dummy.
 // ---------------------------------------------------------------------------------------
@@ -253,7 +253,17 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
   const int hx = I / 8;      // 16-byte words per h vector
   const int hw = KT * hx;    // 16-byte words of the token's k h vectors
 
-  // 1. the token's h vectors into registers (named registers: an array live across the
+  // 1. wave 0: the token's ids and weights (clamped, unconditional loads) go out first, so
+  // the slot table below does not wait behind the h vectors (loads return in order)
+  int ej_raw = 0;
+  uint32_t wj_raw = 0u;
+  if (tid < 64) {  // wave-uniform
+    const int jc = min(tid, KT - 1);
+    ej_raw = ids[(size_t)t * KT + jc];
+    wj_raw = __float_as_uint(wts[(size_t)t * KT + jc]);
+  }
+
+  // 2. the token's h vectors into registers (named registers: an array live across the
   // table code below would be placed in private memory)
   const uint4* hv = reinterpret_cast<const uint4*>(hbuf + (size_t)t * KT * I);
   static_assert(HR >= 1 && HR <= 4, "h rounds");
@@ -262,19 +272,19 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
   if constexpr (HR > 2) hr2 = hv[min(tid + 2 * kDCThreads, hw - 1)];
   if constexpr (HR > 3) hr3 = hv[min(tid + 3 * kDCThreads, hw - 1)];
 
-  // 2. canonical slot order: lane jj < KT of wave 0 ranks slot jj; lane 0 writes the table
+  // 3. canonical slot order: lane jj < KT of wave 0 ranks slot jj; lane 0 writes the table
   // in rank order, entries past the valid slots pointing at expert 0 / slot 0 (used only
   // by clamped loads whose results are discarded)
   if (tid < 64) {
     const int jj = tid;
-    const int ej = (jj < KT) ? ids[(size_t)t * KT + jj] : -1;
-    const uint32_t wj = (jj < KT) ? __float_as_uint(wts[(size_t)t * KT + jj]) : 0u;
+    const int ej = (jj < KT) ? ej_raw : -1;
+    const uint32_t wj = (jj < KT) ? wj_raw : 0u;
     const bool okj = jj < KT && ej >= 0 && ej < n_experts;
     int rank = 0;
 #pragma unroll
-    for (int i = 0; i < KT; ++i) {
-      const int ei = __shfl(ej, i, 64);
-      const uint32_t wi = (uint32_t)__shfl((int)wj, i, 64);
+    for (int i = 0; i < KT; ++i) {  // readlane: a register read, not an LDS round trip
+      const int ei = __builtin_amdgcn_readlane(ej, i);
+      const uint32_t wi = (uint32_t)__builtin_amdgcn_readlane((int)wj, i);
       const bool oki = ei >= 0 && ei < n_experts;
       const bool before = ei < ej || (ei == ej && (wi < wj || (wi == wj && i < jj)));
       rank += (oki && before) ? 1 : 0;
@@ -284,8 +294,8 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
     for (int r = 0; r < KT; ++r) {
       const int sr = __ffsll((long long)__ballot(okj && rank == r)) - 1;  // wave-uniform
       const int src = sr < 0 ? 0 : sr;
-      const int er = __shfl(ej, src, 64);
-      const uint32_t wr = (uint32_t)__shfl((int)wj, src, 64);
+      const int er = __builtin_amdgcn_readlane(ej, src);
+      const uint32_t wr = (uint32_t)__builtin_amdgcn_readlane((int)wj, src);
       if (lane == 0) {
         s_sid[r] = sr < 0 ? 0 : er;
         s_slot[r] = src;
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
     return packed + (((uint64_t)hi << 32) | lo);
   };
 
-  // 3. this wave's first batch of weights. Steps s = p * nch + c (position p, chunk c) are
+  // 4. this wave's first batch of weights. Steps s = p * nch + c (position p, chunk c) are
   // walked with carried (p, c) counters, all wave-uniform. Steps past this wave's range
   // repeat its last step (or step 0 when the token has no valid slot), so every load
   // reads packed data of a real expert.
@@ -340,7 +350,7 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
   };
   load_batch(s_begin, p_first, c_first);
 
-  // 4. h into LDS
+  // 5. h into LDS
   const int dummy = hw + 4;
   {
     const int c0 = tid, c1 = tid + kDCThreads, c2 = tid + 2 * kDCThreads, c3 = tid + 3 * kDCThreads;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(float* _
           (double)rb[it].x * rb[it].x + (double)rb[it].y * rb[it].y +
           (double)rb[it].z * rb[it].z + (double)rb[it].w * rb[it].w;
   }
-  ss = group_sum_f64<64>(ss);
+  ss = wave_sum_f64(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
   double tot = 0.0;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(const uint16_t* _
       }
     }
   }
-  acc = group_sum_f64<64>(acc);
+  acc = wave_sum_f64(acc);
   if (lane == 0) logits[(size_t)t * E + e] = acc;
 }
 
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
   __shared__ double s_logit[kRouteRowsPerWG];
 #pragma unroll
   for (int r = 0; r < kRouteRowsPerWave; ++r) {
-    acc[r] = group_sum_f64<64>(acc[r]);
+    acc[r] = wave_sum_f64(acc[r]);
     if (lane == 0) s_logit[wv * kRouteRowsPerWave + r] = acc[r];
   }
   __syncthreads();

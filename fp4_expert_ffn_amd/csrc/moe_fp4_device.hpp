@@ -55,32 +55,51 @@ __device__ __forceinline__ float fp4_block_dot(const uint4 c, const uint4 a0, co
   return s0 + s1;
 }
 
-// Sum over groups of LPR consecutive lanes (LPR a power of two <= 64); every lane of the
-// group ends with the group sum. All 64 lanes must execute this call.
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// fp64 value moved across lanes by a DPP pattern (both 32-bit halves alike).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-template <int LPR>
-__device__ __forceinline__ double group_sum_f64(double v) {
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// Sum over the 64 lanes of a wavefront (all lanes active); every lane gets the same sum.
+// Pairs of lanes add each other's partial sums: DPP inside 16-lane rows (quad swaps, then
+// the 8- and 16-lane mirrors), then gfx950's lane swaps across rows. Partners add the same
+// two operands (a + b and b + a are equal in IEEE arithmetic), so all lanes hold identical
+// bits, and the pairing is the same on every call.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const auto l32 = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
+  v = __longlong_as_double((long long)(((unsigned long long)(unsigned)h32[0] << 32) | (unsigned)l32[0])) +
+      __longlong_as_double((long long)(((unsigned long long)(unsigned)h32[1] << 32) | (unsigned)l32[1]));
+  const unsigned long long c = (unsigned long long)__double_as_longlong(v);
+  const auto l16 = __builtin_amdgcn_permlane16_swap((unsigned)c, (unsigned)c, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap((unsigned)(c >> 32), (unsigned)(c >> 32), false, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)h16[0] << 32) | (unsigned)l16[0])) +
+         __longlong_as_double((long long)(((unsigned long long)(unsigned)h16[1] << 32) | (unsigned)l16[1]));
 }
 
 // Wave-wide maximum of a uint32 (all 64 lanes active): a DPP butterfly inside each row of
-// 16 lanes, then the four row results through scalar registers. Every lane gets the result.
+// 16 lanes, then two lane swaps across rows. Every lane gets the result.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
+  // every lane now holds its 16-lane row's maximum; gfx950's lane swaps combine the rows
+  // in vector registers (rows 2, 3 against rows 0, 1, then odd against even rows), so the
+  // result reaches every lane without scalar round trips
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max((uint32_t)h[0], (uint32_t)h[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
