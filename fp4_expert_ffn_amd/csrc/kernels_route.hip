@@ -144,9 +144,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
       }
     }
   }
-  // The workgroup's logits go through LDS to wave 0, which stores them all and then
-  // raises the flag with a release: the release orders only the releasing wave's own
-  // stores, so no other wave of the workgroup may store logits.
+  // The workgroup's logits go through LDS to wave 0. It stores them with relaxed
+  // agent-scope atomic stores (written through to the agent-coherent level, so no L2
+  // write-back fence is needed), waits until they are acknowledged, then raises the flag
+  // with a relaxed agent-scope store. Workgroup 0 polls the flags with relaxed loads and
+  // takes one acquire fence before reading the logits (agent-scope atomic loads would each
+  // wait for completion, one after the other).
   __shared__ double s_logit[kRouteRowsPerWG];
 #pragma unroll
   for (int r = 0; r < kRouteRowsPerWave; ++r) {
@@ -156,15 +159,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
   __syncthreads();
   if (wv == 0) {
     const int row = g * kRouteRowsPerWG + lane;
-    if (lane < kRouteRowsPerWG && row < E) logits[row] = s_logit[lane];
-    if (lane == 0) __hip_atomic_store(&sync[1 + g], target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < kRouteRowsPerWG && row < E)
+      __hip_atomic_store(&logits[row], s_logit[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the logit stores are complete
+    if (lane == 0) __hip_atomic_store(&sync[1 + g], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (g != 0) return;
 
   for (int f = tid; f < G; f += kRouteThreads) {
     unsigned n = 0;
-    // relaxed polls (an acquire per poll would invalidate this XCD's L2 each time), one
-    // acquire fence once the flag is seen
     while (__hip_atomic_load(&sync[1 + f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target) {
       __builtin_amdgcn_s_sleep(1);
       if (++n > kSpinLimit) break;

@@ -161,10 +161,18 @@ __device__ __forceinline__ void wave_topk(const V* __restrict__ row, int E, int 
                                           int (&ids)[8], float (&w)[8]) {
   uint64_t key[PER];
   int kid[PER];
+  double lv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) lv[i] = (double)row[min(lane + i * 64, E - 1)];  // clamped
+  // an empty asm that takes each loaded value keeps the loads unconditional (the compiler
+  // would otherwise sink each into the branch of its select, waiting after every one), so
+  // all PER loads are in flight together
+#pragma unroll
+  for (int i = 0; i < PER; ++i) __asm__ volatile("" : "+v"(lv[i]));
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + i * 64;
-    key[i] = (e < E) ? f64_order_key((double)row[e]) : 0ull;  // 0: empty slot
+    key[i] = (e < E) ? f64_order_key(lv[i]) : 0ull;  // 0: empty slot
     kid[i] = (e < E) ? e : 0x7fffffff;
   }
 #pragma unroll
