@@ -180,6 +180,9 @@ def main() -> int:
     ap.add_argument("--api", choices=["fused", "split"], default="fused",
                     help="fused: one moe_fp4_moe_forward call; split: moe_fp4_route then "
                          "moe_fp4_expert_ffn (three kernel launches either way)")
+    ap.add_argument("--stack-route", choices=["fused", "separate"], default="fused",
+                    help="stack16_decode: route each later layer straight from the residual "
+                         "stream (fused) or run residual + RMSNorm as its own launch (separate)")
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
@@ -391,6 +394,7 @@ def run_stack(args) -> int:
     for lay in layers:
         lay._fws = ws  # one workspace for the whole stack (stream-ordered)
     r = torch.empty((1, H), dtype=torch.float32, device=dev)
+    r2 = torch.empty_like(r)
     xa = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
     xb = torch.empty_like(xa)
     ids = torch.empty((1, k), dtype=torch.int32, device=dev)
@@ -400,11 +404,25 @@ def run_stack(args) -> int:
     def step(t: int) -> None:
         x = xs[t:t + 1]
         C.moe_fp4_residual_init(x, r, 1, H)
+        if args.stack_route == "separate":
+            for l, lay in enumerate(layers):
+                lay.forward_fused(x, ids, w, y)
+                xn = xa if l % 2 == 0 else xb
+                C.moe_fp4_residual_rmsnorm(r, y, xn, 1, H, 1e-6)
+                x = xn
+            return
+        # layers after the first route straight from the residual stream: the router kernel
+        # adds the previous layer's y, normalises and routes in one launch
+        rc, rn = r, r2
         for l, lay in enumerate(layers):
-            lay.forward_fused(x, ids, w, y)
+            if l == 0:
+                lay.forward_fused(x, ids, w, y)
+                continue
             xn = xa if l % 2 == 0 else xb
-            C.moe_fp4_residual_rmsnorm(r, y, xn, 1, H, 1e-6)
-            x = xn
+            lay.route_residual(rc, y, rn, xn, 1e-6, ids, w)
+            lay.ffn(xn, ids, w, y)
+            rc, rn = rn, rc
+        C.moe_fp4_residual_rmsnorm(rc, y, xa, 1, H, 1e-6)  # the last layer's residual + norm
 
     for t in range(W):
         step(t)
@@ -463,7 +481,8 @@ def run_stack(args) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": L, "hidden": H, "intermediate": I, "experts": E,
+        "config": {"workload": wl.name, "layers": L, "stack_route": args.stack_route, "hidden": H,
+                   "intermediate": I, "experts": E,
                    "top_k": k, "batch_tokens": 1, "launch": args.mode, "parallelism": "none (1 GPU)"},
         "algorithmic_gbps": round(token_bytes * K / elapsed_s / 1e9, 1),
         "hbm_frac_step": round(token_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),

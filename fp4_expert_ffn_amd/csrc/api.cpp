@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -155,6 +156,41 @@ int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden
                              static_cast<hipStream_t>(stream)));
 }
 
+static bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+int moe_fp4_route_residual(const float* residual_in, const uint16_t* y_prev, float* residual_out,
+                           uint16_t* x_out, float eps, const uint16_t* w_router, int T, int hidden,
+                           int n_experts, int k, int32_t* topk_ids, float* topk_w, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!residual_in || !y_prev || !residual_out || !x_out || !w_router || !topk_ids || !topk_w ||
+      !workspace)
+    return MOE_FP4_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return MOE_FP4_ERR_INVALID_ARG;
+  int st = check_topk_args(T, n_experts, k);
+  if (st != MOE_FP4_OK) return st;
+  if (!valid_dim(hidden)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(residual_in) || !aligned16(y_prev) || !aligned16(residual_out) ||
+      !aligned16(x_out) || !aligned16(w_router) || !aligned4(topk_ids) || !aligned4(topk_w) ||
+      !aligned16(workspace))
+    return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < moe_fp4_route_workspace_bytes(T, n_experts)) return MOE_FP4_ERR_WORKSPACE;
+  const size_t rb = (size_t)T * (size_t)hidden * sizeof(float);
+  if (ranges_overlap(residual_in, rb, residual_out, rb)) return MOE_FP4_ERR_INVALID_ARG;
+  if (T == 0) return MOE_FP4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* sync = static_cast<uint32_t*>(workspace);
+  double* logits = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + kRouteSyncBytes);
+  if (T == 1 && (size_t)route_decode_sync_words(n_experts) * 4 <= kRouteSyncBytes)
+    return from_hip(launch_route_decode_norm(residual_in, y_prev, residual_out, x_out, eps, w_router,
+                                             hidden, n_experts, k, sync, logits, topk_ids, topk_w, s));
+  if (launch_residual_rmsnorm(residual_in, y_prev, residual_out, x_out, T, hidden, eps, s) != hipSuccess)
+    return MOE_FP4_ERR_HIP;
+  return from_hip(route_impl(x_out, w_router, T, hidden, n_experts, k, topk_ids, topk_w, workspace, s));
+}
+
 int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,
                          float* topk_w, void* stream) {
   if (!logits || !topk_ids || !topk_w) return MOE_FP4_ERR_INVALID_ARG;
@@ -279,7 +315,7 @@ int moe_fp4_residual_rmsnorm(float* residual, const uint16_t* y, uint16_t* x_out
   if (hidden % 8 != 0 || hidden > kMaxDim) return MOE_FP4_ERR_BAD_SHAPE;
   if (!aligned16(residual) || !aligned16(y) || !aligned16(x_out)) return MOE_FP4_ERR_MISALIGNED;
   if (T == 0) return MOE_FP4_OK;
-  return from_hip(launch_residual_rmsnorm(residual, y, x_out, T, hidden, eps,
+  return from_hip(launch_residual_rmsnorm(residual, y, residual, x_out, T, hidden, eps,
                                           static_cast<hipStream_t>(stream)));
 }
 

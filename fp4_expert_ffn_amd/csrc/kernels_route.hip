@@ -95,17 +95,53 @@ constexpr int kRouteRowsPerWG = kRouteRowsPerWave * kRouteWaves;
 constexpr int kRouteThreads = kRouteWaves * 64;
 constexpr unsigned kSpinLimit = 1u << 22;
 
-template <int PER>
+// NIT > 0: the router input is computed here from a residual stream: r_out = r_in + y_prev
+// and x = bf16(r_out / rms) (the shared row helpers, so the bits equal the standalone norm
+// kernel's). Every workgroup normalises the row into LDS for its own GEMV (waves 0-3, the
+// helpers' 256 threads) and writes its 1/G slice of r_out and x_out for the later kernels.
+template <int PER, int NIT>
 __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int H, int E, int k,
     uint32_t* __restrict__ sync, double* __restrict__ logits, int32_t* __restrict__ ids,
-    float* __restrict__ w) {
+    float* __restrict__ w, const float* __restrict__ r_in, const uint16_t* __restrict__ y_prev,
+    float* __restrict__ r_out, uint16_t* __restrict__ x_out, float eps) {
   const int G = gridDim.x;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const uint32_t target = sync[0] + 1u;
+
+  extern __shared__ uint4 s_x[];  // NIT > 0: the normalised row, H / 8 words
+  if constexpr (NIT > 0) {
+    __shared__ double npart[kNormRowThreads / 64];
+    float4 ra[NIT], rb[NIT];
+    if (tid < kNormRowThreads) {  // wave-uniform
+      double ss = norm_row_add<NIT>(r_in, y_prev, H, tid, ra, rb);
+      ss = wave_sum_f64(ss);
+      if (lane == 0) npart[wv] = ss;
+    }
+    __syncthreads();
+    if (tid < kNormRowThreads) {
+      const double inv = norm_row_inv(npart, H, eps);
+      const int n8 = H / 8;
+      const int s0 = (int)((long)g * n8 / G), s1 = (int)((long)(g + 1) * n8 / G);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int q = tid + it * kNormRowThreads;  // group of 8 elements
+        if (q < n8) {
+          const uint4 xo = norm_row_pack8(ra[it], rb[it], inv);
+          s_x[q] = xo;
+          if (q >= s0 && q < s1) {
+            *reinterpret_cast<uint4*>(x_out + 8 * q) = xo;
+            *reinterpret_cast<float4*>(r_out + 8 * q) = ra[it];
+            *reinterpret_cast<float4*>(r_out + 8 * q + 4) = rb[it];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   // GEMV, fp64 accumulation of the exact bf16 x bf16 products (same order for every row)
   const int row0 = g * kRouteRowsPerWG + wv * kRouteRowsPerWave;
@@ -120,7 +156,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int c = c0 + u * 64;
-      a[u] = (c < chunks) ? xv[c] : make_uint4(0, 0, 0, 0);
+      if constexpr (NIT > 0)
+        a[u] = (c < chunks) ? s_x[c] : make_uint4(0, 0, 0, 0);
+      else
+        a[u] = (c < chunks) ? xv[c] : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < kRouteRowsPerWave; ++r) {
         const int row = min(row0 + r, E - 1);
@@ -234,14 +273,17 @@ hipError_t launch_topk(const V* logits, int T, int n_experts, int k, int32_t* id
   return launch_kernel(kKindTopk, topk_kernel<V, 32>, grid, block, 0, s, logits, T, n_experts, k, ids, w);
 }
 
-hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden, int n_experts,
+template <int NIT>
+hipError_t route_decode_launch(const uint16_t* x, const uint16_t* wr, int hidden, int n_experts,
                                int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
-                               hipStream_t s) {
+                               const float* r_in, const uint16_t* y_prev, float* r_out,
+                               uint16_t* x_out, float eps, hipStream_t s) {
   const dim3 grid((unsigned)((n_experts + kRouteRowsPerWG - 1) / kRouteRowsPerWG)), block(kRouteThreads);
+  const uint32_t lds = NIT > 0 ? (uint32_t)hidden * 2u : 0u;
   const int per = (n_experts + 63) / 64;
-#define MOE_FP4_ROUTE_LAUNCH(P)                                                                  \
-  return launch_kernel(kKindRouteDecode, route_decode_kernel<P>, grid, block, 0, s, x, wr, hidden, \
-                       n_experts, k, sync, logits, ids, w)
+#define MOE_FP4_ROUTE_LAUNCH(P)                                                                   \
+  return launch_kernel(kKindRouteDecode, route_decode_kernel<P, NIT>, grid, block, lds, s, x, wr,  \
+                       hidden, n_experts, k, sync, logits, ids, w, r_in, y_prev, r_out, x_out, eps)
   if (per <= 2) MOE_FP4_ROUTE_LAUNCH(2);
   if (per <= 4) MOE_FP4_ROUTE_LAUNCH(4);
   if (per <= 6) MOE_FP4_ROUTE_LAUNCH(6);
@@ -249,6 +291,29 @@ hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden
   if (per <= 16) MOE_FP4_ROUTE_LAUNCH(16);
   MOE_FP4_ROUTE_LAUNCH(32);
 #undef MOE_FP4_ROUTE_LAUNCH
+}
+
+hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden, int n_experts,
+                               int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
+                               hipStream_t s) {
+  return route_decode_launch<0>(x, wr, hidden, n_experts, k, sync, logits, ids, w, nullptr,
+                                nullptr, nullptr, nullptr, 0.f, s);
+}
+
+hipError_t launch_route_decode_norm(const float* r_in, const uint16_t* y_prev, float* r_out,
+                                    uint16_t* x_out, float eps, const uint16_t* wr, int hidden,
+                                    int n_experts, int k, uint32_t* sync, double* logits,
+                                    int32_t* ids, float* w, hipStream_t s) {
+  if (hidden % 8 != 0 || hidden > 8 * 8 * kNormRowThreads) return hipErrorInvalidValue;
+  const int nit = (hidden + 8 * kNormRowThreads - 1) / (8 * kNormRowThreads);
+#define MOE_FP4_RN(N)                                                                            \
+  return route_decode_launch<N>(nullptr, wr, hidden, n_experts, k, sync, logits, ids, w, r_in,   \
+                                y_prev, r_out, x_out, eps, s)
+  if (nit <= 1) MOE_FP4_RN(1);
+  if (nit <= 2) MOE_FP4_RN(2);
+  if (nit <= 4) MOE_FP4_RN(4);
+  MOE_FP4_RN(8);
+#undef MOE_FP4_RN
 }
 
 int route_decode_sync_words(int n_experts) {

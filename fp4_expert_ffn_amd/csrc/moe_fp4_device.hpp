@@ -104,6 +104,67 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 
+// Residual add and RMS normalisation of one row of H elements (H % 8 == 0), shared by the
+// standalone norm kernel and the router kernel that normalises its own input, so both give
+// identical bits. Thread t of the kNormRowThreads owns the NIT groups of 8 consecutive
+// elements starting at 8 (t + kNormRowThreads it): norm_row_add loads them (all loads
+// issued before any use), adds y to r in fp32 and returns the thread's fp64 sum of squares
+// in a fixed order; the caller reduces it over the four wavefronts in wave order, and
+// norm_row_pack8 rounds r * inv of one group to bf16.
+constexpr int kNormRowThreads = 256;
+
+template <int NIT>
+__device__ __forceinline__ double norm_row_add(const float* __restrict__ r, const uint16_t* __restrict__ y,
+                                               int H, int t, float4 (&ra)[NIT], float4 (&rb)[NIT]) {
+  uint4 yv[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i0 = 8 * (t + it * kNormRowThreads);
+    ra[it] = rb[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    yv[it] = make_uint4(0, 0, 0, 0);
+    if (i0 < H) {
+      ra[it] = *reinterpret_cast<const float4*>(r + i0);
+      rb[it] = *reinterpret_cast<const float4*>(r + i0 + 4);
+      yv[it] = *reinterpret_cast<const uint4*>(y + i0);
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    ra[it].x += bf16_bits_to_f32(yv[it].x & 0xffffu);
+    ra[it].y += bf16_bits_to_f32(yv[it].x >> 16);
+    ra[it].z += bf16_bits_to_f32(yv[it].y & 0xffffu);
+    ra[it].w += bf16_bits_to_f32(yv[it].y >> 16);
+    rb[it].x += bf16_bits_to_f32(yv[it].z & 0xffffu);
+    rb[it].y += bf16_bits_to_f32(yv[it].z >> 16);
+    rb[it].z += bf16_bits_to_f32(yv[it].w & 0xffffu);
+    rb[it].w += bf16_bits_to_f32(yv[it].w >> 16);
+    ss += (double)ra[it].x * ra[it].x + (double)ra[it].y * ra[it].y +
+          (double)ra[it].z * ra[it].z + (double)ra[it].w * ra[it].w +
+          (double)rb[it].x * rb[it].x + (double)rb[it].y * rb[it].y +
+          (double)rb[it].z * rb[it].z + (double)rb[it].w * rb[it].w;
+  }
+  return ss;
+}
+
+__device__ __forceinline__ uint4 norm_row_pack8(const float4& a, const float4& b, double inv) {
+  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = (uint32_t)f32_to_bf16_rne((float)((double)f[2 * q] * inv)) |
+           ((uint32_t)f32_to_bf16_rne((float)((double)f[2 * q + 1] * inv)) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// inv = 1 / sqrt(mean of squares + eps) from the four wavefronts' partial sums, in order.
+__device__ __forceinline__ double norm_row_inv(const double* part, int H, float eps) {
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kNormRowThreads / 64; ++w) tot += part[w];
+  return 1.0 / sqrt(tot / H + (double)eps);
+}
+
 // Order-preserving map of an fp64 value to uint64 (larger value -> larger key; -0 and +0
 // map to the same key). NaN is not ordered meaningfully.
 __device__ __forceinline__ uint64_t f64_order_key(double v) {

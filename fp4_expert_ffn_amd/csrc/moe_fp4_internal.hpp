@@ -103,6 +103,12 @@ hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden
                                int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
                                hipStream_t s);
 int route_decode_sync_words(int n_experts);
+// The same with the router input computed in the kernel from a residual stream (one token):
+// r_out = r_in + y_prev, x_out = bf16(r_out / rms) with the standalone norm kernel's bits.
+hipError_t launch_route_decode_norm(const float* r_in, const uint16_t* y_prev, float* r_out,
+                                    uint16_t* x_out, float eps, const uint16_t* wr, int hidden,
+                                    int n_experts, int k, uint32_t* sync, double* logits,
+                                    int32_t* ids, float* w, hipStream_t s);
 
 hipError_t launch_topk_f64(const double* logits, int T, int n_experts, int k, int32_t* ids,
                            float* w, hipStream_t s);
@@ -141,8 +147,8 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
 
 // Layer chaining helpers (multi-layer decode harness).
 hipError_t launch_residual_init(const uint16_t* x, float* r, int T, int hidden, hipStream_t s);
-hipError_t launch_residual_rmsnorm(float* r, const uint16_t* y, uint16_t* x, int T, int hidden,
-                                   float eps, hipStream_t s);
+hipError_t launch_residual_rmsnorm(const float* r_in, const uint16_t* y, float* r_out, uint16_t* x,
+                                   int T, int hidden, float eps, hipStream_t s);
 
 // Measurement kernels: a streaming read of `bytes` bytes, and n_workgroups x 4 wavefronts
 // each issuing iters x probe_mfma_chains() block-scaled 16x16x128 MFMAs (B FP4, A FP4 when

@@ -86,6 +86,21 @@ class MoeFp4Layer:
                         stream=stream)
         return ids, w
 
+    def route_residual(self, r_in: torch.Tensor, y_prev: torch.Tensor, r_out: torch.Tensor,
+                       x_out: torch.Tensor, eps: float = 1e-6, ids: Optional[torch.Tensor] = None,
+                       w: Optional[torch.Tensor] = None, stream=None):
+        """moe_fp4_route_residual: r_out = r_in + y_prev, x_out = RMSNorm(r_out), then route
+        x_out (one launch at batch 1)."""
+        T = r_in.shape[0]
+        if ids is None:
+            ids = torch.empty((T, self.k), dtype=torch.int32, device=self.device)
+        if w is None:
+            w = torch.empty((T, self.k), dtype=torch.float32, device=self.device)
+        ws = self._route_workspace(T)
+        C.moe_fp4_route_residual(r_in, y_prev, r_out, x_out, eps, self.w_router, T, self.hidden,
+                                 self.n_experts, self.k, ids, w, ws, stream=stream)
+        return ids, w
+
     def route_logits(self, logits: torch.Tensor, stream=None):
         T = logits.shape[0]
         ids = torch.empty((T, self.k), dtype=torch.int32, device=self.device)

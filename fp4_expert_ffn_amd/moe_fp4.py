@@ -59,6 +59,8 @@ _SIGNATURES = {
     "moe_fp4_expert_ffn_ex": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _I, _P]),
     "moe_fp4_residual_init": (_I, [_P, _P, _I, _I, _P]),
     "moe_fp4_residual_rmsnorm": (_I, [_P, _P, _P, _I, _I, ctypes.c_float, _P]),
+    "moe_fp4_route_residual": (_I, [_P, _P, _P, _P, ctypes.c_float, _P, _I, _I, _I, _I, _P, _P, _P,
+                                    _Z, _P]),
     "moe_fp4_moe_forward_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
@@ -187,6 +189,16 @@ def moe_fp4_residual_rmsnorm(residual, y, x_out, T: int, hidden: int, eps: float
                              stream=None) -> None:
     _check(lib().moe_fp4_residual_rmsnorm(_ptr(residual), _ptr(y), _ptr(x_out), T, hidden, eps,
                                           _stream(stream)), "moe_fp4_residual_rmsnorm")
+
+
+def moe_fp4_route_residual(residual_in, y_prev, residual_out, x_out, eps: float, w_router, T: int,
+                           hidden: int, n_experts: int, k: int, topk_ids, topk_w, workspace,
+                           stream=None) -> None:
+    _check(lib().moe_fp4_route_residual(_ptr(residual_in), _ptr(y_prev), _ptr(residual_out),
+                                        _ptr(x_out), eps, _ptr(w_router), T, hidden, n_experts, k,
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)), "moe_fp4_route_residual")
 
 
 def moe_fp4_expert_ffn_ex(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: int,

@@ -200,6 +200,23 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
  * alignment. Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, HIP.
  * ------------------------------------------------------------------------------------ */
 int moe_fp4_residual_init(const uint16_t* x, float* residual, int T, int hidden, void* stream);
+
+/* The next layer's routing straight from the residual stream, for chained layers:
+ * residual_out = residual_in + y_prev (fp32 add), x_out = bf16_rne(residual_out /
+ * sqrt(mean(residual_out^2) + eps)) (the same bits as moe_fp4_residual_rmsnorm), then the
+ * top-k routing of x_out exactly as moe_fp4_route. At T == 1 this is one launch: every
+ * workgroup of the router kernel normalises the row itself, so the separate norm launch of
+ * a decode step goes away ([A100-FP4], section 然后又发现每 token 启动 2000 次内核: per-token
+ * launches cost more than their math). residual_in, residual_out [T x hidden] fp32 must not
+ * overlap; y_prev, x_out [T x hidden] bf16; eps >= 0 and finite; the workspace as for
+ * moe_fp4_route (its first 4 KB carry the synchronisation words between calls). hidden % 32
+ * == 0 and <= 16384; 16-byte alignment except topk_ids / topk_w (4).
+ * Errors: INVALID_ARG (null, eps, overlap, T / k / n_experts as moe_fp4_route), BAD_SHAPE,
+ * MISALIGNED, WORKSPACE, HIP. */
+int moe_fp4_route_residual(const float* residual_in, const uint16_t* y_prev, float* residual_out,
+                           uint16_t* x_out, float eps, const uint16_t* w_router, int T, int hidden,
+                           int n_experts, int k, int32_t* topk_ids, float* topk_w, void* workspace,
+                           size_t workspace_bytes, void* stream);
 int moe_fp4_residual_rmsnorm(float* residual, const uint16_t* y, uint16_t* x_out, int T,
                              int hidden, float eps, void* stream);
 

@@ -184,3 +184,27 @@ def test_probe_helpers_argument_checks(L):
     assert g(4, 1, 1, MIS4, None) == C.ERR_MISALIGNED
     assert C.PROBE_MFMA_CHAINS == 8
     assert len(C.KERNEL_NAMES) == 14
+
+
+def test_route_residual_argument_checks(L):
+    f = L.moe_fp4_route_residual
+    B = 0x20000  # a second aligned fake address, far from A
+    big = 1 << 20
+    args = lambda **kw: dict(dict(ri=A, y=A, ro=B, xo=A, eps=1e-6, wr=A, T=1, H=64, E=8, k=2,
+                                  ids=A, w=A, ws=A, wsb=big), **kw)
+    def call(**kw):
+        a = args(**kw)
+        return f(a["ri"], a["y"], a["ro"], a["xo"], a["eps"], a["wr"], a["T"], a["H"], a["E"],
+                 a["k"], a["ids"], a["w"], a["ws"], a["wsb"], None)
+    assert call(T=0) == C.OK
+    assert call(ri=None) == C.ERR_INVALID_ARG
+    assert call(y=None) == C.ERR_INVALID_ARG
+    assert call(eps=-1.0) == C.ERR_INVALID_ARG
+    assert call(eps=float("nan")) == C.ERR_INVALID_ARG
+    assert call(ro=A) == C.ERR_INVALID_ARG  # residual_in and residual_out overlap (checked before any launch)
+    assert call(ro=A + 64 * 4 - 16, T=1) == C.ERR_INVALID_ARG
+    assert call(k=9) == C.ERR_INVALID_ARG
+    assert call(H=100) == C.ERR_BAD_SHAPE
+    assert call(ri=MIS) == C.ERR_MISALIGNED
+    assert call(ids=MIS4) == C.ERR_MISALIGNED
+    assert call(wsb=16) == C.ERR_WORKSPACE

@@ -457,6 +457,34 @@ def test_residual_rmsnorm_matches_oracle(dev, H):
     assert np.mean(xg == xr) > 0.99
 
 
+@pytest.mark.parametrize("H,E,k,T", [(4096, 384, 6, 1), (320, 24, 4, 1), (96, 8, 2, 1),
+                                     (16384, 16, 6, 1), (4096, 384, 6, 3)])
+def test_route_residual_matches_norm_then_route(dev, H, E, k, T):
+    """moe_fp4_route_residual (one launch at T = 1) gives bit-identical residual, normalised
+    input, ids and weights to moe_fp4_residual_rmsnorm followed by moe_fp4_route."""
+    C, D = _mods()
+    rng = np.random.default_rng(H + E + T)
+    base = S.small_workload(H, 64, E, k, T, wid=600 + H % 97)
+    wr = D.upload_bf16(S.router_weights(base, 0), dev)
+    layer = D.MoeFp4Layer(torch.empty(16, dtype=torch.uint8, device=dev), E, H, 64, k, wr)
+    for rep in range(3):  # repeated calls reuse the workspace's synchronisation words
+        r0 = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(dev)
+        y = D.upload_bf16(O.f64_to_bf16_bits(rng.standard_normal((T, H)) * 2.0), dev)
+        r_fused = torch.empty_like(r0)
+        x_fused = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ids1, w1 = layer.route_residual(r0, y, r_fused, x_fused, 1e-6)
+        r_ref = r0.clone()
+        x_ref = torch.empty_like(x_fused)
+        C.moe_fp4_residual_rmsnorm(r_ref, y, x_ref, T, H, 1e-6)
+        ids2, w2 = layer.route(x_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(r_fused, r_ref), (H, E, T, rep)
+        assert torch.equal(x_fused.view(torch.int16), x_ref.view(torch.int16)), (H, E, T, rep)
+        assert torch.equal(ids1, ids2) and torch.equal(w1, w2), (H, E, T, rep)
+        ids_o, w_o, _ = O.route(D.bf16_bits(x_ref), S.router_weights(base, 0), k)
+        check_route(ids1.cpu().numpy(), w1.cpu().numpy(), ids_o, w_o, f"route_residual H{H} T{T}")
+
+
 def test_layer_stack_teacher_forced(dev):
     """Four chained layers at batch 1: every layer's routing (bit-exact), FFN (tolerance)
     and residual + RMSNorm (within one bf16 ulp) checked against the oracle on the GPU's own
