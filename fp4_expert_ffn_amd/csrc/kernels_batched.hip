@@ -33,6 +33,16 @@
 #include "moe_fp4_device.hpp"
 #include "moe_fp4_internal.hpp"
 
+// B sets of the grouped gate/up K loop (2 or 3: how many chunks ahead its B words load) and
+// its A staging depth (1, or 2 with 2 B sets: chunks between an A load and its LDS store).
+// Measured at 8192 and 32768 tokens: 3 sets 1-2 % ahead of 2; A depth 2 no faster than 1.
+#ifndef MOE_FP4_GU_BSETS
+#define MOE_FP4_GU_BSETS 3
+#endif
+#ifndef MOE_FP4_GU_ADEPTH
+#define MOE_FP4_GU_ADEPTH 1
+#endif
+
 namespace moe_fp4 {
 
 namespace {
@@ -386,27 +396,35 @@ __device__ __forceinline__ void mfma2(f32x4_t& acc, const i32x8_t& ahi, const i3
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, (int)b.s);
 }
 
-// PAIR: the K loop runs two chunks per trip with two B sets used alternately and reloaded
-// in place (gate/up, which has the registers for it; measured 6-9 % faster). Without PAIR
+// BSETS 2 or 3: the K loop runs BSETS chunks per trip with BSETS B sets used in turn and
+// reloaded in place, BSETS chunks ahead (gate/up, which has the registers for it). BSETS 1:
 // one B set rotates (current = next), a register copy that waits for the next set's loads,
-// and the smaller register budget of down keeps it spill-free.
-template <int NB, bool PAIR>
+// two chunks ahead; the smaller register budget of down keeps it spill-free.
+// ADEPTH 2 (with BSETS 2): the A staging loads run two chunks ahead of their LDS store, in
+// two register sets used on alternate chunks (no copies between them).
+template <int NB, int BSETS, int ADEPTH = 1>
 __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, int rows,
                                             uint8_t* lds, uint8_t* lds_s, Acc<NB>& acc) {
+  static_assert(ADEPTH == 1 || (ADEPTH == 2 && BSETS == 2), "A depth 2 runs with two B sets");
+  constexpr bool PAIR = BSETS > 1;
+  static_assert(BSETS >= 1 && BSETS <= 3, "B sets");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int r = lane & 15;
   const int nch = (cx.KB + 3) / 4;
   constexpr int kBuf = kBlockRows * kAPitch;
   constexpr int kBufS = kBlockRows * 8;
-  uint4 d0, d1, d2, d3;
-  uint32_t sv;
+  uint4 d0, d1, d2, d3, e0, e1, e2, e3;
+  uint32_t sv, se;
   stage_load(cx, 0, d0, d1, d2, d3, sv);
   stage_store(lds, lds_s, d0, d1, d2, d3, sv);
   stage_load(cx, min(1, nch - 1), d0, d1, d2, d3, sv);
-  // two B sets: chunk c uses b0 (PAIR: even chunks) or the rotated pair b0 <- b1
+  if constexpr (ADEPTH == 2) stage_load(cx, min(2, nch - 1), e0, e1, e2, e3, se);
+  // B sets: chunk c uses b[c % BSETS] (BSETS > 1) or the rotated pair b0 <- b1
   BSet<NB> b0 = load_bset<NB>(bp, 0, cx.KB);
   BSet<NB> b1 = load_bset<NB>(bp, min(1, nch - 1), cx.KB);
+  BSet<NB> b2 = b1;
+  if constexpr (BSETS == 3) b2 = load_bset<NB>(bp, min(2, nch - 1), cx.KB);
   const bool any_on = bp.on0;  // tile 0 of matrix 0 is the wave's first tile
   __syncthreads();
   // One chunk C with B set BS: MFMAs on the A buffer of C, then A of C + 1 into the other
@@ -415,7 +433,7 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   // 4 C + 2 h + g / 2; its scale: K-block 4 C + g. Past K the data is zeroed and the scale
   // forced to 1: padding scale bytes are never written, and a NaN scale (byte 255) would
   // poison the product even with zero data.
-#define MOE_FP4_KSTEP(C, BS)                                                                     \
+#define MOE_FP4_KSTEP(C, BS, X0, X1, X2, X3, XS)                                                 \
   {                                                                                             \
     const uint8_t* A = lds + ((C) & 1) * kBuf;                                                  \
     const uint8_t* AS = lds_s + ((C) & 1) * kBufS;                                              \
@@ -438,14 +456,14 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
         }                                                                                       \
       }                                                                                         \
     }                                                                                           \
-    stage_store(lds + (((C) + 1) & 1) * kBuf, lds_s + (((C) + 1) & 1) * kBufS, d0, d1, d2, d3,  \
-                sv);                                                                            \
+    stage_store(lds + (((C) + 1) & 1) * kBuf, lds_s + (((C) + 1) & 1) * kBufS, X0, X1, X2, X3,  \
+                XS);                                                                            \
     const int cn = min((C) + 2, nch - 1);                                                       \
-    stage_load(cx, cn, d0, d1, d2, d3, sv);                                                     \
+    stage_load(cx, min((C) + 1 + ADEPTH, nch - 1), X0, X1, X2, X3, XS);                         \
     if constexpr (PAIR) {                                                                       \
       /* the A loads go out before the B loads, so the next LDS store waits for A only */       \
       __builtin_amdgcn_sched_barrier(0);                                                        \
-      BS = load_bset<NB>(bp, cn, cx.KB);                                                        \
+      BS = load_bset<NB>(bp, min((C) + BSETS, nch - 1), cx.KB);                                 \
     } else {                                                                                    \
       b0 = b1;                                                                                  \
       b1 = load_bset<NB>(bp, cn, cx.KB);                                                        \
@@ -455,16 +473,33 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   // the pair loop has no condition inside, so both B sets keep their registers across the
   // back edge (a conditional second step makes the compiler copy them, which waits for
   // their loads); an odd last chunk runs after it
-  if constexpr (PAIR) {
+  if constexpr (BSETS == 3) {
+    int c = 0;
+    for (; c + 2 < nch; c += 3) {
+      MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
+      MOE_FP4_KSTEP(c + 1, b1, d0, d1, d2, d3, sv)
+      MOE_FP4_KSTEP(c + 2, b2, d0, d1, d2, d3, sv)
+    }
+    if (c < nch) MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
+    if (c + 1 < nch) MOE_FP4_KSTEP(c + 1, b1, d0, d1, d2, d3, sv)
+  } else if constexpr (BSETS == 2 && ADEPTH == 2) {
     int c = 0;
     for (; c + 1 < nch; c += 2) {
-      MOE_FP4_KSTEP(c, b0)
-      MOE_FP4_KSTEP(c + 1, b1)
+      MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
+      MOE_FP4_KSTEP(c + 1, b1, e0, e1, e2, e3, se)
     }
-    if (c < nch) MOE_FP4_KSTEP(c, b0)
+    if (c < nch) MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
+  } else if constexpr (BSETS == 2) {
+    int c = 0;
+    for (; c + 1 < nch; c += 2) {
+      MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
+      MOE_FP4_KSTEP(c + 1, b1, d0, d1, d2, d3, sv)
+    }
+    if (c < nch) MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
   } else {
-    for (int c = 0; c < nch; ++c) MOE_FP4_KSTEP(c, b0)
+    for (int c = 0; c < nch; ++c) MOE_FP4_KSTEP(c, b0, d0, d1, d2, d3, sv)
   }
+
 #undef MOE_FP4_KSTEP
 }
 
@@ -563,7 +598,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<4, true>(cx, bp, rows, lds, lds_s, acc);
+  gemm_k_loop<4, MOE_FP4_GU_BSETS, MOE_FP4_GU_ADEPTH>(cx, bp, rows, lds, lds_s, acc);
 
   // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
@@ -654,7 +689,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   Acc<2> acc;
 #pragma unroll
   for (int m = 0; m < kMSub; ++m) acc.a[m][0] = acc.a[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<2, false>(cx, bp, rows, lds, lds_s, acc);
+  gemm_k_loop<2, 1>(cx, bp, rows, lds, lds_s, acc);
 
 #pragma unroll
   for (int s2 = 0; s2 < kNS; ++s2) {
