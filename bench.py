@@ -44,10 +44,12 @@ def gate_up_bytes(hidden: int, inter: int) -> int:
 
 
 TRAFFIC_SUMMARIES = [os.path.join(ROOT, "profiles", "decode_layer_hbm_traffic.md"),
-                     os.path.join(ROOT, "profiles", "grouped_hbm_traffic.md")]
+                     os.path.join(ROOT, "profiles", "grouped_hbm_traffic.md"),
+                     os.path.join(ROOT, "profiles", "small_m_kernel_trace_and_traffic.md")]
 KERNEL_SOURCES = {"gate_up_kernel": "kernels_ffn.hip", "down_combine_kernel": "kernels_ffn.hip",
                   "route_decode_kernel": "kernels_route.hip",
-                  "gemm_gate_up_kernel": "kernels_batched.hip", "gemm_down_kernel": "kernels_batched.hip"}
+                  "gemm_gate_up_kernel": "kernels_batched.hip", "gemm_down_kernel": "kernels_batched.hip",
+                  "gate_up_multi_kernel": "kernels_small_m.hip"}
 
 
 def measured_traffic(kernel: str, workload: str = ""):
@@ -171,9 +173,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default="layer_decode_h4096_i2880_e384",
                     choices=["layer_decode_h4096_i2880_e384", "batched64_zipf", "prefill8192_uniform",
-                             "prefill32768_uniform", "stack16_decode", "expert_h256_i128"],
+                             "prefill32768_uniform", "stack16_decode", "expert_h256_i128",
+                             "mtp4_correlated", "streams8_uniform"],
                     help="the batch-1 decode layer (default, the headline line), or one of the "
-                         "batched shapes run through the grouped GEMM path")
+                         "multi-token shapes (small-M path below 24 tokens, grouped GEMM path "
+                         "from 24 on)")
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", choices=["graph", "stream"], default="graph")
@@ -539,9 +543,10 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 (the f8f6f4 MFMA runs at this 
 
 
 def run_batched(args) -> int:
-    """A batched step: top-k of the step's router logits (drawn directly, as the workload
-    defines them) then moe_fp4_expert_ffn, which takes the grouped GEMM path. Fresh logits
-    every step, so the experts read and their token counts change from step to step."""
+    """A multi-token step: top-k of the step's router logits (drawn directly, as the workload
+    defines them) then moe_fp4_expert_ffn, which takes the small-M path below 24 tokens and
+    the grouped GEMM path from 24 on. Fresh logits every step, so the experts read and their
+    token counts change from step to step."""
     import torch
 
     from fp4_expert_ffn_amd import device as D
@@ -626,6 +631,17 @@ def run_batched(args) -> int:
                 kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n}
         C.moe_fp4_timing_reset()
         gu = kernels.get("grouped_gate_up")
+        sg = kernels.get("small_m_gate_up")
+        if sg:
+            # algorithmic bytes: each distinct expert's gate and up once, x read, h written
+            t_s = sg["avg_us"] * 1e-6
+            alg = d_avg * gate_up_bytes(H, I) + T * H * 2 + pairs * I * 2
+            achieved = alg / t_s / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("gate_up_multi_kernel", wl.name),
+                        "kernel": "small_m_gate_up", "bytes_per_launch": round(alg),
+                        "avg_launch_us": round(sg["avg_us"], 3)}
         if gu:
             t_s = gu["avg_us"] * 1e-6
             if wl.tokens >= 32768:  # enough tokens per expert for a matrix-core bound
@@ -647,6 +663,13 @@ def run_batched(args) -> int:
 
     pct = step_percentiles(torch, step, range(W + K, W + 2 * K))
     log(f"per-step us (stream): {json.dumps(pct)}")
+    decode_pct = None
+    if T < 24:  # the one-pair-at-a-time decode kernels on the same steps, for comparison
+        def step_decode(i: int) -> None:
+            C.moe_fp4_route_logits(lgs[i], T, E, k, ids, w)
+            layer.ffn(xs[i % 2], ids, w, y, path=1)
+        decode_pct = step_percentiles(torch, step_decode, range(W + K, W + 2 * K))
+        log(f"per-step us with the decode path (stream): {json.dumps(decode_pct)}")
     peaks = None if args.no_peaks else measure_peaks(torch, C, dev)
     roofline = with_measured_peak(roofline, peaks)
 
@@ -656,7 +679,7 @@ def run_batched(args) -> int:
 
         from oracle import moe_oracle as O
 
-        n_tok = min(args.cpu_tokens, 8)
+        n_tok = min(args.cpu_tokens, 8, T)
         lg = S.router_logits(wl, 0, W).astype(np.float64)[:n_tok]
         x_bits = S.activations(wl, 0, W % 2)[:n_tok]
         with threadpool_limits(limits=1):
@@ -667,10 +690,11 @@ def run_batched(args) -> int:
         cpu = {"value": n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": f"{n_tok} tokens of one step (top-k + expert FFN, fp64 NumPy, 1 thread), {dt:.1f} s"}
 
+    small = T < 24
     out = {
-        "metric": "batched FP4 TFLOP/s",
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
+        "metric": "multi-token decode tokens/s" if small else "batched FP4 TFLOP/s",
+        "value": round(T * K / elapsed_s, 1) if small else round(tflops, 2),
+        "unit": "tokens/s" if small else "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
@@ -678,11 +702,13 @@ def run_batched(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8(hi+lo) x fp4",
+        "dtype": "bf16 x fp4" if small else "fp8(hi+lo) x fp4",
         "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
                    "tokens": T, "routing": wl.routing, "launch": args.mode, "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(T * K / elapsed_s, 1),
+        "tflops": round(tflops, 2),
+        "decode_path_step_us": decode_pct,
         "algorithmic_gbps": round(step_bytes * K / elapsed_s / 1e9, 1),
         "distinct_experts_per_step": d_avg,
         "step_us": pct,

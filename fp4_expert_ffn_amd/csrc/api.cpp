@@ -212,7 +212,7 @@ size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inte
   // decode path: h for every (token, slot) pair, bf16; grouped path: see batched_layout
   const size_t decode = align256((size_t)T * (size_t)k * (size_t)inter * 2);
   const size_t grouped = batched_layout(T, k, n_experts, hidden, inter).bytes;
-  return std::max(decode, grouped);
+  return std::max(std::max(decode, grouped), small_m_workspace_bytes(T, k, hidden, inter));
 }
 
 static bool lds_fits(int k, int inter) { return (size_t)k * (size_t)inter * 2 <= (size_t)kMaxLdsH; }
@@ -224,6 +224,9 @@ static hipError_t ffn_impl(const uint16_t* x, const int32_t* topk_ids, const flo
   if (path == MOE_FP4_PATH_GROUPED)
     return launch_batched_ffn(x, topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, y,
                               workspace, s);
+  if (path == MOE_FP4_PATH_SMALL_M)
+    return launch_small_m_ffn(x, topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, workspace,
+                              y, s);
   uint16_t* hbuf = static_cast<uint16_t*>(workspace);
   hipError_t e = launch_gate_up(x, topk_ids, T, k, pk, n_experts, hidden, inter, hbuf, s);
   if (e != hipSuccess) return e;
@@ -231,15 +234,25 @@ static hipError_t ffn_impl(const uint16_t* x, const int32_t* topk_ids, const flo
 }
 
 // Resolves MOE_FP4_PATH_AUTO and checks the shape limits of the chosen path.
-static int choose_path(int path, int T, int k, int n_experts, int inter) {
+static bool small_m_fits(int T, int k, int hidden, int inter) {
+  return T >= 2 && (long)T * k <= 256 && small_m_rows(T, hidden, inter) >= 2;
+}
+
+static int choose_path(int path, int T, int k, int n_experts, int hidden, int inter) {
   if (path == MOE_FP4_PATH_AUTO) {
-    path = (T >= kGroupedMinTokens && n_experts <= kMaxExpertsTopk) ? MOE_FP4_PATH_GROUPED
-                                                                    : MOE_FP4_PATH_DECODE;
+    if (T >= kGroupedMinTokens && n_experts <= kMaxExpertsTopk)
+      path = MOE_FP4_PATH_GROUPED;
+    else if (small_m_fits(T, k, hidden, inter))
+      path = MOE_FP4_PATH_SMALL_M;
+    else
+      path = MOE_FP4_PATH_DECODE;
     if (path == MOE_FP4_PATH_DECODE && !lds_fits(k, inter) && n_experts <= kMaxExpertsTopk)
       path = MOE_FP4_PATH_GROUPED;
   }
   if (path == MOE_FP4_PATH_DECODE) return lds_fits(k, inter) ? path : MOE_FP4_ERR_BAD_SHAPE;
   if (path == MOE_FP4_PATH_GROUPED) return n_experts <= kMaxExpertsTopk ? path : MOE_FP4_ERR_BAD_SHAPE;
+  if (path == MOE_FP4_PATH_SMALL_M)
+    return (T == 0 || small_m_fits(T, k, hidden, inter)) ? path : MOE_FP4_ERR_BAD_SHAPE;
   return MOE_FP4_ERR_INVALID_ARG;
 }
 
@@ -250,7 +263,7 @@ int moe_fp4_expert_ffn_ex(const uint16_t* x, const int32_t* topk_ids, const floa
   if (!x || !topk_ids || !topk_w || !packed || !y || !workspace) return MOE_FP4_ERR_INVALID_ARG;
   if (T < 0 || n_experts <= 0 || k < 1 || k > kMaxK || k > n_experts) return MOE_FP4_ERR_INVALID_ARG;
   if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
-  const int chosen = choose_path(path, T, k, n_experts, inter);
+  const int chosen = choose_path(path, T, k, n_experts, hidden, inter);
   if (chosen < 0) return chosen;
   if (!aligned16(x) || !aligned4(topk_ids) || !aligned4(topk_w) || !aligned16(packed) ||
       !aligned16(y) || !aligned16(workspace))
@@ -286,7 +299,7 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
   int st = check_topk_args(T, n_experts, k);
   if (st != MOE_FP4_OK) return st;
   if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
-  const int chosen = choose_path(MOE_FP4_PATH_AUTO, T, k, n_experts, inter);
+  const int chosen = choose_path(MOE_FP4_PATH_AUTO, T, k, n_experts, hidden, inter);
   if (chosen < 0) return chosen;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(packed) || !aligned4(topk_ids) ||
       !aligned4(topk_w) || !aligned16(y) || !aligned16(workspace))

@@ -711,39 +711,72 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
 }
 
 // ---------------------------------------------------------------------------------------
-// 5. combine: one workgroup per token
+// 5. combine: workgroup = one token x kCombineCols columns, four consecutive columns per
+// thread. Every thread ranks the token's slots itself (the ids and weights are the same
+// for the whole workgroup), so the k row loads are issued together, before the ranks are
+// known, and summed afterwards in canonical order: ascending expert id, then weight bits,
+// then slot; invalid ids dropped.
 // ---------------------------------------------------------------------------------------
+constexpr int kCombineCols = 4 * 256;
+
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ ids,
                                                       const float* __restrict__ wts, int k,
-                                                      int n_experts, int H,
+                                                      int n_experts, int H, int col_blocks,
                                                       const float* __restrict__ ypair,
                                                       uint16_t* __restrict__ y) {
-  __shared__ int s_slot[kMaxK], s_nv;
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int jj = tid;
-    const int ej = (jj < k) ? ids[(size_t)t * k + jj] : -1;
-    const uint32_t wj = (jj < k) ? __float_as_uint(wts[(size_t)t * k + jj]) : 0u;
-    const bool okj = jj < k && ej >= 0 && ej < n_experts;
-    int rank = 0;
-    for (int i = 0; i < k; ++i) {
-      const int ei = __builtin_amdgcn_readlane(ej, i);
-      const uint32_t wi = (uint32_t)__builtin_amdgcn_readlane((int)wj, i);
-      const bool oki = ei >= 0 && ei < n_experts;
-      const bool before = ei < ej || (ei == ej && (wi < wj || (wi == wj && i < jj)));
-      rank += (oki && before) ? 1 : 0;
-    }
-    const int nvl = __popcll(__ballot(okj));  // every lane of the wave votes
-    if (okj) s_slot[rank] = jj;
-    if (jj == 0) s_nv = nvl;
+  const int t = blockIdx.x / col_blocks;
+  const int n0 = (blockIdx.x - t * col_blocks) * kCombineCols + 4 * threadIdx.x;
+  const bool col_ok = n0 < H;
+  // lane j < k of every wave: slot j's id, weight bits and rank among the valid slots
+  const int lane = threadIdx.x & 63;
+  const int jl = min(lane, k - 1);
+  const int e_l = ids[(size_t)t * k + jl];
+  const uint32_t w_l = __float_as_uint(wts[(size_t)t * k + jl]);
+  // the k row loads, issued before the ranks are known; unconditional, at clamped slots
+  // and columns (rows of invalid slots are loaded but never summed)
+  const int nc = min(n0, H - 4);
+  float vx[kMaxK], vy[kMaxK], vz[kMaxK], vw[kMaxK];  // one array per component
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    const float4 r = *reinterpret_cast<const float4*>(ypair + ((size_t)t * k + min(j, k - 1)) * H + nc);
+    vx[j] = r.x;
+    vy[j] = r.y;
+    vz[j] = r.z;
+    vw[j] = r.w;
   }
-  __syncthreads();
-  const int nv = s_nv;
-  for (int n = tid; n < H; n += 256) {
-    float acc = 0.f;
-    for (int p = 0; p < nv; ++p) acc += ypair[((size_t)t * k + s_slot[p]) * H + n];
-    y[(size_t)t * H + n] = f32_to_bf16_rne(acc);
+  // one wait for all the loads above; keeps the row loads here rather than in the sum
+  int e_r = e_l;
+  uint32_t w_r = w_l;
+  asm volatile("" : "+v"(e_r), "+v"(w_r));
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) asm volatile("" : "+v"(vx[j]), "+v"(vy[j]), "+v"(vz[j]), "+v"(vw[j]));
+
+  const bool ok_l = lane < k && e_r >= 0 && e_r < n_experts;
+  const unsigned long long okm = __ballot(ok_l);  // every lane votes
+  int rank = 0;
+  for (int i = 0; i < k; ++i) {
+    const int ei = __builtin_amdgcn_readlane(e_r, i);
+    const uint32_t wi = (uint32_t)__builtin_amdgcn_readlane((int)w_r, i);
+    const bool before = ei < e_r || (ei == e_r && (wi < w_r || (wi == w_r && i < lane)));
+    rank += (((okm >> i) & 1ull) && before) ? 1 : 0;
+  }
+  // order: the slot of rank p in bits 4p..4p+3
+  uint32_t order = 0;
+  for (int j = 0; j < k; ++j)
+    if ((okm >> j) & 1ull) order |= (uint32_t)j << (4 * __builtin_amdgcn_readlane(rank, j));
+  const int nv = __popcll(okm);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < nv; ++p) {
+    const int j = (int)((order >> (4 * p)) & 15u);
+    acc.x += vx[j];
+    acc.y += vy[j];
+    acc.z += vz[j];
+    acc.w += vw[j];
+  }
+  if (col_ok) {
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(y + (size_t)t * H + n0) = make_uint2(lo, hi);
   }
 }
 
@@ -829,8 +862,16 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
                     dn_tiles, ypair);
   if (e != hipSuccess) return e;
 
-  return launch_kernel(kKindBatchedCombine, combine_kernel, dim3((unsigned)T), dim3(256), 0, s, ids,
-                       w, k, n_experts, hidden, ypair, y);
+  return launch_combine_pairs(ids, w, T, k, n_experts, hidden, ypair, y, s);
+}
+
+hipError_t launch_combine_pairs(const int32_t* ids, const float* w, int T, int k, int n_experts,
+                                int hidden, const float* ypair, uint16_t* y, hipStream_t s) {
+  const int col_blocks = (hidden + kCombineCols - 1) / kCombineCols;
+  const long grid = (long)T * col_blocks;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  return launch_kernel(kKindBatchedCombine, combine_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                       ids, w, k, n_experts, hidden, col_blocks, ypair, y);
 }
 
 }  // namespace moe_fp4

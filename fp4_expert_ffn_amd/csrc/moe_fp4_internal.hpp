@@ -21,7 +21,8 @@ enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp
                   kKindDownCombine = 4, kKindRouteDecode = 5, kKindBatchedSort = 6,
                   kKindBatchedQuant = 7, kKindBatchedGateUp = 8, kKindBatchedDown = 9,
                   kKindBatchedCombine = 10, kKindNorm = 11,
-                  kKindProbeStream = 12, kKindProbeMfma = 13 };
+                  kKindProbeStream = 12, kKindProbeMfma = 13, kKindSmallGateUp = 14,
+                  kKindSmallDown = 15 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -149,6 +150,19 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
 hipError_t launch_residual_init(const uint16_t* x, float* r, int T, int hidden, hipStream_t s);
 hipError_t launch_residual_rmsnorm(const float* r_in, const uint16_t* y, float* r_out, uint16_t* x,
                                    int T, int hidden, float eps, hipStream_t s);
+
+// Small-M FFN (a few tokens; pairs that chose one expert share its weight stream): gate/up
+// and down per group of up to small_m_rows(...) pairs, then the fixed-order combine.
+// Workspace: small_m_workspace_bytes(...). T * k <= 256.
+int small_m_rows(int T, int hidden, int inter);
+size_t small_m_workspace_bytes(int T, int k, int hidden, int inter);
+hipError_t launch_small_m_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
+                              const uint8_t* packed, int n_experts, int hidden, int inter,
+                              void* workspace, uint16_t* y, hipStream_t s);
+// The grouped path's combine: y[t] = sum over t's valid slots, in canonical order, of the
+// pair rows ypair [T*k x hidden] fp32 (already weighted), rounded to bf16.
+hipError_t launch_combine_pairs(const int32_t* ids, const float* w, int T, int k, int n_experts,
+                                int hidden, const float* ypair, uint16_t* y, hipStream_t s);
 
 // Measurement kernels: a streaming read of `bytes` bytes, and n_workgroups x 4 wavefronts
 // each issuing iters x probe_mfma_chains() block-scaled 16x16x128 MFMAs (B FP4, A FP4 when

@@ -29,7 +29,7 @@ ERR_HIP = -5
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
 KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
                 "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine",
-                "norm", "probe_stream", "probe_mfma")
+                "norm", "probe_stream", "probe_mfma", "small_m_gate_up", "small_m_down")
 PROBE_MFMA_CHAINS = 8  # independent block-scaled MFMAs per wavefront per loop iteration
 
 
@@ -177,7 +177,7 @@ def moe_fp4_expert_ffn(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: i
                                     workspace_bytes, _stream(stream)), "moe_fp4_expert_ffn")
 
 
-PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
+PATH_AUTO, PATH_DECODE, PATH_GROUPED, PATH_SMALL_M = 0, 1, 2, 3
 
 
 def moe_fp4_residual_init(x, residual, T: int, hidden: int, stream=None) -> None:

@@ -152,14 +152,25 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
  *    h enter the matrix cores as two-term MXFP8 (E4M3 hi + lo, one ue8m0 scale per 32
  *    elements each), accumulation is fp32, each pair's weighted output is combined per token
  *    in canonical slot order (five launches; needs n_experts <= 2048).
- *  MOE_FP4_PATH_AUTO: GROUPED from 24 tokens on, DECODE below (the measured crossover on
- *    the 384-expert layer with uniform routing lies between 16 and 24 tokens).
+ *  MOE_FP4_PATH_SMALL_M: for a few tokens per call (several draft tokens of one sequence,
+ *    a few streams): the pairs that chose the same expert share one read of its weights in
+ *    groups of up to G pairs (the tokens of a group are rows of one matrix-core tile), h is
+ *    bit-identical to DECODE's, each pair's weighted output is combined per token in
+ *    canonical slot order (three launches). G is the largest power of two <= min(T, 8)
+ *    with G * max(hidden, inter) <= 16384 (the group's bf16 rows fit in 32 KB of LDS);
+ *    needs 2 <= T, T * k <= 256 and G >= 2 (max(hidden, inter) <= 8192).
+ *  MOE_FP4_PATH_AUTO: GROUPED from 24 tokens on; SMALL_M from 2 to 23 tokens where its
+ *    limits hold; DECODE otherwise (one token, or a shape SMALL_M refuses). Measured on the
+ *    384-expert layer: SMALL_M is faster than DECODE at every T >= 2, with uniform and with
+ *    correlated routing; GROUPED overtakes SMALL_M between 12 and 24 tokens when the tokens
+ *    share most experts, and not below 42 tokens with uniform routing.
  * moe_fp4_expert_ffn is this call with MOE_FP4_PATH_AUTO. The workspace size covers every
  * path. Errors: as moe_fp4_expert_ffn; an unknown path is INVALID_ARG, a shape the chosen
  * path cannot take is BAD_SHAPE. */
 #define MOE_FP4_PATH_AUTO 0
 #define MOE_FP4_PATH_DECODE 1
 #define MOE_FP4_PATH_GROUPED 2
+#define MOE_FP4_PATH_SMALL_M 3
 int moe_fp4_expert_ffn_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                           int k, const void* packed, int n_experts, int hidden, int inter,
                           uint16_t* y, void* workspace, size_t workspace_bytes, int path,
@@ -275,7 +286,9 @@ int moe_fp4_debug_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32_t* si
 #define MOE_FP4_KERNEL_NORM 11 /* residual init and residual + RMSNorm */
 #define MOE_FP4_KERNEL_PROBE_STREAM 12 /* moe_fp4_debug_stream_read */
 #define MOE_FP4_KERNEL_PROBE_MFMA 13   /* moe_fp4_debug_mfma_loop */
-#define MOE_FP4_KERNEL_KINDS 14
+#define MOE_FP4_KERNEL_SMALL_M_GATE_UP 14
+#define MOE_FP4_KERNEL_SMALL_M_DOWN 15
+#define MOE_FP4_KERNEL_KINDS 16
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

@@ -36,8 +36,9 @@ class Workload:
     k: int
     tokens: int              # tokens per step
     layers: int = 1
-    routing: str = "router"  # "router" (x -> W_r GEMV), "zipf", "uniform", "fixed"
+    routing: str = "router"  # "router" (x -> W_r GEMV), "zipf", "uniform", "correlated", "fixed"
     zipf_s: float = 1.1
+    corr: float = 0.9        # "correlated": logit correlation between the tokens of a step
     scale_lo: int = 120      # ue8m0 scale bytes drawn uniformly from [scale_lo, scale_hi]
     scale_hi: int = 130
     router_std: float = 0.02
@@ -70,6 +71,14 @@ WORKLOADS = {
     # 8192 tokens, uniform router logits.
     "prefill8192_uniform": Workload("prefill8192_uniform", 5, 4096, 2880, 384, 6, 8192,
                                     routing="uniform", note="8192 tokens, U(0,1) logits"),
+    # Several draft tokens of one sequence per step (multi-token prediction with three
+    # draft tokens): the tokens' logits share a per-step component, correlation 0.9
+    # (two tokens share about 2.4 of their 6 experts; about 14 distinct experts per step).
+    "mtp4_correlated": Workload("mtp4_correlated", 7, 4096, 2880, 384, 6, 4, routing="correlated",
+                                note="4 tokens per step, logits correlated 0.9 across the step"),
+    # Eight independent streams decoded together.
+    "streams8_uniform": Workload("streams8_uniform", 8, 4096, 2880, 384, 6, 8, routing="uniform",
+                                 note="8 tokens per step, U(0,1) logits"),
     # Supplementary compute-bound shape.
     "prefill32768_uniform": Workload("prefill32768_uniform", 6, 4096, 2880, 384, 6, 32768,
                                      routing="uniform", note="32768 tokens, U(0,1) logits"),
@@ -127,11 +136,18 @@ def router_logits(wl: Workload, layer: int, step: int, tokens: Optional[int] = N
              r = 1..E and pi a seeded permutation fixed per layer; the top-k of these is a
              draw of k experts without replacement with probabilities p.
     uniform: logits i.i.d. U(0, 1), so the top-k is a uniform k-subset.
+    correlated: logits[t, e] = c g[e] + sqrt(1 - c^2) z[t, e] with g (one draw per step) and
+             z i.i.d. N(0, 1), c = corr: each token's top-k is uniform over the experts, and
+             the tokens of a step share experts more often the larger c is.
     """
     t = wl.tokens if tokens is None else tokens
     rng = rng_for(root, wl.wid, layer, step, T_LOGITS)
     if wl.routing == "uniform":
         return rng.random((t, wl.n_experts), dtype=np.float32)
+    if wl.routing == "correlated":
+        g = rng.standard_normal(wl.n_experts)
+        z = rng.standard_normal((t, wl.n_experts))
+        return (wl.corr * g[None, :] + np.sqrt(1.0 - wl.corr * wl.corr) * z).astype(np.float32)
     if wl.routing == "zipf":
         perm = rng_for(root, wl.wid, layer, 0, T_PERM).permutation(wl.n_experts)
         ranks = np.arange(1, wl.n_experts + 1, dtype=np.float64)

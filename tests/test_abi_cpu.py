@@ -183,7 +183,7 @@ def test_probe_helpers_argument_checks(L):
     assert g(0, 1, (1 << 20) + 1, A, None) == C.ERR_INVALID_ARG
     assert g(4, 1, 1, MIS4, None) == C.ERR_MISALIGNED
     assert C.PROBE_MFMA_CHAINS == 8
-    assert len(C.KERNEL_NAMES) == 14
+    assert len(C.KERNEL_NAMES) == 16
 
 
 def test_route_residual_argument_checks(L):

@@ -48,12 +48,23 @@ def _random_routing(rng, T, k, E, distinct=True):
     return ids, w
 
 
-DECODE, GROUPED = 1, 2  # moe_fp4_expert_ffn_ex paths
-PATHS = pytest.mark.parametrize("path", [DECODE, GROUPED], ids=["decode", "grouped"])
+DECODE, GROUPED, SMALL_M = 1, 2, 3  # moe_fp4_expert_ffn_ex paths
+PATHS = pytest.mark.parametrize("path", [DECODE, GROUPED, SMALL_M], ids=["decode", "grouped", "small_m"])
 
 
 def _run_ffn(layer, x_bits, ids, w, dev, path=None):
     _, D = _mods()
+    T, k = ids.shape
+    if path == SMALL_M and (T < 2 or T * k > 256):
+        pytest.skip("the small-M path takes 2 <= T and T * k <= 256")
+    if path == SMALL_M and max(layer.hidden, layer.inter) > 8192:
+        # groups of two bf16 rows no longer fit the path's 32 KB of LDS: refused, not run
+        C, _ = _mods()
+        with pytest.raises(C.MoeFp4Error) as err:
+            layer.ffn(D.upload_bf16(x_bits, dev), torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev), path=path)
+        assert err.value.status == C.ERR_BAD_SHAPE
+        pytest.skip("max(hidden, inter) > 8192: the small-M path refuses the shape")
     x = D.upload_bf16(x_bits, dev)
     ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev)
     w_d = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev)
@@ -394,7 +405,7 @@ def test_slot_permutation_is_bit_identical(dev, small_layer, path):
     assert np.array_equal(y0[tp], y2)
 
 
-@pytest.mark.parametrize("path", [None, DECODE, GROUPED], ids=["auto", "decode", "grouped"])
+@pytest.mark.parametrize("path", [None, DECODE, GROUPED, SMALL_M], ids=["auto", "decode", "grouped", "small_m"])
 @pytest.mark.parametrize("T", [1, 17, 64, 65, 300, 1024])
 def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
     """Same input five times: bit-identical outputs and no NaN/Inf, at token counts on both
@@ -413,12 +424,33 @@ def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
     check_ffn(outs[0][sample], ref, f"T={T} path {path}")
 
 
+@pytest.mark.parametrize("E,k,T", [(3, 2, 24), (4, 2, 16), (16, 6, 8)])
+def test_small_m_shared_experts(dev, E, k, T):
+    """Many pairs per expert: groups larger than the tile's 8 rows split into several groups
+    (E 3, T 24: about 16 pairs per expert), and every token choosing the same experts (the
+    MTP-like case, one group per expert). Checked against the oracle and the decode path."""
+    wl = S.small_workload(320, 160, E, k, T, wid=700 + E)
+    layer = _layer(wl, dev)
+    rng = np.random.default_rng(E * 100 + T)
+    ids, w = _random_routing(rng, T, k, E)
+    x_bits = S.activations(wl, 0, 0)
+    for label, idv in (("random", ids), ("shared", np.tile(ids[:1], (T, 1)))):
+        y_s = _run_ffn(layer, x_bits, idv, w, dev, SMALL_M)
+        y_d = _run_ffn(layer, x_bits, idv, w, dev, DECODE)
+        ref = O.expert_ffn(x_bits, idv, w, S.expert_source(wl), E, wl.hidden, wl.inter)
+        check_ffn(y_s, ref, f"small_m {label} E{E} k{k} T{T}")
+        check_ffn(y_d, ref, f"decode {label} E{E} k{k} T{T}")
+
+
 def test_auto_path_choice(dev, small_layer):
-    """The automatic choice runs the decode kernels below 24 tokens and the grouped ones
-    from 24 on (read from the library's per-kernel launch counters)."""
+    """The automatic choice runs the decode kernels for one token, the small-M ones from 2
+    to 23 tokens and the grouped ones from 24 on (read from the library's per-kernel launch
+    counters)."""
     C, D = _mods()
     wl, layer = small_layer
-    for T, expect in ((23, "gate_up"), (24, "grouped_gate_up")):
+    names = ("gate_up", "small_m_gate_up", "grouped_gate_up")
+    for T, expect in ((1, "gate_up"), (2, "small_m_gate_up"), (23, "small_m_gate_up"),
+                      (24, "grouped_gate_up")):
         rng = np.random.default_rng(T)
         ids, w = _random_routing(rng, T, 6, wl.n_experts)
         x_bits = S.activations(wl, 0, 5, tokens=T)
@@ -428,7 +460,7 @@ def test_auto_path_choice(dev, small_layer):
         C.moe_fp4_timing_enable(False)
         launched = {n for kind, n in enumerate(C.KERNEL_NAMES) if C.moe_fp4_timing_read(kind)[0]}
         C.moe_fp4_timing_reset()
-        assert expect in launched and ("grouped_gate_up" if expect == "gate_up" else "gate_up") not in launched, (T, launched)
+        assert expect in launched and not (set(names) - {expect}) & launched, (T, launched)
 
 
 # ------------------------------------------------------------------------------ layer chain
