@@ -187,6 +187,9 @@ def main() -> int:
     ap.add_argument("--stack-route", choices=["fused", "separate"], default="fused",
                     help="stack16_decode: route each later layer straight from the residual "
                          "stream (fused) or run residual + RMSNorm as its own launch (separate)")
+    ap.add_argument("--act-terms", type=int, choices=[1, 2], default=2,
+                    help="grouped-path workloads: activations as two MXFP8 terms (default, meets "
+                         "the output tolerance) or one (the opt-in FP8-activation path)")
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
@@ -570,10 +573,12 @@ def run_batched(args) -> int:
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     layer._workspace(T, k)
+    fp8 = args.act_terms == 1 and T >= 24
+    path = C.PATH_GROUPED_FP8 if fp8 else None  # None: the automatic choice
 
     def step(i: int) -> None:
         C.moe_fp4_route_logits(lgs[i], T, E, k, ids, w)
-        layer.ffn(xs[i % 2], ids, w, y)
+        layer.ffn(xs[i % 2], ids, w, y, path=path)
 
     for i in range(W):
         step(i)
@@ -652,11 +657,13 @@ def run_batched(args) -> int:
                             "flops_per_launch": pairs * 4.0 * H * I, "avg_launch_us": round(gu["avg_us"], 3)}
             else:
                 Hp, Ip = (H + 127) // 128 * 128, (I + 127) // 128 * 128
-                alg = d_avg * gate_up_bytes(H, I) + T * Hp * 2 * (1 + 1 / 32) + pairs * Ip * 2 * (1 + 1 / 32)
+                nterm = 1 if fp8 else 2  # MXFP8 terms of x and h
+                alg = (d_avg * gate_up_bytes(H, I) + T * Hp * nterm * (1 + 1 / 32)
+                       + pairs * Ip * nterm * (1 + 1 / 32))
                 achieved = alg / t_s / 1e9
                 roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("gemm_gate_up_kernel", wl.name),
+                            "traffic": None if fp8 else measured_traffic("gemm_gate_up_kernel", wl.name),
                             "kernel": "grouped_gate_up", "bytes_per_launch": round(alg),
                             "avg_launch_us": round(gu["avg_us"], 3)}
         log("kernels: " + json.dumps(kernels))
@@ -702,10 +709,11 @@ def run_batched(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 x fp4" if small else "fp8(hi+lo) x fp4",
+        "dtype": "bf16 x fp4" if small else ("fp8 x fp4" if fp8 else "fp8(hi+lo) x fp4"),
         "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
-                   "tokens": T, "routing": wl.routing, "launch": args.mode, "parallelism": "none (1 GPU)"},
+                   "tokens": T, "routing": wl.routing, "launch": args.mode, "parallelism": "none (1 GPU)",
+                   "activations": "bf16" if small else ("MXFP8 one term" if fp8 else "MXFP8 hi + lo")},
         "tokens_per_s": round(T * K / elapsed_s, 1),
         "tflops": round(tflops, 2),
         "decode_path_step_us": decode_pct,

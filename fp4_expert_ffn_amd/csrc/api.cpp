@@ -221,9 +221,9 @@ static bool lds_fits(int k, int inter) { return (size_t)k * (size_t)inter * 2 <=
 static hipError_t ffn_impl(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                            int k, const uint8_t* pk, int n_experts, int hidden, int inter,
                            uint16_t* y, void* workspace, int path, hipStream_t s) {
-  if (path == MOE_FP4_PATH_GROUPED)
+  if (path == MOE_FP4_PATH_GROUPED || path == MOE_FP4_PATH_GROUPED_FP8)
     return launch_batched_ffn(x, topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, y,
-                              workspace, s);
+                              workspace, path == MOE_FP4_PATH_GROUPED ? 2 : 1, s);
   if (path == MOE_FP4_PATH_SMALL_M)
     return launch_small_m_ffn(x, topk_ids, topk_w, T, k, pk, n_experts, hidden, inter, workspace,
                               y, s);
@@ -250,7 +250,8 @@ static int choose_path(int path, int T, int k, int n_experts, int hidden, int in
       path = MOE_FP4_PATH_GROUPED;
   }
   if (path == MOE_FP4_PATH_DECODE) return lds_fits(k, inter) ? path : MOE_FP4_ERR_BAD_SHAPE;
-  if (path == MOE_FP4_PATH_GROUPED) return n_experts <= kMaxExpertsTopk ? path : MOE_FP4_ERR_BAD_SHAPE;
+  if (path == MOE_FP4_PATH_GROUPED || path == MOE_FP4_PATH_GROUPED_FP8)
+    return n_experts <= kMaxExpertsTopk ? path : MOE_FP4_ERR_BAD_SHAPE;
   if (path == MOE_FP4_PATH_SMALL_M)
     return (T == 0 || small_m_fits(T, k, hidden, inter)) ? path : MOE_FP4_ERR_BAD_SHAPE;
   return MOE_FP4_ERR_INVALID_ARG;

@@ -10,7 +10,10 @@
 // 2. quant_x_kernel: x -> two-term MXFP8 (E4M3) hi + lo with one ue8m0 scale per 32 elements
 //    each. The pair reproduces bf16 inputs to about 2^-8 of the block maximum; one FP8 term
 //    alone does not meet the output tolerance. The scale exponent is the smallest X with
-//    max|v| <= 448 * 2^X, so no element overflows the E4M3 range.
+//    max|v| <= 448 * 2^X, so no element overflows the E4M3 range. The opt-in single-term
+//    mode (TERMS = 1) keeps only hi: DeepSeek's own FP8 activation numerics with ue8m0
+//    scales ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug), half the activation bytes
+//    and half the matrix-core work.
 // 3. gemm_gate_up_kernel: per (M-block, 128 rows of I): g and u for 128 rows of gate and up,
 //    h = silu(g) * u, quantised in the epilogue to MXFP8 hi + lo (blocks of 32 along I).
 // 4. gemm_down_kernel: per (M-block, 128 rows of H): y_e = W_down h, times the pair's router
@@ -87,7 +90,8 @@ __device__ __forceinline__ int mx_exponent(float a) {
 }
 
 // v[0..31] (fp32) -> hi, lo E4M3 bytes (16-byte words h0,h1 / l0,l1 in element order) and
-// their scale bytes.
+// their scale bytes; TERMS = 1 encodes hi only (lo zero, scale byte 127).
+template <int TERMS>
 __device__ __forceinline__ void mx8_encode_block(const float (&v)[32], uint4& h0, uint4& h1,
                                                  uint4& l0, uint4& l1, uint32_t& sh,
                                                  uint32_t& sl) {
@@ -103,11 +107,20 @@ __device__ __forceinline__ void mx8_encode_block(const float (&v)[32], uint4& h0
     w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * d], -X), ldexpf(v[4 * d + 1], -X), w, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * d + 2], -X), ldexpf(v[4 * d + 3], -X), w, true);
     hw[d] = (uint32_t)w;
+    if constexpr (TERMS == 1) continue;
     // residual against the decoded hi value (exact in fp32)
     r[4 * d + 0] = v[4 * d + 0] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 0), X);
     r[4 * d + 1] = v[4 * d + 1] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 1), X);
     r[4 * d + 2] = v[4 * d + 2] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 2), X);
     r[4 * d + 3] = v[4 * d + 3] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hw[d], 3), X);
+  }
+  h0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  h1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+  sh = (uint32_t)(X + 127);
+  if constexpr (TERMS == 1) {
+    l0 = l1 = make_uint4(0, 0, 0, 0);
+    sl = 127u;
+    return;
   }
   float rmax = 0.f;
 #pragma unroll
@@ -121,11 +134,8 @@ __device__ __forceinline__ void mx8_encode_block(const float (&v)[32], uint4& h0
     w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[4 * d + 2], -Xl), ldexpf(r[4 * d + 3], -Xl), w, true);
     lw[d] = (uint32_t)w;
   }
-  h0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-  h1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
   l0 = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   l1 = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-  sh = (uint32_t)(X + 127);
   sl = (uint32_t)(Xl + 127);
 }
 
@@ -206,9 +216,10 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. x -> MXFP8 hi / lo, one thread per (token, 32-block); blocks past H are zero (scale
-//    byte 127)
+// 2. x -> MXFP8 hi / lo (hi only for TERMS = 1), one thread per (token, 32-block); blocks
+//    past H are zero (scale byte 127)
 // ---------------------------------------------------------------------------------------
+template <int TERMS>
 __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                       int Hp, uint8_t* __restrict__ qhi,
                                                       uint8_t* __restrict__ qlo,
@@ -234,16 +245,18 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
         v[8 * q + 2 * i + 1] = bf16_bits_to_f32(ww[i] >> 16);
       }
     }
-    mx8_encode_block(v, h0, h1, l0, l1, sh, sl);
+    mx8_encode_block<TERMS>(v, h0, h1, l0, l1, sh, sl);
   }
   uint4* dh = reinterpret_cast<uint4*>(qhi + t * Hp + kBlock * b);
-  uint4* dl = reinterpret_cast<uint4*>(qlo + t * Hp + kBlock * b);
   dh[0] = h0;
   dh[1] = h1;
-  dl[0] = l0;
-  dl[1] = l1;
   shi[t * nbk + b] = (uint8_t)sh;
-  slo[t * nbk + b] = (uint8_t)sl;
+  if constexpr (TERMS == 2) {
+    uint4* dl = reinterpret_cast<uint4*>(qlo + t * Hp + kBlock * b);
+    dl[0] = l0;
+    dl[1] = l1;
+    slo[t * nbk + b] = (uint8_t)sl;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -268,38 +281,49 @@ struct GemmCtx {
   const uint8_t* alo;
   const uint8_t* ashi;
   const uint8_t* aslo;
-  long r0, r1, r2, r3;  // byte offsets of the A rows of this thread's four pieces
+  long r0, r1, r2, r3;  // byte offsets of the A rows of this thread's pieces (four; two hi
+                        // pieces with one term)
   long sr;              // byte offset of the scale row of this thread's scale dword
-  int part;             // 16-byte piece of the row (0..7 hi, 8..15 lo), same for all four
+  int part;             // 16-byte piece of the row (0..7 hi, 8..15 lo), same for all pieces
   int KB;               // K blocks of 32
   int Kp;               // padded K (row pitch of the A data, bytes)
 };
 
 // The staged values travel in five separate registers (d0..d3, s): a struct or array
-// carried around the K loop is placed in private memory.
+// carried around the K loop is placed in private memory. With one term a thread moves two
+// hi pieces (d0, d1) and its scale dword is the hi one (the lo slot of the LDS scale row is
+// filled with the same bytes and never read).
+template <int TERMS>
 __device__ __forceinline__ void stage_load(const GemmCtx& cx, int c, uint4& d0, uint4& d1,
                                            uint4& d2, uint4& d3, uint32_t& sv) {
   const long off = 128L * c + 16 * (cx.part & 7);
   const uint8_t* base = cx.part < 8 ? cx.ahi : cx.alo;
   d0 = *reinterpret_cast<const uint4*>(base + cx.r0 + off);
   d1 = *reinterpret_cast<const uint4*>(base + cx.r1 + off);
-  d2 = *reinterpret_cast<const uint4*>(base + cx.r2 + off);
-  d3 = *reinterpret_cast<const uint4*>(base + cx.r3 + off);
+  if constexpr (TERMS == 2) {
+    d2 = *reinterpret_cast<const uint4*>(base + cx.r2 + off);
+    d3 = *reinterpret_cast<const uint4*>(base + cx.r3 + off);
+  }
   const int tid = threadIdx.x;
-  const uint8_t* sb = (tid & 1) ? cx.aslo : cx.ashi;
+  const uint8_t* sb = (TERMS == 2 && (tid & 1)) ? cx.aslo : cx.ashi;
   sv = *reinterpret_cast<const uint32_t*>(sb + cx.sr + 4L * c);
 }
 
-// piece i of thread tid: q = tid + kBThreads i, row q / 16, part q % 16
+// piece i of thread tid: q = tid + kBThreads i, row q / 16, part q % 16 (two terms) or row
+// q / 8, part q % 8 (one term)
+template <int TERMS>
 __device__ __forceinline__ void stage_store(uint8_t* lds, uint8_t* lds_s, uint4 d0, uint4 d1,
                                             uint4 d2, uint4 d3, uint32_t sv) {
   const int tid = threadIdx.x;
-  uint8_t* p = lds + (tid >> 4) * kAPitch + 16 * (tid & 15);
-  constexpr int kRowStep = (kBThreads / 16) * kAPitch;
+  constexpr int kParts = 8 * TERMS;
+  uint8_t* p = lds + (tid / kParts) * kAPitch + 16 * (tid % kParts);
+  constexpr int kRowStep = (kBThreads / kParts) * kAPitch;
   *reinterpret_cast<uint4*>(p) = d0;
   *reinterpret_cast<uint4*>(p + kRowStep) = d1;
-  *reinterpret_cast<uint4*>(p + 2 * kRowStep) = d2;
-  *reinterpret_cast<uint4*>(p + 3 * kRowStep) = d3;
+  if constexpr (TERMS == 2) {
+    *reinterpret_cast<uint4*>(p + 2 * kRowStep) = d2;
+    *reinterpret_cast<uint4*>(p + 3 * kRowStep) = d3;
+  }
   if (tid < 2 * kBlockRows) *reinterpret_cast<uint32_t*>(lds_s + 4 * tid) = sv;
 }
 
@@ -396,13 +420,19 @@ __device__ __forceinline__ void mfma2(f32x4_t& acc, const i32x8_t& ahi, const i3
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, (int)b.s);
 }
 
+__device__ __forceinline__ void mfma1(f32x4_t& acc, const i32x8_t& ahi, const BWord& b, int sw_hi) {
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, b_operand(b.w), acc, 0, 4, 0, sw_hi, 0,
+                                                         (int)b.s);
+}
+
 // BSETS 2 or 3: the K loop runs BSETS chunks per trip with BSETS B sets used in turn and
 // reloaded in place, BSETS chunks ahead (gate/up, which has the registers for it). BSETS 1:
 // one B set rotates (current = next), a register copy that waits for the next set's loads,
 // two chunks ahead; the smaller register budget of down keeps it spill-free.
 // ADEPTH 2 (with BSETS 2): the A staging loads run two chunks ahead of their LDS store, in
 // two register sets used on alternate chunks (no copies between them).
-template <int NB, int BSETS, int ADEPTH = 1>
+// TERMS 1: the A rows hold one MXFP8 term (hi), one MFMA per B word.
+template <int NB, int BSETS, int ADEPTH, int TERMS>
 __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, int rows,
                                             uint8_t* lds, uint8_t* lds_s, Acc<NB>& acc) {
   static_assert(ADEPTH == 1 || (ADEPTH == 2 && BSETS == 2), "A depth 2 runs with two B sets");
@@ -416,10 +446,10 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   constexpr int kBufS = kBlockRows * 8;
   uint4 d0, d1, d2, d3, e0, e1, e2, e3;
   uint32_t sv, se;
-  stage_load(cx, 0, d0, d1, d2, d3, sv);
-  stage_store(lds, lds_s, d0, d1, d2, d3, sv);
-  stage_load(cx, min(1, nch - 1), d0, d1, d2, d3, sv);
-  if constexpr (ADEPTH == 2) stage_load(cx, min(2, nch - 1), e0, e1, e2, e3, se);
+  stage_load<TERMS>(cx, 0, d0, d1, d2, d3, sv);
+  stage_store<TERMS>(lds, lds_s, d0, d1, d2, d3, sv);
+  stage_load<TERMS>(cx, min(1, nch - 1), d0, d1, d2, d3, sv);
+  if constexpr (ADEPTH == 2) stage_load<TERMS>(cx, min(2, nch - 1), e0, e1, e2, e3, se);
   // B sets: chunk c uses b[c % BSETS] (BSETS > 1) or the rotated pair b0 <- b1
   BSet<NB> b0 = load_bset<NB>(bp, 0, cx.KB);
   BSet<NB> b1 = load_bset<NB>(bp, min(1, nch - 1), cx.KB);
@@ -445,21 +475,28 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
         if (16 * m < rows) { /* wave-uniform */                                                 \
           const i32x8_t ahi = PAIR ? a_operand(A, m, lane, false, h0, h1)                       \
                                    : a_operand_br(A, m, lane, false, h0, h1);                   \
-          const i32x8_t alo = PAIR ? a_operand(A, m, lane, true, h0, h1)                        \
-                                   : a_operand_br(A, m, lane, true, h0, h1);                    \
           const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;                         \
-          const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;                     \
-          mfma2(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo);                                    \
-          if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo);              \
-          if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo);              \
-          if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo);              \
+          if constexpr (TERMS == 2) {                                                           \
+            const i32x8_t alo = PAIR ? a_operand(A, m, lane, true, h0, h1)                      \
+                                     : a_operand_br(A, m, lane, true, h0, h1);                  \
+            const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;                   \
+            mfma2(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo);                                  \
+            if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo);            \
+            if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo);            \
+            if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo);            \
+          } else {                                                                              \
+            mfma1(acc.a[m][0], ahi, BS.w0, sw_hi);                                              \
+            if constexpr (NB > 1) mfma1(acc.a[m][1], ahi, BS.w1, sw_hi);                        \
+            if constexpr (NB > 2) mfma1(acc.a[m][2], ahi, BS.w2, sw_hi);                        \
+            if constexpr (NB > 3) mfma1(acc.a[m][3], ahi, BS.w3, sw_hi);                        \
+          }                                                                                     \
         }                                                                                       \
       }                                                                                         \
     }                                                                                           \
-    stage_store(lds + (((C) + 1) & 1) * kBuf, lds_s + (((C) + 1) & 1) * kBufS, X0, X1, X2, X3,  \
-                XS);                                                                            \
+    stage_store<TERMS>(lds + (((C) + 1) & 1) * kBuf, lds_s + (((C) + 1) & 1) * kBufS, X0, X1,   \
+                       X2, X3, XS);                                                             \
     const int cn = min((C) + 2, nch - 1);                                                       \
-    stage_load(cx, min((C) + 1 + ADEPTH, nch - 1), X0, X1, X2, X3, XS);                         \
+    stage_load<TERMS>(cx, min((C) + 1 + ADEPTH, nch - 1), X0, X1, X2, X3, XS);                  \
     if constexpr (PAIR) {                                                                       \
       /* the A loads go out before the B loads, so the next LDS store waits for A only */       \
       __builtin_amdgcn_sched_barrier(0);                                                        \
@@ -505,15 +542,20 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
 
 // Fills the per-thread A row offsets. row_of(i) returns the A row (token or sorted position)
 // of block row i (clamped into the block by the caller).
-template <typename RowOf>
+template <int TERMS, typename RowOf>
 __device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
   const int tid = threadIdx.x;
-  constexpr int kRows = kBThreads / 16;  // rows covered by one piece index
-  cx.r0 = (long)row_of(tid >> 4) * cx.Kp;
-  cx.r1 = (long)row_of((tid >> 4) + kRows) * cx.Kp;
-  cx.r2 = (long)row_of((tid >> 4) + 2 * kRows) * cx.Kp;
-  cx.r3 = (long)row_of((tid >> 4) + 3 * kRows) * cx.Kp;
-  cx.part = tid & 15;
+  constexpr int kParts = 8 * TERMS;              // 16-byte pieces per staged row
+  constexpr int kRows = kBThreads / kParts;      // rows covered by one piece index
+  static_assert(kRows * (2 * TERMS) == kBlockRows, "pieces cover the block's rows");
+  cx.r0 = (long)row_of(tid / kParts) * cx.Kp;
+  cx.r1 = (long)row_of(tid / kParts + kRows) * cx.Kp;
+  cx.r2 = cx.r3 = cx.r0;
+  if constexpr (TERMS == 2) {
+    cx.r2 = (long)row_of(tid / kParts + 2 * kRows) * cx.Kp;
+    cx.r3 = (long)row_of(tid / kParts + 3 * kRows) * cx.Kp;
+  }
+  cx.part = tid % kParts;
   cx.sr = (long)row_of(min(tid >> 1, kBlockRows - 1)) * (cx.Kp / kBlock);
 }
 
@@ -547,6 +589,7 @@ __device__ __forceinline__ bool map_block_tile(int b, int nb, int n_tiles, int& 
 // ---------------------------------------------------------------------------------------
 // 3. gate / up / SiLU / h quantisation
 // ---------------------------------------------------------------------------------------
+template <int TERMS>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_gate_up_kernel(
     const uint8_t* __restrict__ xhi, const uint8_t* __restrict__ xlo,
     const uint8_t* __restrict__ xshi, const uint8_t* __restrict__ xslo, int Hp,
@@ -576,7 +619,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   cx.aslo = xslo;
   cx.KB = KB;
   cx.Kp = Hp;
-  gemm_ctx_rows(cx, [&](int i) { return perm[row0 + min(i, rows - 1)] / k; });
+  gemm_ctx_rows<TERMS>(cx, [&](int i) { return perm[row0 + min(i, rows - 1)] / k; });
 
   const uint8_t* base = packed + (size_t)e * stride;
   const int nt16 = I / 16;
@@ -598,7 +641,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<4, MOE_FP4_GU_BSETS, MOE_FP4_GU_ADEPTH>(cx, bp, rows, lds, lds_s, acc);
+  gemm_k_loop<4, MOE_FP4_GU_BSETS, MOE_FP4_GU_ADEPTH, TERMS>(cx, bp, rows, lds, lds_s, acc);
 
   // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
@@ -625,16 +668,18 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int i = 0; i < 32; ++i) v[i] = htile[r * kHP + 32 * b + i];
       uint4 h0, h1, l0, l1;
       uint32_t sh, sl;
-      mx8_encode_block(v, h0, h1, l0, l1, sh, sl);
+      mx8_encode_block<TERMS>(v, h0, h1, l0, l1, sh, sl);
       const long pos = row0 + r;
       uint4* dh = reinterpret_cast<uint4*>(hhi + pos * Ip + col);
-      uint4* dl = reinterpret_cast<uint4*>(hlo + pos * Ip + col);
       dh[0] = h0;
       dh[1] = h1;
-      dl[0] = l0;
-      dl[1] = l1;
       hshi[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sh;
-      hslo[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sl;
+      if constexpr (TERMS == 2) {
+        uint4* dl = reinterpret_cast<uint4*>(hlo + pos * Ip + col);
+        dl[0] = l0;
+        dl[1] = l1;
+        hslo[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sl;
+      }
     }
   }
 }
@@ -642,6 +687,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 // ---------------------------------------------------------------------------------------
 // 4. down projection, times the router weight, fp32 per pair
 // ---------------------------------------------------------------------------------------
+template <int TERMS>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_down_kernel(
     const uint8_t* __restrict__ hhi, const uint8_t* __restrict__ hlo,
     const uint8_t* __restrict__ hshi, const uint8_t* __restrict__ hslo, int Ip,
@@ -670,7 +716,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   cx.aslo = hslo;
   cx.KB = KB;
   cx.Kp = Ip;
-  gemm_ctx_rows(cx, [&](int i) { return row0 + min(i, rows - 1); });
+  gemm_ctx_rows<TERMS>(cx, [&](int i) { return row0 + min(i, rows - 1); });
 
   const uint8_t* base = packed + (size_t)e * stride;
   const int nt16 = H / 16;
@@ -689,7 +735,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   Acc<2> acc;
 #pragma unroll
   for (int m = 0; m < kMSub; ++m) acc.a[m][0] = acc.a[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<2, 1>(cx, bp, rows, lds, lds_s, acc);
+  gemm_k_loop<2, 1, 1, TERMS>(cx, bp, rows, lds, lds_s, acc);
 
 #pragma unroll
   for (int s2 = 0; s2 < kNS; ++s2) {
@@ -816,7 +862,8 @@ BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter)
   return L;
 }
 
-hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
+template <int TERMS>
+static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
                               const uint8_t* packed, int n_experts, int hidden, int inter,
                               uint16_t* y, void* workspace, hipStream_t s) {
   const BatchedLayout B = batched_layout(T, k, n_experts, hidden, inter);
@@ -837,7 +884,7 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
   if (e != hipSuccess) return e;
 
   const long qn = (long)T * (B.Hp / kBlock);
-  e = launch_kernel(kKindBatchedQuant, quant_x_kernel, dim3((unsigned)((qn + 255) / 256)), dim3(256), 0,
+  e = launch_kernel(kKindBatchedQuant, quant_x_kernel<TERMS>, dim3((unsigned)((qn + 255) / 256)), dim3(256), 0,
                     s, x, T, hidden, B.Hp, ws + B.xhi, ws + B.xlo, ws + B.xshi, ws + B.xslo);
   if (e != hipSuccess) return e;
 
@@ -845,7 +892,7 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
   static_assert(kXcds == 8, "grid rounding below");
   const long gu_grid = ((long)B.nb_max * gu_tiles + 7) / 8 * 8;  // a multiple of the XCD count
   if (gu_grid > 0x7fffffffL) return hipErrorInvalidValue;
-  e = launch_kernel(kKindBatchedGateUp, gemm_gate_up_kernel, dim3((unsigned)gu_grid), dim3(kBThreads), 0,
+  e = launch_kernel(kKindBatchedGateUp, gemm_gate_up_kernel<TERMS>, dim3((unsigned)gu_grid), dim3(kBThreads), 0,
                     s, ws + B.xhi, ws + B.xlo, ws + B.xshi, ws + B.xslo, B.Hp, perm, bexp, brow0,
                     brows, nblk, k, packed, L.stride, L.m[0].codes, L.m[1].codes, L.m[0].scales,
                     L.m[1].scales, hidden, inter, gu_tiles, ws + B.hhi, ws + B.hlo, ws + B.hshi,
@@ -856,13 +903,23 @@ hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float
   const long dn_grid = ((long)B.nb_max * dn_tiles + 7) / 8 * 8;
   if (dn_grid > 0x7fffffffL) return hipErrorInvalidValue;
   float* ypair = reinterpret_cast<float*>(ws + B.ypair);
-  e = launch_kernel(kKindBatchedDown, gemm_down_kernel, dim3((unsigned)dn_grid), dim3(kBThreads), 0, s,
+  e = launch_kernel(kKindBatchedDown, gemm_down_kernel<TERMS>, dim3((unsigned)dn_grid), dim3(kBThreads), 0, s,
                     ws + B.hhi, ws + B.hlo, ws + B.hshi, ws + B.hslo, B.Ip, perm, w, bexp, brow0,
                     brows, nblk, packed, L.stride, L.m[2].codes, L.m[2].scales, hidden, inter,
                     dn_tiles, ypair);
   if (e != hipSuccess) return e;
 
   return launch_combine_pairs(ids, w, T, k, n_experts, hidden, ypair, y, s);
+}
+
+hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
+                              const uint8_t* packed, int n_experts, int hidden, int inter,
+                              uint16_t* y, void* workspace, int terms, hipStream_t s) {
+  if (terms == 1)
+    return batched_ffn<1>(x, ids, w, T, k, packed, n_experts, hidden, inter, y, workspace, s);
+  if (terms == 2)
+    return batched_ffn<2>(x, ids, w, T, k, packed, n_experts, hidden, inter, y, workspace, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine_pairs(const int32_t* ids, const float* w, int T, int k, int n_experts,

@@ -142,9 +142,10 @@ struct BatchedLayout {
 
 BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter);
 
+// terms: 2 = x and h as two-term MXFP8 (hi + lo), 1 = one term (hi only)
 hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
                               const uint8_t* packed, int n_experts, int hidden, int inter,
-                              uint16_t* y, void* workspace, hipStream_t s);
+                              uint16_t* y, void* workspace, int terms, hipStream_t s);
 
 // Layer chaining helpers (multi-layer decode harness).
 hipError_t launch_residual_init(const uint16_t* x, float* r, int T, int hidden, hipStream_t s);

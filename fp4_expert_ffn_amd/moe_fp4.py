@@ -177,7 +177,7 @@ def moe_fp4_expert_ffn(x, topk_ids, topk_w, T: int, k: int, packed, n_experts: i
                                     workspace_bytes, _stream(stream)), "moe_fp4_expert_ffn")
 
 
-PATH_AUTO, PATH_DECODE, PATH_GROUPED, PATH_SMALL_M = 0, 1, 2, 3
+PATH_AUTO, PATH_DECODE, PATH_GROUPED, PATH_SMALL_M, PATH_GROUPED_FP8 = 0, 1, 2, 3, 4
 
 
 def moe_fp4_residual_init(x, residual, T: int, hidden: int, stream=None) -> None:

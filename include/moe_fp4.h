@@ -159,6 +159,12 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
  *    canonical slot order (three launches). G is the largest power of two <= min(T, 8)
  *    with G * max(hidden, inter) <= 16384 (the group's bf16 rows fit in 32 KB of LDS);
  *    needs 2 <= T, T * k <= 256 and G >= 2 (max(hidden, inter) <= 8192).
+ *  MOE_FP4_PATH_GROUPED_FP8: opt-in; GROUPED with the activations x and h as one MXFP8
+ *    term (E4M3, one ue8m0 scale per 32 elements): DeepSeek's FP8 activation numerics
+ *    ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug: activations quantised with ue8m0
+ *    scales). Half the activation bytes and matrix-core work of GROUPED; the result is that
+ *    of the quantised activations, which on the 384-expert layer lies further from the exact
+ *    bf16 computation than the 2e-2 normwise bar of the other paths. AUTO never picks it.
  *  MOE_FP4_PATH_AUTO: GROUPED from 24 tokens on; SMALL_M from 2 to 23 tokens where its
  *    limits hold; DECODE otherwise (one token, or a shape SMALL_M refuses). Measured on the
  *    384-expert layer: SMALL_M is faster than DECODE at every T >= 2, with uniform and with
@@ -171,6 +177,7 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
 #define MOE_FP4_PATH_DECODE 1
 #define MOE_FP4_PATH_GROUPED 2
 #define MOE_FP4_PATH_SMALL_M 3
+#define MOE_FP4_PATH_GROUPED_FP8 4
 int moe_fp4_expert_ffn_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_w, int T,
                           int k, const void* packed, int n_experts, int hidden, int inter,
                           uint16_t* y, void* workspace, size_t workspace_bytes, int path,

@@ -48,8 +48,17 @@ def _random_routing(rng, T, k, E, distinct=True):
     return ids, w
 
 
-DECODE, GROUPED, SMALL_M = 1, 2, 3  # moe_fp4_expert_ffn_ex paths
-PATHS = pytest.mark.parametrize("path", [DECODE, GROUPED, SMALL_M], ids=["decode", "grouped", "small_m"])
+DECODE, GROUPED, SMALL_M, GROUPED_FP8 = 1, 2, 3, 4  # moe_fp4_expert_ffn_ex paths
+PATHS = pytest.mark.parametrize("path", [DECODE, GROUPED, SMALL_M, GROUPED_FP8],
+                                ids=["decode", "grouped", "small_m", "grouped_fp8"])
+
+
+def _ref(path, x_bits, ids, w, src, E, H, I):
+    """The oracle result a path is held to: the exact FFN, or for the opt-in single-term FP8
+    path the FFN on x and h quantised to one MXFP8 term (its own numerics)."""
+    if path == GROUPED_FP8:
+        return O.expert_ffn_mx(x_bits, ids, w, src, E, H, I, "e4m3", 1)
+    return O.expert_ffn(x_bits, ids, w, src, E, H, I)
 
 
 def _run_ffn(layer, x_bits, ids, w, dev, path=None):
@@ -224,7 +233,7 @@ def test_ffn_small_shapes(dev, H, I, E, k, T, path):
     ids, w = _random_routing(rng, T, k, E)
     x_bits = S.activations(wl, 0, 0)
     y = _run_ffn(layer, x_bits, ids, w, dev, path)
-    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), E, H, I)
+    ref = _ref(path, x_bits, ids, w, S.expert_source(wl), E, H, I)
     err, cos = check_ffn(y, ref, f"path {path} H{H} I{I} E{E} k{k} T{T}")
     log(f"path {path} H{H} I{I} E{E} k{k} T{T}: normwise {err:.2e} cosine {cos:.7f}")
 
@@ -295,6 +304,17 @@ def test_layer_batched64_zipf_full_size(dev, decode_layer):
         err, cos = check_ffn(D.bf16_bits(y), ref, f"zipf64 path {path}")
         log(f"batched64 zipf path {path}: {len(np.unique(ids_ref))} distinct experts, "
             f"normwise {err:.2e} cosine {cos:.7f}")
+    # the single-term FP8 path against its own oracle numerics, on a sample of tokens
+    sample = np.sort(np.random.default_rng(64).choice(64, size=8, replace=False))
+    ref8 = O.expert_ffn_mx(x_bits[sample], ids_ref[sample], w_ref[sample], S.expert_source(wl_l),
+                           384, 4096, 2880, "e4m3", 1)
+    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w, path=GROUPED_FP8)
+    torch.cuda.synchronize()
+    yb = D.bf16_bits(y)
+    err, cos = check_ffn(yb[sample], ref8, "zipf64 grouped_fp8")
+    err_x = max(O.normwise_rel_err(O.bf16_to_f64(yb[sample][i]), ref[sample][i]) for i in range(8))
+    log(f"batched64 zipf grouped_fp8, sample of 8: normwise {err:.2e} cosine {cos:.7f} against the "
+        f"one-term MX oracle; {err_x:.2e} from the exact result")
 
 
 def test_layer_prefill8192_sampled(dev, decode_layer):
@@ -364,7 +384,7 @@ def test_invalid_and_duplicate_ids(dev, small_layer, path):
     w = np.random.default_rng(9).random((3, 6)).astype(np.float32)
     x_bits = S.activations(wl, 0, 1, tokens=3)
     y = _run_ffn(layer, x_bits, ids, w, dev, path)
-    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), E, wl.hidden, wl.inter)
+    ref = _ref(path, x_bits, ids, w, S.expert_source(wl), E, wl.hidden, wl.inter)
     check_ffn(y[:2], ref[:2], f"invalid/duplicate ids, path {path}")
     assert np.all(O.bf16_to_f64(y[2]) == 0.0)  # no valid id: exactly zero
     bad = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -381,7 +401,7 @@ def test_k_extremes(dev, small_layer, k, path):
     ids, w = _random_routing(rng, 5, k, wl.n_experts)
     x_bits = S.activations(wl, 0, 2, tokens=5)
     y = _run_ffn(layer, x_bits, ids, w, dev, path)
-    ref = O.expert_ffn(x_bits, ids, w, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
+    ref = _ref(path, x_bits, ids, w, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
     check_ffn(y, ref, f"k={k} path {path}")
 
 
@@ -405,7 +425,8 @@ def test_slot_permutation_is_bit_identical(dev, small_layer, path):
     assert np.array_equal(y0[tp], y2)
 
 
-@pytest.mark.parametrize("path", [None, DECODE, GROUPED, SMALL_M], ids=["auto", "decode", "grouped", "small_m"])
+@pytest.mark.parametrize("path", [None, DECODE, GROUPED, SMALL_M, GROUPED_FP8],
+                         ids=["auto", "decode", "grouped", "small_m", "grouped_fp8"])
 @pytest.mark.parametrize("T", [1, 17, 64, 65, 300, 1024])
 def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
     """Same input five times: bit-identical outputs and no NaN/Inf, at token counts on both
@@ -419,8 +440,8 @@ def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
         assert np.array_equal(o, outs[0])
     assert np.all(np.isfinite(O.bf16_to_f64(outs[0])))
     sample = np.unique(np.linspace(0, T - 1, min(T, 8)).astype(int))
-    ref = O.expert_ffn(x_bits[sample], ids[sample], w[sample], S.expert_source(wl), wl.n_experts,
-                       wl.hidden, wl.inter)
+    ref = _ref(path, x_bits[sample], ids[sample], w[sample], S.expert_source(wl), wl.n_experts,
+               wl.hidden, wl.inter)
     check_ffn(outs[0][sample], ref, f"T={T} path {path}")
 
 
