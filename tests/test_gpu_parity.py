@@ -317,6 +317,36 @@ def test_layer_batched64_zipf_full_size(dev, decode_layer):
         f"one-term MX oracle; {err_x:.2e} from the exact result")
 
 
+@pytest.mark.parametrize("name", ["mtp4_correlated", "streams8_uniform"])
+def test_layer_multi_token_full_size(dev, decode_layer, name):
+    """The multi-token decode shapes through the 384-expert layer as the bench runs them
+    (automatic path choice: the small-M kernels), every token against the oracle, and the
+    decode kernels on the same routing."""
+    C, D = _mods()
+    wl_l, layer = decode_layer
+    wl = S.WORKLOADS[name]
+    lg = S.router_logits(wl, 0, 0)
+    ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
+    ids_ref, w_ref = O.topk_softmax(lg.astype(np.float64), 6)
+    torch.cuda.synchronize()
+    check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, name)
+    x_bits = S.activations(wl, 0, 0)
+    ref = O.expert_ffn(x_bits, ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
+    C.moe_fp4_timing_reset()
+    C.moe_fp4_timing_enable(True)
+    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w)
+    torch.cuda.synchronize()
+    C.moe_fp4_timing_enable(False)
+    launched = {n for kind, n in enumerate(C.KERNEL_NAMES) if C.moe_fp4_timing_read(kind)[0]}
+    C.moe_fp4_timing_reset()
+    assert "small_m_gate_up" in launched and "gate_up" not in launched, launched
+    err, cos = check_ffn(D.bf16_bits(y), ref, f"{name} small-M")
+    y_d = layer.ffn(D.upload_bf16(x_bits, dev), ids, w, path=DECODE)
+    torch.cuda.synchronize()
+    check_ffn(D.bf16_bits(y_d), ref, f"{name} decode")
+    log(f"{name}: {len(np.unique(ids_ref))} distinct experts, small-M normwise {err:.2e} cosine {cos:.7f}")
+
+
 def test_layer_prefill8192_sampled(dev, decode_layer):
     """8192 tokens with uniform logits; the oracle checks a seeded sample of tokens."""
     _, D = _mods()
