@@ -352,6 +352,22 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
                                        matrix, out, s));
 }
 
+size_t moe_fp4_debug_act_quant_bytes(int T, int hidden) {
+  if (T < 0 || !valid_dim(hidden)) return 0;
+  return debug_act_quant_bytes(T, hidden);
+}
+
+int moe_fp4_debug_act_quant(const uint16_t* x, int T, int hidden, int terms, void* workspace,
+                            size_t workspace_bytes, float* out, void* stream) {
+  if (!x || !out || !workspace || T < 0 || terms < 1 || terms > 2) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(hidden)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < debug_act_quant_bytes(T, hidden)) return MOE_FP4_ERR_WORKSPACE;
+  if (T == 0) return MOE_FP4_OK;
+  return from_hip(launch_debug_act_quant(x, T, hidden, terms, workspace, out,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int moe_fp4_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   if (!src || !sink || bytes == 0 || bytes % 16 != 0) return MOE_FP4_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned4(sink)) return MOE_FP4_ERR_MISALIGNED;

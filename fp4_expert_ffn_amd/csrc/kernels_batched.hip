@@ -826,6 +826,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   }
 }
 
+// Debug: x quantised as the grouped path does it, decoded back to fp32: out[t][h] = the sum
+// of the terms, each E4M3 code times 2^(scale - 127) (exact in fp32: a term has at most four
+// significant bits and the two terms of a block are a few binades apart).
+template <int TERMS>
+__global__ __launch_bounds__(256) void dequant_act_kernel(const uint8_t* __restrict__ qhi,
+                                                          const uint8_t* __restrict__ qlo,
+                                                          const uint8_t* __restrict__ shi,
+                                                          const uint8_t* __restrict__ slo, int T,
+                                                          int H, int Hp, float* __restrict__ out) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)T * H) return;
+  const long t = idx / H;
+  const int h = (int)(idx - t * H);
+  const long sb = t * (Hp / kBlock) + h / kBlock;
+  float r = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)qhi[t * Hp + h], 0), (int)shi[sb] - 127);
+  if constexpr (TERMS == 2)
+    r += ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)qlo[t * Hp + h], 0), (int)slo[sb] - 127);
+  out[idx] = r;
+}
+
+template <int TERMS>
+hipError_t debug_act_quant(const uint16_t* x, int T, int H, uint8_t* ws, float* out, hipStream_t s) {
+  const int Hp = (H + 127) / 128 * 128;
+  const size_t q = (size_t)T * Hp, sc = (size_t)T * (Hp / kBlock);
+  uint8_t *qhi = ws, *qlo = ws + q, *shi = ws + 2 * q, *slo = ws + 2 * q + sc;
+  const long qn = (long)T * (Hp / kBlock);
+  hipError_t e = launch_kernel(kKindBatchedQuant, quant_x_kernel<TERMS>,
+                               dim3((unsigned)((qn + 255) / 256)), dim3(256), 0, s, x, T, H, Hp, qhi,
+                               qlo, shi, slo);
+  if (e != hipSuccess) return e;
+  const long n = (long)T * H;
+  return launch_kernel(kKindBatchedQuant, dequant_act_kernel<TERMS>, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, qhi, qlo, shi, slo, T, H, Hp, out);
+}
+
 }  // namespace
 
 BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter) {
@@ -929,6 +964,20 @@ hipError_t launch_combine_pairs(const int32_t* ids, const float* w, int T, int k
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
   return launch_kernel(kKindBatchedCombine, combine_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                        ids, w, k, n_experts, hidden, col_blocks, ypair, y);
+}
+
+size_t debug_act_quant_bytes(int T, int H) {
+  const size_t Hp = (size_t)(H + 127) / 128 * 128;
+  return 2 * (size_t)T * Hp + 2 * (size_t)T * (Hp / kBlock);
+}
+
+hipError_t launch_debug_act_quant(const uint16_t* x, int T, int H, int terms, void* ws, float* out,
+                                  hipStream_t s) {
+  if ((long)T * H > 0x7fffffffL * 256L) return hipErrorInvalidValue;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  if (terms == 1) return debug_act_quant<1>(x, T, H, w, out, s);
+  if (terms == 2) return debug_act_quant<2>(x, T, H, w, out, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe_fp4

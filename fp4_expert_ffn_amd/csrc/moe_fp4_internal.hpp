@@ -173,6 +173,12 @@ hipError_t launch_probe_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32
                                   hipStream_t s);
 int probe_mfma_chains();
 
+// The grouped path's activation quantisation of x [T x H] (MXFP8 E4M3, terms 1 or 2)
+// decoded back to fp32 out [T x H]; workspace debug_act_quant_bytes(T, H).
+size_t debug_act_quant_bytes(int T, int H);
+hipError_t launch_debug_act_quant(const uint16_t* x, int T, int H, int terms, void* ws,
+                                  float* out, hipStream_t s);
+
 hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
                                 int matrix, float* out, hipStream_t s);
 

@@ -65,6 +65,8 @@ _SIGNATURES = {
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_fp4_debug_act_quant_bytes": (ctypes.c_size_t, [_I, _I]),
+    "moe_fp4_debug_act_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_size_t, _P, _P]),
     "moe_fp4_debug_stream_read": (_I, [_P, _Z, _P, _P]),
     "moe_fp4_debug_mfma_loop": (_I, [_I, _I, _I, _P, _P]),
     "moe_fp4_timing_enable": (_I, [_I]),
@@ -230,6 +232,17 @@ def moe_fp4_moe_forward(x, w_router, T: int, hidden: int, n_experts: int, k: int
 def moe_fp4_validate_ids(topk_ids, T: int, k: int, n_experts: int, bad_count, stream=None) -> None:
     _check(lib().moe_fp4_validate_ids(_ptr(topk_ids), T, k, n_experts, _ptr(bad_count),
                                       _stream(stream)), "moe_fp4_validate_ids")
+
+
+def moe_fp4_debug_act_quant_bytes(T: int, hidden: int) -> int:
+    return lib().moe_fp4_debug_act_quant_bytes(T, hidden)
+
+
+def moe_fp4_debug_act_quant(x, T: int, hidden: int, terms: int, workspace,
+                            workspace_bytes: int, out, stream=None) -> None:
+    _check(lib().moe_fp4_debug_act_quant(_ptr(x), T, hidden, terms, _ptr(workspace),
+                                         workspace_bytes, _ptr(out), _stream(stream)),
+           "moe_fp4_debug_act_quant")
 
 
 def moe_fp4_debug_dequant(packed, n_experts: int, hidden: int, inter: int, expert: int,

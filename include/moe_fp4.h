@@ -251,6 +251,20 @@ int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,
 int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int inter, int expert,
                           int matrix, float* out, void* stream);
 
+/* Debug helper: the grouped path's activation quantisation of x [T x hidden] bf16 (device),
+ * decoded back to fp32 out [T x hidden] (device): per 32-element block, one or two MXFP8
+ * E4M3 terms (hi, then lo = the same quantisation of x - hi) with one ue8m0 scale each, the
+ * scale the smallest power of two that fits the block's maximum in 448, codes rounded to
+ * nearest with ties to the even code (OCP MX; [8GB-GPU], section RTX 50xx 上的三个从不抛错的
+ * Bug: ue8m0-scaled FP8 activations). terms 2: the GROUPED path's operand; terms 1: the
+ * GROUPED_FP8 path's. out is the exact sum of the decoded terms. workspace:
+ * moe_fp4_debug_act_quant_bytes(T, hidden) bytes of device memory, 16-byte aligned, contents
+ * irrelevant. Errors: INVALID_ARG (null pointer, T < 0, terms not 1 or 2), BAD_SHAPE,
+ * MISALIGNED, WORKSPACE, HIP. */
+size_t moe_fp4_debug_act_quant_bytes(int T, int hidden);
+int moe_fp4_debug_act_quant(const uint16_t* x, int T, int hidden, int terms, void* workspace,
+                            size_t workspace_bytes, float* out, void* stream);
+
 /* Measurement helper (not on the FFN path): reads `bytes` bytes at src with 16-byte
  * non-temporal loads, the load form of the expert kernels, over a grid of up to 2048
  * workgroups; for the measured HBM streaming peak. src: device, 16-byte aligned; bytes a

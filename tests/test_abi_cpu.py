@@ -138,6 +138,25 @@ def test_pack_and_debug_argument_checks(L):
     assert L.moe_fp4_validate_ids(None, 1, 6, 384, A, None) == C.ERR_INVALID_ARG
 
 
+def test_act_quant_argument_checks(L):
+    """Workspace size of the activation-quantiser helper (two terms and two scale rows per
+    token, hidden padded to 128) and its argument checks, none of which launches work."""
+    assert L.moe_fp4_debug_act_quant_bytes(3, 4096) == 2 * 3 * 4096 + 2 * 3 * 128
+    assert L.moe_fp4_debug_act_quant_bytes(1, 96) == 2 * 128 + 2 * 4
+    assert L.moe_fp4_debug_act_quant_bytes(1, 100) == 0
+    assert L.moe_fp4_debug_act_quant_bytes(-1, 128) == 0
+    big = 1 << 30
+    q = L.moe_fp4_debug_act_quant
+    assert q(None, 1, 256, 2, A, big, A, None) == C.ERR_INVALID_ARG
+    assert q(A, -1, 256, 2, A, big, A, None) == C.ERR_INVALID_ARG
+    assert q(A, 1, 256, 0, A, big, A, None) == C.ERR_INVALID_ARG
+    assert q(A, 1, 256, 3, A, big, A, None) == C.ERR_INVALID_ARG
+    assert q(A, 1, 250, 1, A, big, A, None) == C.ERR_BAD_SHAPE
+    assert q(MIS, 1, 256, 1, A, big, A, None) == C.ERR_MISALIGNED
+    assert q(A, 1, 256, 1, A, 100, A, None) == C.ERR_WORKSPACE
+    assert q(A, 0, 256, 2, A, 0, A, None) == C.OK
+
+
 def test_timing_read_without_records(L):
     C.moe_fp4_timing_reset()
     assert C.moe_fp4_timing_read(C.KERNEL_GATE_UP) == (0, 0.0)

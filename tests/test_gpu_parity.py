@@ -126,6 +126,39 @@ def test_pack_round_trip_bit_exact(dev, H, I, E):
             assert np.array_equal(got, O.dequant_fp4(c, s).astype(np.float32)), (e, m)
 
 
+# ------------------------------------------------------------------------------ activation quantiser
+
+@pytest.mark.parametrize("terms", [1, 2])
+@pytest.mark.parametrize("H", [4096, 2880, 96])
+def test_act_quant_bit_exact(dev, terms, H):
+    """The grouped path's activation quantiser (x -> MX hi [+ lo], ue8m0 per 32), decoded
+    back to fp32, equals the oracle's MX quantisation bit for bit: codes and scales are
+    rounding decisions on the same bf16 inputs. Blocks with zeros, a single value, grid ties,
+    values 2^-12 below their block maximum, rows scaled over 2^-40 .. 2^40, and a ragged
+    last 128-chunk (H 96, 2880)."""
+    C, D = _mods()
+    rng = np.random.default_rng(H + terms)
+    T = 37
+    v = rng.standard_normal((T, H)) * np.exp2(rng.integers(-40, 40, size=(T, 1)).astype(np.float64))
+    v[0, :32] = 0.0
+    v[1, :32] = 0.0
+    v[1, 5] = -3.0
+    v[2, :32] = np.arange(32) / 4.0               # E4M3 ties after scaling
+    v[3, :32] = np.where(np.arange(32) % 2 == 0, 1.0, 2.0 ** -12)
+    v[4, :32] = -(np.arange(32) + 0.5) * 0.0625   # every half-step between grid values
+    x_bits = O.f64_to_bf16_bits(v)
+    x = D.upload_bf16(x_bits, dev)
+    nbytes = C.moe_fp4_debug_act_quant_bytes(T, H)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    C.moe_fp4_debug_act_quant(x, T, H, terms, ws, nbytes, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = O.mx_quantize(O.bf16_to_f64(x_bits), "e4m3", terms)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[:3].tolist()}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
+
+
 # ------------------------------------------------------------------------------ router
 
 def test_route_ids_bit_exact_full_size(dev):
