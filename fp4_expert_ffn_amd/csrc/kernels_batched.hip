@@ -578,7 +578,10 @@ __device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
 // each row block's activations are reused by the group's tiles. Returns false for the
 // workgroups past the items (the grid is nb_max x n_tiles rounded up to a multiple of 8).
 constexpr int kXcds = 8;
-constexpr int kColGroup = 4;
+#ifndef MOE_FP4_COL_GROUP
+#define MOE_FP4_COL_GROUP 4  // column tiles whose row blocks are interleaved on one XCD
+#endif
+constexpr int kColGroup = MOE_FP4_COL_GROUP;
 
 __device__ __forceinline__ bool map_block_tile(int b, int nb, int n_tiles, int& blk, int& nt) {
   const long G = (long)nb * n_tiles;
