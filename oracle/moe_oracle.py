@@ -22,6 +22,9 @@ Sources. The pages this follows, cited by title and section:
   FP4 expert with scales. Section 方案：不重写模型，只迁移其存储: the three matrices of an
   expert are stored next to each other (17.7 MB) and the scales are a separate block
   (1.1 MB). Section RTX 50xx 上的三个从不抛错的 Bug: the scale format is ue8m0.
+* [A100-FP4], Chinese translation, section A100 也没有 FP8: the dense weights (the shared
+  expert, the dense projections) are FP8 E4M3, kept as a storage format and turned into bf16
+  matrix-core operands in registers.
 
 Readings taken where the pages are silent (each is listed with its reason in the design notes):
 
@@ -36,8 +39,9 @@ Readings taken where the pages are silent (each is listed with its reason in the
   logit with ties going to the lower expert id; weights = softmax over those k logits only
   (a full softmax renormalised over the chosen k gives the same numbers, since the full
   denominator cancels).
-* SwiGLU: h = silu(g) * u with silu(z) = z / (1 + exp(-z)); no clamp, no shared expert,
-  routed scaling factor 1.
+* SwiGLU: h = silu(g) * u with silu(z) = z / (1 + exp(-z)); no clamp, routed scaling factor
+  1; the routed FFN has no shared expert term (the FP8 shared expert is computed on its own,
+  section 6a).
 * Combine: y = sum_j w_j * y_{e_j}, summed in ascending expert id. Ids outside [0, E)
   contribute nothing. Duplicate ids are legal and add up.
 """
@@ -409,6 +413,61 @@ def expert_ffn_mx(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, expert_sou
         for r in range(rows_t.shape[0]):
             y[rows_t[r]] += w[rows_t[r], slots[r]] * ye[r]
     return y
+
+
+# ---------------------------------------------------------------------------------------
+# 6a. Dense FP8 weights: the shared expert and the dense projections. [A100-FP4], Chinese
+# translation, section A100 也没有 FP8: the dense weights are FP8 (E4M3), used as a storage
+# format only: each weight goes from memory into registers and becomes a bf16 matrix-core
+# operand there. Readings (the pages name FP8 E4M3 but not its encoding details or its
+# scaling): the OCP "FN" E4M3 encoding (bit 7 sign, bits 6:3 exponent with bias 7, bits
+# 2:0 mantissa; exponent field 0 is subnormal; S.1111.111 is NaN; no infinities; largest
+# finite value 448), and one fp32 multiplier per 128 x 128 block of the [out x in] matrix,
+# the block-scaled FP8 layout of DeepSeek's checkpoints.
+# ---------------------------------------------------------------------------------------
+
+#: Rows and columns per fp32 scale block of an FP8 matrix.
+FP8_BLOCK = 128
+
+
+def e4m3_table() -> np.ndarray:
+    """Value of each of the 256 E4M3 codes (NaN for 0x7F and 0xFF)."""
+    out = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            out[code] = np.nan
+        elif e == 0:
+            out[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            out[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def dequant_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """W[n, k] = e4m3(codes[n, k]) * scales[n // 128, k // 128], fp64 [N x K]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    scales = np.asarray(scales, dtype=np.float64)
+    assert scales.shape == ((n + FP8_BLOCK - 1) // FP8_BLOCK, (k + FP8_BLOCK - 1) // FP8_BLOCK)
+    w = e4m3_table()[codes]
+    rows = np.arange(n) // FP8_BLOCK
+    cols = np.arange(k) // FP8_BLOCK
+    return w * scales[rows[:, None], cols[None, :]]
+
+
+def dense_fp8(x_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """y = x W^T for bf16 x [T x K] and an FP8 matrix W [N x K]; fp64 [T x N]."""
+    return np.matmul(bf16_to_f64(x_bits), dequant_fp8(codes, scales).T)
+
+
+def shared_expert_fp8(x_bits: np.ndarray, gate, up, down) -> np.ndarray:
+    """SwiGLU FFN with FP8 matrices (each a (codes, scales) pair): gate, up [I x H],
+    down [H x I]; y = W_d (silu(W_g x) * (W_u x)), fp64 [T x H] (h is not rounded)."""
+    x = bf16_to_f64(x_bits)
+    return swiglu_expert(x, dequant_fp8(*gate), dequant_fp8(*up), dequant_fp8(*down))
 
 
 # ---------------------------------------------------------------------------------------

@@ -438,3 +438,66 @@ def test_residual_rmsnorm_hand_derived_cases():
     b = np.array([[0.25, 2.25, -1.0, 0.5]])
     r2, _ = O.residual_rmsnorm(a, b)
     assert r2.tolist() == [[1.75, 0.0, -1.0, 8.5]]
+
+
+# ------------------------------------------------------------------------------ dense FP8 weights
+
+def test_e4m3_table_matches_torch_float8_e4m3fn():
+    """All 256 E4M3 codes against an independent decoder (torch's float8_e4m3fn, CPU)."""
+    torch = pytest.importorskip("torch")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_table()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_hand_derived_codes():
+    t = O.e4m3_table()
+    assert t[0x38] == 1.0 and t[0xB8] == -1.0          # exponent 7 = bias, mantissa 0
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0      # the largest finite value
+    assert t[0x08] == 2.0 ** -6                         # the smallest normal
+    assert t[0x01] == 2.0 ** -9                         # the smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9                     # the largest subnormal
+    assert t[0x00] == 0.0 and math.copysign(1.0, t[0x80]) == -1.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)                     # codes 0..126 increase
+
+
+def test_fp8_block_scales_apply_per_128_block():
+    """Every code 1.0, a distinct power-of-ten multiplier per 128 x 128 block of a
+    260 x 300 matrix: each element carries its own block's multiplier, including the
+    ragged last blocks and the elements on both sides of each block edge."""
+    n, k = 260, 300
+    codes = np.full((n, k), 0x38, dtype=np.uint8)
+    scales = np.array([[10.0 ** (3 * i + j) for j in range(3)] for i in range(3)], dtype=np.float32)
+    w = O.dequant_fp8(codes, scales)
+    for (r, c) in [(0, 0), (127, 127), (128, 127), (127, 128), (128, 128), (255, 255), (256, 256),
+                   (259, 299)]:
+        assert w[r, c] == np.float64(scales[r // 128, c // 128]), (r, c)
+
+
+def test_shared_expert_fp8_reduces_to_the_routed_expert_oracle():
+    """An FP4 expert re-encoded exactly in FP8 (every FP4 value times its ue8m0 scale is an
+    E4M3 value for scale bytes 120..130; block multipliers 1): the FP8 SwiGLU FFN equals the
+    routed-expert oracle with one slot of weight 1, bit for bit."""
+    wl = S.small_workload(256, 160, 1, 1, 3, wid=901)
+    codes_flat, scales_flat = S.expert_blob(wl, 0, 0)
+    table = O.e4m3_table()
+    finite = ~np.isnan(table)
+    value_to_code = {float(v): c for c, v in enumerate(table) if finite[c] and not (v == 0 and c)}
+    mats = []
+    for (c, s) in O.split_expert(codes_flat, scales_flat, wl.hidden, wl.inter):
+        w = O.dequant_fp4(c, s)
+        fp8 = np.vectorize(lambda v: value_to_code[float(v)] if v != 0 else 0)(w).astype(np.uint8)
+        ones = np.ones(((w.shape[0] + 127) // 128, (w.shape[1] + 127) // 128), dtype=np.float32)
+        assert np.array_equal(O.dequant_fp8(fp8, ones), np.where(w == 0, 0.0, w))
+        mats.append((fp8, ones))
+    x_bits = S.activations(wl, 0, 0)
+    y8 = O.shared_expert_fp8(x_bits, *mats)
+    y4 = O.expert_ffn(x_bits, np.zeros((3, 1), np.int32), np.ones((3, 1)), S.expert_source(wl),
+                      1, wl.hidden, wl.inter)
+    assert np.array_equal(y8, y4)
