@@ -174,7 +174,7 @@ def main() -> int:
     ap.add_argument("--workload", default="layer_decode_h4096_i2880_e384",
                     choices=["layer_decode_h4096_i2880_e384", "batched64_zipf", "prefill8192_uniform",
                              "prefill32768_uniform", "stack16_decode", "expert_h256_i128",
-                             "mtp4_correlated", "streams8_uniform"],
+                             "mtp4_correlated", "streams8_uniform", "shared_expert_fp8_h4096_i2880"],
                     help="the batch-1 decode layer (default, the headline line), or one of the "
                          "multi-token shapes (small-M path below 24 tokens, grouped GEMM path "
                          "from 24 on)")
@@ -209,6 +209,8 @@ def main() -> int:
         return run_stack(args)
     if args.workload == "expert_h256_i128":
         return run_single_expert(args)
+    if args.workload == "shared_expert_fp8_h4096_i2880":
+        return run_shared_expert(args)
     if args.workload != "layer_decode_h4096_i2880_e384":
         return run_batched(args)
 
@@ -538,6 +540,101 @@ def run_single_expert(args) -> int:
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": {"workload": wl.name, "hidden": H, "intermediate": I,
                                             "launch": "stream"}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_shared_expert(args) -> int:
+    """The FP8 SwiGLU shared expert (hidden 4096, intermediate 2880, E4M3 weights with one
+    fp32 multiplier per 128 x 128 block) at batch 1: one fresh token per step, two kernel
+    launches (gate/up + SwiGLU, then down). HBM-bound: 1 byte per weight."""
+    import torch
+
+    from fp4_expert_ffn_amd import moe_fp4 as C
+    from synth import moe_inputs as S
+
+    C.lib()
+    dev = torch.device("cuda:0")
+    H, I = 4096, 2880
+    K, W = min(args.steps, 2000), min(args.warmup, 100)
+    mats = [S.fp8_matrix(I, H, seed=1), S.fp8_matrix(I, H, seed=2), S.fp8_matrix(H, I, seed=3)]
+    packed = []
+    for codes, scales in mats:
+        nb = C.moe_fp4_fp8_packed_bytes(codes.shape[0], codes.shape[1])
+        p = torch.empty(nb, dtype=torch.uint8, device=dev)
+        C.moe_fp4_fp8_pack(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev),
+                           codes.shape[0], codes.shape[1], p, nb)
+        packed.append(p)
+    n_x = W + 2 * K
+    xs = (torch.randn((n_x, H), device=dev) * 0.5).to(torch.bfloat16)
+    y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+    wsb = C.moe_fp4_shared_expert_workspace_bytes(1, I)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step(i: int) -> None:
+        C.moe_fp4_shared_expert(xs[i:i + 1], 1, packed[0], packed[1], packed[2], H, I, y, ws, wsb)
+
+    for i in range(W):
+        step(i)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(W, W + K):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / K
+    weight_bytes = sum(C.moe_fp4_fp8_packed_bytes(c.shape[0], c.shape[1]) for c, _ in mats)
+    alg = 3 * H * I + sum(s.size * 4 for _, s in mats) + 2 * H * 2 + 2 * I * 2
+    kernels = {}
+    C.moe_fp4_timing_reset()
+    C.moe_fp4_timing_enable(True)
+    for i in range(W + K, W + 2 * K):
+        step(i)
+    torch.cuda.synchronize()
+    C.moe_fp4_timing_enable(False)
+    n, ms = C.moe_fp4_timing_read(C.KERNEL_NAMES.index("fp8_gemv"))
+    C.moe_fp4_timing_reset()
+    if n:
+        kernels["fp8_gemv"] = {"launches": n, "avg_us": ms * 1e3 / n}
+    # the roofline kernel time: both launches of a step (gate/up and down share one kernel
+    # kind), from the library's HIP events on the launch stream
+    kern_us = 2 * kernels["fp8_gemv"]["avg_us"] if kernels else us
+    log(f"FP8 shared expert H{H} I{I}: {us:.2f} us per token (graph replay), kernels "
+        f"{kern_us:.2f} us, {alg / (kern_us * 1e-6) / 1e9:.0f} GB/s algorithmic")
+    peaks = None if args.no_peaks else measure_peaks(torch, C, dev)
+    achieved = alg / (kern_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "fp8_gemv (gate/up and down launches of a step)", "bytes_per_step": alg,
+                "kernel_us_per_step": round(kern_us, 3), "packed_weight_bytes": weight_bytes}
+    roofline = with_measured_peak(roofline, peaks)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import moe_oracle as O
+        x_bits = xs[:2].view(torch.int16).cpu().numpy().view(np.uint16)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.shared_expert_fp8(x_bits, *mats)
+            dt = time.perf_counter() - t0
+        cpu = {"value": 2 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"2 tokens through the FP8 shared expert (fp64 NumPy, 1 thread), {dt:.1f} s"}
+    out = {"metric": "FP8 shared-expert tokens/s at batch 1", "value": round(1e6 / us, 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(us / 1e3, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x fp8",
+           "data": "synthetic", "config": {"workload": "shared_expert_fp8_h4096_i2880", "hidden": H,
+                                            "intermediate": I, "launch": "graph"},
+           "kernels": kernels, "measured_peaks": peaks, "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
     return 0
 

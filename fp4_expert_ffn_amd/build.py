@@ -20,7 +20,8 @@ LIB_NAME = "libmoe_fp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["api.cpp", "kernels_pack.hip", "kernels_route.hip", "kernels_ffn.hip",
-           "kernels_batched.hip", "kernels_norm.hip", "kernels_probe.hip", "kernels_small_m.hip"]
+           "kernels_batched.hip", "kernels_norm.hip", "kernels_probe.hip", "kernels_small_m.hip",
+           "kernels_fp8.hip"]
 
 # Packed-fp32 VALU ops are switched off for the device code: the compiler otherwise forms
 # them from ordinary float code, and this library does not rely on them.

@@ -352,6 +352,65 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
                                        matrix, out, s));
 }
 
+size_t moe_fp4_fp8_packed_bytes(int rows, int cols) {
+  if (!valid_dim(rows) || !valid_dim(cols)) return 0;
+  return fp8_packed_bytes(rows, cols);
+}
+
+int moe_fp4_fp8_pack(const uint8_t* codes, const float* scale_inv, int rows, int cols, void* packed,
+                     size_t packed_bytes, void* stream) {
+  if (!codes || !scale_inv || !packed) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(rows) || !valid_dim(cols)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(codes) || !aligned4(scale_inv) || !aligned16(packed)) return MOE_FP4_ERR_MISALIGNED;
+  if (packed_bytes < fp8_packed_bytes(rows, cols)) return MOE_FP4_ERR_WORKSPACE;
+  return from_hip(launch_fp8_pack(codes, scale_inv, rows, cols, static_cast<uint8_t*>(packed),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_fp8_linear(const uint16_t* x, int T, const void* packed, int rows, int cols,
+                       uint16_t* y, void* stream) {
+  if (!x || !packed || !y || T < 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(rows) || !valid_dim(cols)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return MOE_FP4_ERR_MISALIGNED;
+  if (T == 0) return MOE_FP4_OK;
+  return from_hip(launch_fp8_linear(x, T, static_cast<const uint8_t*>(packed), rows, cols, y,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_fp8_swiglu(const uint16_t* x, int T, const void* gate, const void* up, int inter,
+                       int hidden, uint16_t* h, void* stream) {
+  if (!x || !gate || !up || !h || T < 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(inter) || !valid_dim(hidden)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(gate) || !aligned16(up) || !aligned16(h)) return MOE_FP4_ERR_MISALIGNED;
+  if (T == 0) return MOE_FP4_OK;
+  return from_hip(launch_fp8_swiglu(x, T, static_cast<const uint8_t*>(gate),
+                                    static_cast<const uint8_t*>(up), inter, hidden, h,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_fp4_shared_expert_workspace_bytes(int T, int inter) {
+  if (T < 0 || !valid_dim(inter)) return 0;
+  return align256((size_t)T * (size_t)inter * 2);
+}
+
+int moe_fp4_shared_expert(const uint16_t* x, int T, const void* gate, const void* up,
+                          const void* down, int hidden, int inter, uint16_t* y, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!x || !gate || !up || !down || !y || !workspace || T < 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(inter) || !valid_dim(hidden)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(gate) || !aligned16(up) || !aligned16(down) || !aligned16(y) ||
+      !aligned16(workspace))
+    return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < moe_fp4_shared_expert_workspace_bytes(T, inter)) return MOE_FP4_ERR_WORKSPACE;
+  if (T == 0) return MOE_FP4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  hipError_t e = launch_fp8_swiglu(x, T, static_cast<const uint8_t*>(gate),
+                                   static_cast<const uint8_t*>(up), inter, hidden, h, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(launch_fp8_linear(h, T, static_cast<const uint8_t*>(down), hidden, inter, y, s));
+}
+
 size_t moe_fp4_debug_act_quant_bytes(int T, int hidden) {
   if (T < 0 || !valid_dim(hidden)) return 0;
   return debug_act_quant_bytes(T, hidden);

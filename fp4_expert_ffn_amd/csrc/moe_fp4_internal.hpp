@@ -22,7 +22,7 @@ enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp
                   kKindBatchedQuant = 7, kKindBatchedGateUp = 8, kKindBatchedDown = 9,
                   kKindBatchedCombine = 10, kKindNorm = 11,
                   kKindProbeStream = 12, kKindProbeMfma = 13, kKindSmallGateUp = 14,
-                  kKindSmallDown = 15 };
+                  kKindSmallDown = 15, kKindFp8Gemv = 16 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -164,6 +164,16 @@ hipError_t launch_small_m_ffn(const uint16_t* x, const int32_t* ids, const float
 // pair rows ypair [T*k x hidden] fp32 (already weighted), rounded to bf16.
 hipError_t launch_combine_pairs(const int32_t* ids, const float* w, int T, int k, int n_experts,
                                 int hidden, const float* ypair, uint16_t* y, hipStream_t s);
+
+// Dense FP8 (E4M3) matrices [rows x cols] with one fp32 multiplier per 128 x 128 block:
+// load-time packing, y = x W^T, and the SwiGLU pair h = silu(x Wg^T) * (x Wu^T).
+size_t fp8_packed_bytes(int rows, int cols);
+hipError_t launch_fp8_pack(const uint8_t* codes, const float* scale_inv, int rows, int cols,
+                           uint8_t* packed, hipStream_t s);
+hipError_t launch_fp8_linear(const uint16_t* x, int T, const uint8_t* packed, int rows, int cols,
+                             uint16_t* y, hipStream_t s);
+hipError_t launch_fp8_swiglu(const uint16_t* x, int T, const uint8_t* gate, const uint8_t* up,
+                             int inter, int hidden, uint16_t* h, hipStream_t s);
 
 // Measurement kernels: a streaming read of `bytes` bytes, and n_workgroups x 4 wavefronts
 // each issuing iters x probe_mfma_chains() block-scaled 16x16x128 MFMAs (B FP4, A FP4 when

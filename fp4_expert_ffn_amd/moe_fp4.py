@@ -29,7 +29,7 @@ ERR_HIP = -5
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
 KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
                 "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine",
-                "norm", "probe_stream", "probe_mfma", "small_m_gate_up", "small_m_down")
+                "norm", "probe_stream", "probe_mfma", "small_m_gate_up", "small_m_down", "fp8_gemv")
 PROBE_MFMA_CHAINS = 8  # independent block-scaled MFMAs per wavefront per loop iteration
 
 
@@ -66,6 +66,12 @@ _SIGNATURES = {
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_act_quant_bytes": (ctypes.c_size_t, [_I, _I]),
+    "moe_fp4_fp8_packed_bytes": (ctypes.c_size_t, [_I, _I]),
+    "moe_fp4_fp8_pack": (_I, [_P, _P, _I, _I, _P, ctypes.c_size_t, _P]),
+    "moe_fp4_fp8_linear": (_I, [_P, _I, _P, _I, _I, _P, _P]),
+    "moe_fp4_fp8_swiglu": (_I, [_P, _I, _P, _P, _I, _I, _P, _P]),
+    "moe_fp4_shared_expert_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "moe_fp4_shared_expert": (_I, [_P, _I, _P, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]),
     "moe_fp4_debug_act_quant": (_I, [_P, _I, _I, _I, _P, ctypes.c_size_t, _P, _P]),
     "moe_fp4_debug_stream_read": (_I, [_P, _Z, _P, _P]),
     "moe_fp4_debug_mfma_loop": (_I, [_I, _I, _I, _P, _P]),
@@ -232,6 +238,37 @@ def moe_fp4_moe_forward(x, w_router, T: int, hidden: int, n_experts: int, k: int
 def moe_fp4_validate_ids(topk_ids, T: int, k: int, n_experts: int, bad_count, stream=None) -> None:
     _check(lib().moe_fp4_validate_ids(_ptr(topk_ids), T, k, n_experts, _ptr(bad_count),
                                       _stream(stream)), "moe_fp4_validate_ids")
+
+
+def moe_fp4_fp8_packed_bytes(rows: int, cols: int) -> int:
+    return lib().moe_fp4_fp8_packed_bytes(rows, cols)
+
+
+def moe_fp4_fp8_pack(codes, scale_inv, rows: int, cols: int, packed, packed_bytes: int,
+                     stream=None) -> None:
+    _check(lib().moe_fp4_fp8_pack(_ptr(codes), _ptr(scale_inv), rows, cols, _ptr(packed),
+                                  packed_bytes, _stream(stream)), "moe_fp4_fp8_pack")
+
+
+def moe_fp4_fp8_linear(x, T: int, packed, rows: int, cols: int, y, stream=None) -> None:
+    _check(lib().moe_fp4_fp8_linear(_ptr(x), T, _ptr(packed), rows, cols, _ptr(y), _stream(stream)),
+           "moe_fp4_fp8_linear")
+
+
+def moe_fp4_fp8_swiglu(x, T: int, gate, up, inter: int, hidden: int, h, stream=None) -> None:
+    _check(lib().moe_fp4_fp8_swiglu(_ptr(x), T, _ptr(gate), _ptr(up), inter, hidden, _ptr(h),
+                                    _stream(stream)), "moe_fp4_fp8_swiglu")
+
+
+def moe_fp4_shared_expert_workspace_bytes(T: int, inter: int) -> int:
+    return lib().moe_fp4_shared_expert_workspace_bytes(T, inter)
+
+
+def moe_fp4_shared_expert(x, T: int, gate, up, down, hidden: int, inter: int, y, workspace,
+                          workspace_bytes: int, stream=None) -> None:
+    _check(lib().moe_fp4_shared_expert(_ptr(x), T, _ptr(gate), _ptr(up), _ptr(down), hidden, inter,
+                                       _ptr(y), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "moe_fp4_shared_expert")
 
 
 def moe_fp4_debug_act_quant_bytes(T: int, hidden: int) -> int:

@@ -238,6 +238,48 @@ int moe_fp4_route_residual(const float* residual_in, const uint16_t* y_prev, flo
 int moe_fp4_residual_rmsnorm(float* residual, const uint16_t* y, uint16_t* x_out, int T,
                              int hidden, float eps, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Dense FP8 weights: the shared expert and the dense projections. [A100-FP4], Chinese
+ * translation, section A100 也没有 FP8: the dense weights are FP8 E4M3, kept as a storage
+ * format; they go from memory into registers and become bf16 matrix-core operands there,
+ * never expanded in memory. Format taken here: E4M3 "FN" codes (bit 7 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, 0x7F / 0xFF NaN, no infinities) of a row-major [rows x cols]
+ * matrix (out x in) with one fp32 multiplier per 128 x 128 block (row-major
+ * [ceil(rows / 128) x ceil(cols / 128)]): W[n][k] = e4m3(code) * multiplier. rows and cols
+ * are multiples of 32, at most 16384. Products are exact (E4M3 fits bf16), sums are fp32
+ * (one per 128-element chunk, scaled by its multiplier), outputs are rounded to bf16.
+ * ------------------------------------------------------------------------------------ */
+
+/* Bytes of one packed FP8 matrix (0 for an invalid shape). */
+size_t moe_fp4_fp8_packed_bytes(int rows, int cols);
+
+/* Load-time re-layout of one FP8 matrix into the tile-major order the kernels read (codes
+ * device, 16-byte aligned; scale_inv device fp32; packed device, 16-byte aligned, of
+ * moe_fp4_fp8_packed_bytes bytes). Errors: INVALID_ARG (null), BAD_SHAPE, MISALIGNED,
+ * WORKSPACE (packed_bytes too small), HIP. */
+int moe_fp4_fp8_pack(const uint8_t* codes, const float* scale_inv, int rows, int cols, void* packed,
+                     size_t packed_bytes, void* stream);
+
+/* Dense projection y [T x rows] = x [T x cols] W^T (bf16 in and out, device buffers,
+ * 16-byte aligned; packed from moe_fp4_fp8_pack). Up to four tokens share one read of the
+ * weights. T = 0 is a no-op. Errors: INVALID_ARG, BAD_SHAPE, MISALIGNED, HIP. */
+int moe_fp4_fp8_linear(const uint16_t* x, int T, const void* packed, int rows, int cols,
+                       uint16_t* y, void* stream);
+
+/* h [T x inter] = bf16(silu(x W_gate^T) * (x W_up^T)) for x [T x hidden] and packed FP8 gate
+ * and up [inter x hidden]. Errors: as moe_fp4_fp8_linear. */
+int moe_fp4_fp8_swiglu(const uint16_t* x, int T, const void* gate, const void* up, int inter,
+                       int hidden, uint16_t* h, void* stream);
+
+/* The shared expert: y [T x hidden] = W_down h with h from moe_fp4_fp8_swiglu (two launches;
+ * h goes to the workspace, moe_fp4_shared_expert_workspace_bytes(T, inter) bytes, 16-byte
+ * aligned). The caller adds y to the routed experts' output. Errors: as moe_fp4_fp8_linear,
+ * and WORKSPACE. */
+size_t moe_fp4_shared_expert_workspace_bytes(int T, int inter);
+int moe_fp4_shared_expert(const uint16_t* x, int T, const void* gate, const void* up,
+                          const void* down, int hidden, int inter, uint16_t* y, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Debug helper: counts the entries of topk_ids [T x k] outside [0, n_experts) into
  * *bad_count (a device int32 that this call overwrites). */
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,
@@ -309,7 +351,8 @@ int moe_fp4_debug_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32_t* si
 #define MOE_FP4_KERNEL_PROBE_MFMA 13   /* moe_fp4_debug_mfma_loop */
 #define MOE_FP4_KERNEL_SMALL_M_GATE_UP 14
 #define MOE_FP4_KERNEL_SMALL_M_DOWN 15
-#define MOE_FP4_KERNEL_KINDS 16
+#define MOE_FP4_KERNEL_FP8_GEMV 16     /* moe_fp4_fp8_linear, _swiglu, _shared_expert */
+#define MOE_FP4_KERNEL_KINDS 17
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

@@ -182,6 +182,18 @@ def device_expert_blobs(wl: Workload, layer: int, e0: int, e1: int, device, root
     return codes, scales
 
 
+def fp8_matrix(rows: int, cols: int, seed: int, root: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """A dense FP8 matrix: E4M3 codes [rows x cols] uniform over the 254 finite codes, and
+    one fp32 multiplier per 128 x 128 block, 2^u * (1 + v) with u uniform on the integers
+    -12 .. -6 and v uniform on [0, 1) (arbitrary fp32 values, not powers of two)."""
+    rng = np.random.default_rng(np.random.SeedSequence([root, 7000 + seed, rows, cols]))
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = finite[rng.integers(0, finite.size, size=(rows, cols))]
+    nb = ((rows + 127) // 128, (cols + 127) // 128)
+    scales = (np.exp2(rng.integers(-12, -5, size=nb)) * (1.0 + rng.random(nb))).astype(np.float32)
+    return codes, scales
+
+
 def small_workload(hidden: int, inter: int, n_experts: int, k: int, tokens: int,
                    wid: int = 100, **kw) -> Workload:
     """A reduced-size workload with the same value distributions, for parity tests."""

@@ -157,6 +157,35 @@ def test_act_quant_argument_checks(L):
     assert q(A, 0, 256, 2, A, 0, A, None) == C.OK
 
 
+def test_fp8_entry_points_argument_checks(L):
+    """Packed sizes of the FP8 matrices and the argument checks of the dense FP8 calls, none
+    of which launches work."""
+    # 2880 x 4096: 180 tiles x 32 chunks x 2 KB of codes, then 180 x 32 fp32 multipliers
+    assert L.moe_fp4_fp8_packed_bytes(2880, 4096) == 180 * 32 * 2048 + (180 * 32 * 4 + 255) // 256 * 256
+    # 4096 x 2880: K = 2880 is 22.5 chunks, padded to 23
+    assert L.moe_fp4_fp8_packed_bytes(4096, 2880) == 256 * 23 * 2048 + (256 * 23 * 4 + 255) // 256 * 256
+    assert L.moe_fp4_fp8_packed_bytes(100, 128) == 0
+    assert L.moe_fp4_fp8_packed_bytes(128, 32768) == 0
+    big = 1 << 30
+    assert L.moe_fp4_fp8_pack(None, A, 128, 128, A, big, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_fp8_pack(A, A, 130, 128, A, big, None) == C.ERR_BAD_SHAPE
+    assert L.moe_fp4_fp8_pack(MIS, A, 128, 128, A, big, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_fp8_pack(A, MIS4, 128, 128, A, big, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_fp8_pack(A, A, 128, 128, A, 1000, None) == C.ERR_WORKSPACE
+    assert L.moe_fp4_fp8_linear(A, -1, A, 128, 128, A, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_fp8_linear(A, 1, A, 128, 100, A, None) == C.ERR_BAD_SHAPE
+    assert L.moe_fp4_fp8_linear(A, 1, MIS, 128, 128, A, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_fp8_linear(A, 0, A, 128, 128, A, None) == C.OK
+    assert L.moe_fp4_fp8_swiglu(A, 1, None, A, 128, 128, A, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_fp8_swiglu(A, 0, A, A, 128, 128, A, None) == C.OK
+    assert L.moe_fp4_shared_expert_workspace_bytes(3, 2880) == (3 * 2880 * 2 + 255) // 256 * 256
+    se = L.moe_fp4_shared_expert
+    assert se(A, 3, A, A, A, 4096, 2880, A, A, 100, None) == C.ERR_WORKSPACE
+    assert se(A, 3, A, A, A, 4096, 2888, A, A, big, None) == C.ERR_BAD_SHAPE
+    assert se(A, 3, A, A, A, 4096, 2880, A, MIS, big, None) == C.ERR_MISALIGNED
+    assert se(A, 0, A, A, A, 4096, 2880, A, A, 0, None) == C.OK
+
+
 def test_timing_read_without_records(L):
     C.moe_fp4_timing_reset()
     assert C.moe_fp4_timing_read(C.KERNEL_GATE_UP) == (0, 0.0)
@@ -202,7 +231,7 @@ def test_probe_helpers_argument_checks(L):
     assert g(0, 1, (1 << 20) + 1, A, None) == C.ERR_INVALID_ARG
     assert g(4, 1, 1, MIS4, None) == C.ERR_MISALIGNED
     assert C.PROBE_MFMA_CHAINS == 8
-    assert len(C.KERNEL_NAMES) == 16
+    assert len(C.KERNEL_NAMES) == 17
 
 
 def test_route_residual_argument_checks(L):
