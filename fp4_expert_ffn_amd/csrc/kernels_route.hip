@@ -79,9 +79,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const V* __restrict__ lo
 }
 
 // ---------------------------------------------------------------------------------------
-// Batch-1 routing in one launch. Workgroup g computes the logits of experts
-// 12 g .. 12 g + 11 (two per wavefront, the x chunks shared by both rows), publishes them
-// and raises its flag; workgroup 0 then waits for every flag and selects the top-k.
+// Batch-1 routing in one launch. Workgroup g computes the logits of kRouteRowsPerWG
+// consecutive experts (kRouteKSplit wavefronts per row group, each over its part of K),
+// publishes them and raises its flag; workgroup 0 then waits for every flag and selects
+// the top-k.
 // Flags carry an epoch instead of being reset: every workgroup reads the epoch word at
 // start, flags are set to epoch + 1, and workgroup 0 stores epoch + 1 as the next call's
 // epoch once it has seen them all. No atomic read-modify-write is needed (contended
@@ -89,10 +90,24 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const V* __restrict__ lo
 // contents of the synchronisation words do not matter. The wait is bounded: after
 // kSpinLimit polls workgroup 0 proceeds, so the kernel always ends.
 // ---------------------------------------------------------------------------------------
-constexpr int kRouteRowsPerWave = 2;
-constexpr int kRouteWaves = 6;
-constexpr int kRouteRowsPerWG = kRouteRowsPerWave * kRouteWaves;
+// Launch shape, measured on MI355X (H 4096, 384 experts): more workgroups with fewer bytes
+// each shorten the GEMV; overridable at build time.
+#ifndef MOE_FP4_ROUTE_ROWS_PER_WAVE
+#define MOE_FP4_ROUTE_ROWS_PER_WAVE 1  // router rows of one wavefront
+#endif
+#ifndef MOE_FP4_ROUTE_WAVES
+#define MOE_FP4_ROUTE_WAVES 8          // wavefronts per workgroup (at least 4: the norm helpers)
+#endif
+#ifndef MOE_FP4_ROUTE_KSPLIT
+#define MOE_FP4_ROUTE_KSPLIT 4         // wavefronts sharing the K range of one row group
+#endif
+constexpr int kRouteRowsPerWave = MOE_FP4_ROUTE_ROWS_PER_WAVE;
+constexpr int kRouteWaves = MOE_FP4_ROUTE_WAVES;
+constexpr int kRouteKSplit = MOE_FP4_ROUTE_KSPLIT;
+constexpr int kRouteRowsPerWG = kRouteRowsPerWave * kRouteWaves / kRouteKSplit;
 constexpr int kRouteThreads = kRouteWaves * 64;
+static_assert(kRouteWaves >= 4 && kRouteWaves % kRouteKSplit == 0 && kRouteRowsPerWG <= 64,
+              "route launch shape");
 constexpr unsigned kSpinLimit = 1u << 22;
 
 // NIT > 0: the router input is computed here from a residual stream: r_out = r_in + y_prev
@@ -143,28 +158,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
     __syncthreads();
   }
 
-  // GEMV, fp64 accumulation of the exact bf16 x bf16 products (same order for every row)
-  const int row0 = g * kRouteRowsPerWG + wv * kRouteRowsPerWave;
+  // GEMV, fp64 accumulation of the exact bf16 x bf16 products (same order for every row).
+  // Wave wv takes rows row0 .. row0 + kRouteRowsPerWave - 1 over its part ks of the K range.
+  const int ks = wv % kRouteKSplit;
+  const int row0 = g * kRouteRowsPerWG + (wv / kRouteKSplit) * kRouteRowsPerWave;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const int chunks = H / 8;
+  const int c_beg = ks * chunks / kRouteKSplit, c_end = (ks + 1) * chunks / kRouteKSplit;
   double acc[kRouteRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRouteRowsPerWave; ++r) acc[r] = 0.0;
-  constexpr int kBatch = 8;
-  for (int c0 = lane; c0 < chunks; c0 += 64 * kBatch) {
+  constexpr int kBatch = 8 / kRouteKSplit > 0 ? 8 / kRouteKSplit : 1;
+  for (int c0 = c_beg + lane; c0 < c_end; c0 += 64 * kBatch) {
     uint4 a[kBatch], b[kRouteRowsPerWave][kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int c = c0 + u * 64;
       if constexpr (NIT > 0)
-        a[u] = (c < chunks) ? s_x[c] : make_uint4(0, 0, 0, 0);
+        a[u] = (c < c_end) ? s_x[c] : make_uint4(0, 0, 0, 0);
       else
-        a[u] = (c < chunks) ? xv[c] : make_uint4(0, 0, 0, 0);
+        a[u] = (c < c_end) ? xv[c] : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < kRouteRowsPerWave; ++r) {
         const int row = min(row0 + r, E - 1);
-        b[r][u] = (c < chunks) ? reinterpret_cast<const uint4*>(wr + (size_t)row * H)[c]
-                               : make_uint4(0, 0, 0, 0);
+        b[r][u] = (c < c_end) ? reinterpret_cast<const uint4*>(wr + (size_t)row * H)[c]
+                              : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -189,17 +207,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
   // with a relaxed agent-scope store. Workgroup 0 polls the flags with relaxed loads and
   // takes one acquire fence before reading the logits (agent-scope atomic loads would each
   // wait for completion, one after the other).
-  __shared__ double s_logit[kRouteRowsPerWG];
+  // The K parts of a row are added in ascending part order.
+  __shared__ double s_part[kRouteWaves * kRouteRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRouteRowsPerWave; ++r) {
     acc[r] = wave_sum_f64(acc[r]);
-    if (lane == 0) s_logit[wv * kRouteRowsPerWave + r] = acc[r];
+    if (lane == 0) s_part[wv * kRouteRowsPerWave + r] = acc[r];
   }
   __syncthreads();
   if (wv == 0) {
     const int row = g * kRouteRowsPerWG + lane;
-    if (lane < kRouteRowsPerWG && row < E)
-      __hip_atomic_store(&logits[row], s_logit[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < kRouteRowsPerWG && row < E) {
+      const int rg = lane / kRouteRowsPerWave, r = lane - rg * kRouteRowsPerWave;
+      double logit = s_part[rg * kRouteKSplit * kRouteRowsPerWave + r];
+#pragma unroll
+      for (int p = 1; p < kRouteKSplit; ++p)
+        logit += s_part[(rg * kRouteKSplit + p) * kRouteRowsPerWave + r];
+      __hip_atomic_store(&logits[row], logit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the logit stores are complete
     if (lane == 0) __hip_atomic_store(&sync[1 + g], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
