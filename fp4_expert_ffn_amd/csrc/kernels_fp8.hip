@@ -11,9 +11,12 @@
 // blocks past K are zero codes. Then one fp32 per (tile, chunk): the multiplier of the
 // 128 x 128 block holding that tile and chunk (a 16-row tile lies inside one 128-row block).
 //
-// GEMV kernel: a workgroup of 16 wavefronts owns one 16-row tile of each of its NMAT
-// matrices for up to MR tokens, whose rows are matrix-core rows (x staged in LDS); the
-// waves split the K chunks. A chunk's four MFMAs accumulate into a fresh register set that
+// GEMV kernel: a workgroup of 16 wavefronts owns 16 weight rows for up to MR tokens, whose
+// rows are matrix-core rows (x staged in LDS); the waves split the K chunks. With one matrix
+// the 16 rows are one tile. With two (gate and up) they are 8 rows of each: half h of a
+// tile, gate rows in MFMA columns 0-7 and the same up rows in columns 8-15. The launch then
+// has twice as many workgroups, enough to cover the compute units at the shared expert's
+// size, and SiLU(gate) * up pairs column c with c + 8. A chunk's four MFMAs accumulate into a fresh register set that
 // is then added into the running sum times the chunk's multiplier (the conversion to bf16
 // is exact, so every product is exact and only fp32 sums round).
 #include <algorithm>
@@ -26,9 +29,16 @@ namespace moe_fp4 {
 
 namespace {
 
-constexpr int kF8Waves = 16;
+// Launch shape, overridable at build time.
+#ifndef MOE_FP4_F8_WAVES
+#define MOE_FP4_F8_WAVES 16   // wavefronts per workgroup (they split K)
+#endif
+#ifndef MOE_FP4_F8_BATCH
+#define MOE_FP4_F8_BATCH 2    // chunks loaded per wave before use
+#endif
+constexpr int kF8Waves = MOE_FP4_F8_WAVES;
 constexpr int kF8Threads = kF8Waves * 64;
-constexpr int kF8Batch = 2;             // chunks loaded per wave before use
+constexpr int kF8Batch = MOE_FP4_F8_BATCH;
 constexpr int kF8LdsBytes = 32768;      // staged activation rows per workgroup
 constexpr int kF8Stage = kF8LdsBytes / (16 * kF8Threads);  // 16-byte words per thread: 2
 
@@ -107,8 +117,11 @@ __global__ __launch_bounds__(kF8Threads) void fp8_gemv_kernel(const uint16_t* __
                                                              int tiles, int nch,
                                                              uint16_t* __restrict__ out) {
   extern __shared__ uint4 smem[];
-  const int grp = blockIdx.x / tiles;
-  const int tile = blockIdx.x - grp * tiles;
+  constexpr int kUnits = NMAT == 2 ? 2 : 1;  // workgroups per 16-row tile
+  const int grp = blockIdx.x / (tiles * kUnits);
+  const int unit = blockIdx.x - grp * tiles * kUnits;
+  const int tile = unit / kUnits;
+  const int half = unit - tile * kUnits;
   const long t0 = (long)grp * MR;
   const int m = (int)min((long)MR, (long)T - t0);
   const int tid = threadIdx.x;
@@ -125,21 +138,20 @@ __global__ __launch_bounds__(kF8Threads) void fp8_gemv_kernel(const uint16_t* __
   // 2. this wave's chunks and its first batch of weights (every load issued, clamped)
   const int c_begin = wv * nch / kF8Waves;
   const int c_end = (wv + 1) * nch / kF8Waves;
-  const uint4* w0 = reinterpret_cast<const uint4*>(p0) + (size_t)tile * nch * 128;
-  const uint4* w1 = reinterpret_cast<const uint4*>(p1) + (size_t)tile * nch * 128;
-  const float* s0 = reinterpret_cast<const float*>(p0 + scales_off) + (size_t)tile * nch;
-  const float* s1 = reinterpret_cast<const float*>(p1 + scales_off) + (size_t)tile * nch;
-  uint4 a0[kF8Batch], b0[kF8Batch], a1[kF8Batch], b1[kF8Batch];
+  // this lane's matrix (column j: gate for j < 8, up for j >= 8 with two matrices) and its
+  // word (g, row) inside each 1 KB half of a (tile, chunk)
+  const bool second = NMAT == 2 && j >= 8;
+  const int wrow = NMAT == 2 ? 8 * half + (j & 7) : j;
+  const uint4* wl = reinterpret_cast<const uint4*>(second ? p1 : p0) + (size_t)tile * nch * 128 +
+                    16 * g + wrow;
+  const float* sl = reinterpret_cast<const float*>((second ? p1 : p0) + scales_off) + (size_t)tile * nch;
+  uint4 a0[kF8Batch], b0[kF8Batch];
   auto load_batch = [&](int c0) {
 #pragma unroll
     for (int q = 0; q < kF8Batch; ++q) {
       const int c = max(min(c0 + q, c_end - 1), 0);
-      a0[q] = ld_stream(w0 + (size_t)c * 128 + lane);
-      b0[q] = ld_stream(w0 + (size_t)c * 128 + 64 + lane);
-      if constexpr (NMAT == 2) {
-        a1[q] = ld_stream(w1 + (size_t)c * 128 + lane);
-        b1[q] = ld_stream(w1 + (size_t)c * 128 + 64 + lane);
-      }
+      a0[q] = ld_stream(wl + (size_t)c * 128);
+      b0[q] = ld_stream(wl + (size_t)c * 128 + 64);
     }
   };
   load_batch(c_begin);
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(kF8Threads) void fp8_gemv_kernel(const uint16_t* __
   uint32_t a_off[4];
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) a_off[ms] = (uint32_t)(rj * nx + 4 * g + (ms ^ (rj & 3))) * 16u;
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
   auto chunk = [&](int c, const uint4& lo, const uint4& hi, float sc, f32x4_t& acc) {
     const uint32_t cb = (4 * c + g < KB) ? (uint32_t)c * 256u : 0u - 64u * (uint32_t)g;
     const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -171,35 +183,31 @@ __global__ __launch_bounds__(kF8Threads) void fp8_gemv_kernel(const uint16_t* __
     for (int q = 0; q < kF8Batch; ++q) {
       const int c = c0 + q;
       if (c < c_end) {  // wave-uniform
-        chunk(c, a0[q], b0[q], s0[c], acc0);
-        if constexpr (NMAT == 2) chunk(c, a1[q], b1[q], s1[c], acc1);
+        chunk(c, a0[q], b0[q], sl[c], acc0);
       }
     }
     if (c0 + kF8Batch < c_end) load_batch(c0 + kF8Batch);
   }
 
-  // 3. partial sums over the staged rows' LDS: [matrix][wave][row][column]
+  // 3. partial sums over the staged rows' LDS: [wave][row][column]
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
-  constexpr int kRed = kF8Waves * MR * 16;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 4 * g + q;  // accumulator element q: row 4 (lane / 16) + q, column lane % 16
-    if (r < m) {
-      red[(wv * MR + r) * 16 + j] = acc0[q];
-      if constexpr (NMAT == 2) red[kRed + (wv * MR + r) * 16 + j] = acc1[q];
-    }
+    if (r < m) red[(wv * MR + r) * 16 + j] = acc0[q];
   }
   __syncthreads();
-  if (tid < MR * 16) {
-    const int r = tid / 16, c = tid % 16;
-    const int n = 16 * tile + c;
+  constexpr int kCols = 16 / kUnits;  // outputs per token: 16 rows, or 8 (gate, up) pairs
+  if (tid < MR * kCols) {
+    const int r = tid / kCols, c = tid % kCols;
+    const int n = 16 * tile + kCols * half + c;
     if (r < m && n < N) {
       float v0 = 0.f, v1 = 0.f;
 #pragma unroll
       for (int w = 0; w < kF8Waves; ++w) {
         v0 += red[(w * MR + r) * 16 + c];
-        if constexpr (NMAT == 2) v1 += red[kRed + (w * MR + r) * 16 + c];
+        if constexpr (NMAT == 2) v1 += red[(w * MR + r) * 16 + c + 8];
       }
       const float v = NMAT == 2 ? silu_f32(v0) * v1 : v0;
       out[(size_t)(t0 + r) * N + n] = f32_to_bf16_rne(v);
@@ -220,9 +228,9 @@ hipError_t fp8_gemv_launch(const uint16_t* x, int T, int K, int N, const uint8_t
                            const uint8_t* p1, uint16_t* out, hipStream_t s) {
   const Fp8Layout L = fp8_layout(N, K);
   const long groups = (T + MR - 1) / MR;
-  const long grid = groups * L.tiles;
+  const long grid = groups * L.tiles * NMAT;  // two matrices: a workgroup per half tile
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-  const uint32_t lds = (uint32_t)std::max(MR * (K / 8) * 16, NMAT * kF8Waves * MR * 16 * 4);
+  const uint32_t lds = (uint32_t)std::max(MR * (K / 8) * 16, kF8Waves * MR * 16 * 4);
   return launch_kernel(kKindFp8Gemv, fp8_gemv_kernel<NMAT, MR>, dim3((unsigned)grid),
                        dim3(kF8Threads), lds, s, x, T, K, N, p0, p1, L.scales_off, L.tiles, L.nch,
                        out);
