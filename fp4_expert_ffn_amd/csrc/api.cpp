@@ -113,8 +113,9 @@ int moe_fp4_pack(const uint8_t* codes, const uint8_t* scales, int n_experts, int
                                             static_cast<uint8_t*>(packed), s)));
 }
 
-// Route workspace: a 4 KB synchronisation area (kept between calls), then fp64 logits.
-constexpr size_t kRouteSyncBytes = 4096;
+// Route workspace: a 16 KB synchronisation area (kept between calls: the epoch word and one
+// 16-byte logit record per expert for the batch-1 kernel), then fp64 logits.
+constexpr size_t kRouteSyncBytes = 16384;
 
 size_t moe_fp4_route_workspace_bytes(int T, int n_experts) {
   if (T < 0 || n_experts <= 0) return 0;

@@ -80,15 +80,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const V* __restrict__ lo
 
 // ---------------------------------------------------------------------------------------
 // Batch-1 routing in one launch. Workgroup g computes the logits of kRouteRowsPerWG
-// consecutive experts (kRouteKSplit wavefronts per row group, each over its part of K),
-// publishes them and raises its flag; workgroup 0 then waits for every flag and selects
-// the top-k.
-// Flags carry an epoch instead of being reset: every workgroup reads the epoch word at
-// start, flags are set to epoch + 1, and workgroup 0 stores epoch + 1 as the next call's
-// epoch once it has seen them all. No atomic read-modify-write is needed (contended
-// atomics across the eight XCDs cost tens of microseconds at this width), and the initial
-// contents of the synchronisation words do not matter. The wait is bounded: after
-// kSpinLimit polls workgroup 0 proceeds, so the kernel always ends.
+// consecutive experts (kRouteKSplit wavefronts per row group, each over its part of K) and
+// publishes each as a self-checking record: its fp64 bits and those bits XOR a key derived
+// from the call's epoch. Workgroup 0 polls the records themselves with agent-coherent
+// loads until every check word matches its value, so the logits arrive with the
+// readiness test (no flag round trip, then no reload), and selects the top-k. A record
+// read half old and half new fails the check, as does one left by an earlier call.
+// The epoch is not reset: every workgroup reads the epoch word at start, and workgroup 0
+// stores epoch + 1 as the next call's epoch once it has seen every record (so every
+// workgroup has read it). No atomic read-modify-write is needed (contended atomics across
+// the eight XCDs cost tens of microseconds at this width), and the initial contents of the
+// synchronisation words do not matter. The wait is bounded: after kSpinLimit polls
+// workgroup 0 proceeds, so the kernel always ends.
 // ---------------------------------------------------------------------------------------
 // Launch shape, measured on MI355X (H 4096, 384 experts): more workgroups with fewer bytes
 // each shorten the GEMV; overridable at build time.
@@ -109,6 +112,25 @@ constexpr int kRouteThreads = kRouteWaves * 64;
 static_assert(kRouteWaves >= 4 && kRouteWaves % kRouteKSplit == 0 && kRouteRowsPerWG <= 64,
               "route launch shape");
 constexpr unsigned kSpinLimit = 1u << 22;
+constexpr int kRouteRecOffset = 16;  // sync words before the logit records (64 bytes)
+
+// Epoch -> record key (the splitmix64 finaliser: consecutive epochs give unrelated keys).
+__device__ __forceinline__ uint64_t route_record_key(uint32_t epoch) {
+  uint64_t z = (uint64_t)epoch + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+typedef unsigned route_u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte record read at the agent-coherent level (the form of an agent-scope atomic
+// load), waited for at once.
+__device__ __forceinline__ route_u32x4 ld_record(const uint64_t* p) {
+  route_u32x4 v;
+  __asm__ volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
 
 // NIT > 0: the router input is computed here from a residual stream: r_out = r_in + y_prev
 // and x = bf16(r_out / rms) (the shared row helpers, so the bits equal the standalone norm
@@ -126,6 +148,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const uint32_t target = sync[0] + 1u;
+  const uint64_t key = route_record_key(target);
+  uint64_t* rec = reinterpret_cast<uint64_t*>(sync + kRouteRecOffset);
 
   extern __shared__ uint4 s_x[];  // NIT > 0: the normalised row, H / 8 words
   if constexpr (NIT > 0) {
@@ -223,26 +247,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
 #pragma unroll
       for (int p = 1; p < kRouteKSplit; ++p)
         logit += s_part[(rg * kRouteKSplit + p) * kRouteRowsPerWave + r];
-      __hip_atomic_store(&logits[row], logit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t vb = (uint64_t)__double_as_longlong(logit);
+      __hip_atomic_store(&rec[2 * row], vb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&rec[2 * row + 1], vb ^ key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the logit stores are complete
-    if (lane == 0) __hip_atomic_store(&sync[1 + g], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (g != 0) return;
 
-  for (int f = tid; f < G; f += kRouteThreads) {
+  // workgroup 0: every record, checked, into LDS for the selection
+  __shared__ double s_lg[64 * PER];
+  for (int f = tid; f < E; f += kRouteThreads) {
     unsigned n = 0;
-    while (__hip_atomic_load(&sync[1 + f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target) {
+    uint64_t vb;
+    while (true) {
+      const route_u32x4 r = ld_record(&rec[2 * f]);
+      vb = ((uint64_t)r.y << 32) | r.x;
+      const uint64_t ck = ((uint64_t)r.w << 32) | r.z;
+      if (ck == (vb ^ key)) break;
       __builtin_amdgcn_s_sleep(1);
       if (++n > kSpinLimit) break;
     }
+    s_lg[f] = __longlong_as_double((long long)vb);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   if (wv == 0) {
     int sid[8];
     float sw[8];
-    wave_topk<PER>(logits, E, k, lane, sid, sw);
+    wave_topk<PER>(s_lg, E, k, lane, sid, sw);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k && lane == j) {
@@ -342,7 +373,7 @@ hipError_t launch_route_decode_norm(const float* r_in, const uint16_t* y_prev, f
 }
 
 int route_decode_sync_words(int n_experts) {
-  return 1 + (n_experts + kRouteRowsPerWG - 1) / kRouteRowsPerWG;
+  return kRouteRecOffset + 4 * n_experts;  // the epoch word, then a 16-byte record per expert
 }
 
 hipError_t launch_topk_f64(const double* logits, int T, int n_experts, int k, int32_t* ids,

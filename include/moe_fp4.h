@@ -100,7 +100,7 @@ size_t moe_fp4_route_workspace_bytes(int T, int n_experts);
 
 /* x [T x hidden] bf16, w_router [n_experts x hidden] bf16 (row-major), outputs
  * topk_ids int32 [T x k], topk_w fp32 [T x k]. workspace: device scratch of at least
- * moe_fp4_route_workspace_bytes(T, n_experts) bytes, owned by the caller. Its first 4 KB
+ * moe_fp4_route_workspace_bytes(T, n_experts) bytes, owned by the caller. Its first 16 KB
  * hold synchronisation words that a batch-1 call (T == 1: GEMV and selection in one
  * launch) carries from call to call; their initial contents do not matter, the caller
  * must not write them between calls, and calls that may run concurrently need distinct
@@ -190,7 +190,7 @@ int moe_fp4_expert_ffn_ex(const uint16_t* x, const int32_t* topk_ids, const floa
  * topk_w receive the routing (bit-identical to moe_fp4_route), y the layer output
  * (bit-identical to moe_fp4_expert_ffn). Cutting launches per layer is the pages' own
  * lesson ([A100-FP4], section 然后又发现每 token 启动 2000 次内核). The workspace's first
- * 4 KB follow the rules given for moe_fp4_route.
+ * 16 KB follow the rules given for moe_fp4_route.
  * ------------------------------------------------------------------------------------ */
 
 /* Workspace bytes moe_fp4_moe_forward needs. */
@@ -227,7 +227,7 @@ int moe_fp4_residual_init(const uint16_t* x, float* residual, int T, int hidden,
  * a decode step goes away ([A100-FP4], section 然后又发现每 token 启动 2000 次内核: per-token
  * launches cost more than their math). residual_in, residual_out [T x hidden] fp32 must not
  * overlap; y_prev, x_out [T x hidden] bf16; eps >= 0 and finite; the workspace as for
- * moe_fp4_route (its first 4 KB carry the synchronisation words between calls). hidden % 32
+ * moe_fp4_route (its first 16 KB carry the synchronisation words between calls). hidden % 32
  * == 0 and <= 16384; 16-byte alignment except topk_ids / topk_w (4).
  * Errors: INVALID_ARG (null, eps, overlap, T / k / n_experts as moe_fp4_route), BAD_SHAPE,
  * MISALIGNED, WORKSPACE, HIP. */
