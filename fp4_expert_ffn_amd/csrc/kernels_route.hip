@@ -139,7 +139,7 @@ __device__ __forceinline__ route_u32x4 ld_record(const uint64_t* p) {
 template <int PER, int NIT>
 __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int H, int E, int k,
-    uint32_t* __restrict__ sync, double* __restrict__ logits, int32_t* __restrict__ ids,
+    uint32_t* __restrict__ sync, int32_t* __restrict__ ids,
     float* __restrict__ w, const float* __restrict__ r_in, const uint16_t* __restrict__ y_prev,
     float* __restrict__ r_out, uint16_t* __restrict__ x_out, float eps) {
   const int G = gridDim.x;
@@ -225,13 +225,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
       }
     }
   }
-  // The workgroup's logits go through LDS to wave 0. It stores them with relaxed
-  // agent-scope atomic stores (written through to the agent-coherent level, so no L2
-  // write-back fence is needed), waits until they are acknowledged, then raises the flag
-  // with a relaxed agent-scope store. Workgroup 0 polls the flags with relaxed loads and
-  // takes one acquire fence before reading the logits (agent-scope atomic loads would each
-  // wait for completion, one after the other).
-  // The K parts of a row are added in ascending part order.
+  // The workgroup's logits go through LDS to wave 0, which writes each one's record with
+  // relaxed agent-scope atomic stores (written through to the agent-coherent level, so no
+  // L2 write-back fence is needed). The K parts of a row are added in ascending part order.
   __shared__ double s_part[kRouteWaves * kRouteRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRouteRowsPerWave; ++r) {
@@ -334,12 +330,13 @@ hipError_t route_decode_launch(const uint16_t* x, const uint16_t* wr, int hidden
                                int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
                                const float* r_in, const uint16_t* y_prev, float* r_out,
                                uint16_t* x_out, float eps, hipStream_t s) {
+  (void)logits;  // the batch-1 kernel keeps its logits in the records of the sync area
   const dim3 grid((unsigned)((n_experts + kRouteRowsPerWG - 1) / kRouteRowsPerWG)), block(kRouteThreads);
   const uint32_t lds = NIT > 0 ? (uint32_t)hidden * 2u : 0u;
   const int per = (n_experts + 63) / 64;
 #define MOE_FP4_ROUTE_LAUNCH(P)                                                                   \
   return launch_kernel(kKindRouteDecode, route_decode_kernel<P, NIT>, grid, block, lds, s, x, wr,  \
-                       hidden, n_experts, k, sync, logits, ids, w, r_in, y_prev, r_out, x_out, eps)
+                       hidden, n_experts, k, sync, ids, w, r_in, y_prev, r_out, x_out, eps)
   if (per <= 2) MOE_FP4_ROUTE_LAUNCH(2);
   if (per <= 4) MOE_FP4_ROUTE_LAUNCH(4);
   if (per <= 6) MOE_FP4_ROUTE_LAUNCH(6);
