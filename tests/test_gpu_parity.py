@@ -203,6 +203,31 @@ def test_route_batch1_sequence(dev, n_experts, k):
             assert list(ids_ref[0][:2]) == [3, n_experts - 1]
 
 
+@pytest.mark.parametrize("n_experts", [1020, 1021])
+def test_route_batch1_record_area_edge(dev, n_experts):
+    """The one-launch batch-1 route keeps one 16-byte logit record per expert in the route
+    workspace's synchronisation area: 1020 experts are the most it holds, 1021 take the
+    two-launch route. Both must match the oracle over consecutive calls on one workspace,
+    including a token with an exact tie between the first and the last expert."""
+    C, D = _mods()
+    k = 6
+    wl = S.small_workload(4096, 128, n_experts, k, 1, wid=920)
+    wr_bits = S.router_weights(wl, 0).copy()
+    wr_bits[n_experts - 1] = wr_bits[0]
+    layer = D.MoeFp4Layer(torch.empty(256, dtype=torch.uint8, device=dev), n_experts,
+                          wl.hidden, wl.inter, k, D.upload_bf16(wr_bits, dev))
+    for step in range(6):
+        x_bits = S.activations(wl, 0, step)
+        if step == 3:
+            x_bits = wr_bits[0:1].copy()
+        ids_ref, w_ref, _ = O.route(x_bits, wr_bits, k)
+        ids, w = layer.route(D.upload_bf16(x_bits, dev))
+        torch.cuda.synchronize()
+        check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"E {n_experts} step {step}")
+        if step == 3:
+            assert list(ids_ref[0][:2]) == [0, n_experts - 1]
+
+
 @pytest.mark.parametrize("routing", ["zipf", "uniform", "ties"])
 def test_route_logits_bit_exact(dev, routing):
     C, D = _mods()
