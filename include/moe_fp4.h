@@ -297,8 +297,10 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
  * decoded back to fp32 out [T x hidden] (device): per 32-element block, one or two MXFP8
  * E4M3 terms (hi, then lo = the same quantisation of x - hi) with one ue8m0 scale each, the
  * scale the smallest power of two that fits the block's maximum in 448, codes rounded to
- * nearest with ties to the even code (OCP MX; [8GB-GPU], section RTX 50xx 上的三个从不抛错的
- * Bug: ue8m0-scaled FP8 activations). terms 2: the GROUPED path's operand; terms 1: the
+ * nearest with ties to the even code ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug:
+ * ue8m0-scaled FP8 activations). This scale rule is the library's own reading, not the OCP
+ * MX one (2^(floor(log2 max) - 8) with clipping): where the block maximum's significand
+ * exceeds 1.75 it takes the next power of two, so no element is clipped. terms 2: the GROUPED path's operand; terms 1: the
  * GROUPED_FP8 path's. out is the exact sum of the decoded terms. workspace:
  * moe_fp4_debug_act_quant_bytes(T, hidden) bytes of device memory, 16-byte aligned, contents
  * irrelevant. Errors: INVALID_ARG (null pointer, T < 0, terms not 1 or 2), BAD_SHAPE,

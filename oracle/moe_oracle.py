@@ -313,9 +313,14 @@ def moe_layer(x_bits: np.ndarray, w_router_bits: np.ndarray, k: int, expert_sour
 # 5. MX activation formats: the reading taken for activations that enter block-scaled
 #    matrix cores. DeepSeek quantises activations to FP8 with ue8m0 block scales
 #    ([8GB-GPU], RTX 50xx 上的三个从不抛错的 Bug names the act_quant step and its ue8m0 format);
-#    the pages give no block size or rounding, so this follows the OCP MX definition:
-#    blocks of 32 along K, one power-of-two scale 2^X per block, elements rounded to the
-#    nearest value of the element format with ties to the even code.
+#    the pages give no block size, scale rule or rounding. The reading taken here: blocks of
+#    32 along K, one power-of-two scale 2^X per block, X the SMALLEST integer with
+#    max|v| <= vmax * 2^X (vmax the element format's largest value), elements rounded to the
+#    nearest value of the element format with ties to the even code. This scale rule is this
+#    project's own choice, not the OCP MX v1.0 one: OCP takes X = floor(log2(max|v|)) - emax
+#    (emax = 8 for E4M3) and saturates the elements that then exceed vmax. The two agree
+#    unless the block maximum's significand exceeds vmax's (1.75 for E4M3, 1.875 for E2M3,
+#    1.5 for E2M1); there this rule picks X one larger, so no element is ever clipped.
 # ---------------------------------------------------------------------------------------
 
 #: element formats: (exponent bits, mantissa bits, exponent bias, largest finite value)
@@ -356,7 +361,8 @@ def mx_round(v: np.ndarray, fmt: str) -> np.ndarray:
 
 def mx_scale_exponent(amax: float, vmax: float) -> int:
     """Smallest integer X with amax <= vmax * 2^X, clamped to the ue8m0 range [-127, 127];
-    amax == 0 gives -127."""
+    amax == 0 gives -127. (This project's scale rule; see the section note: it is one larger
+    than the OCP MX rule's exponent when amax's significand exceeds vmax's.)"""
     if amax == 0.0:
         return -127
     x = math.frexp(amax)[1] - math.frexp(vmax)[1] - 1

@@ -501,3 +501,164 @@ def test_shared_expert_fp8_reduces_to_the_routed_expert_oracle():
     y4 = O.expert_ffn(x_bits, np.zeros((3, 1), np.int32), np.ones((3, 1)), S.expert_source(wl),
                       1, wl.hidden, wl.inter)
     assert np.array_equal(y8, y4)
+
+
+# ------------------------------------------------------------------ MX oracle mode: hand values
+
+def _signed_identity_expert(H, I):
+    """gate = +identity [I x H], up = -identity (code 0b1010 = -1.0), down = +identity
+    [H x I], every scale byte 127: with inputs q >= 38 (where silu(q) == q exactly in fp64,
+    since exp(-38) is below half an ulp of 1.0) the expert gives h = -q * q exactly."""
+    def mat(rows, k, code):
+        c = np.zeros((rows, k // 2), dtype=np.uint8)
+        for r in range(min(rows, k)):
+            byte_idx, hi = divmod(r, 2)
+            c[r, byte_idx] |= (code << 4) if hi else code
+        return c, np.full((rows, k // 32), 127, dtype=np.uint8)
+    parts = [mat(I, H, 0x2), mat(I, H, 0xA), mat(H, I, 0x2)]
+    return (np.concatenate([p[0].ravel() for p in parts]),
+            np.concatenate([p[1].ravel() for p in parts]))
+
+
+# One 32-block of x, every value exact in bf16 and >= 38. Its maximum 61 = 1.90625 * 2^5 has
+# a significand above 1.75, so the scale rule matters: the smallest X with 61 <= 448 * 2^X is
+# X = -2 (448 / 8 = 56 < 61), so x / 2^X = 4x is rounded on the E4M3 grid (step 16 on
+# [128, 256)). The OCP MX rule would take X = -3 and clip 488 to 448 (q = 56, not 60).
+_X_BLOCK = [61, 40, 41, 42, 43, 44, 46, 50, 54, 60.5, 38, 39, 58, 48, 56, 52,
+            45, 47, 49, 51, 53, 55, 57, 59, 38.5, 40.5, 44.5, 48.5, 52.5, 56.5, 60, 47.5]
+# 4x -> nearest grid value, ties to the even mantissa:
+#   244->240, 160, 164->160, 168->160 (tie: 160 is m=2), 172->176, 176, 184->192 (tie: m=4),
+#   200->192 (tie: m=4), 216->224 (tie: m=6), 242->240, 152->160 (tie: m=2), 156->160,
+#   232->224 (tie: m=6), 192, 224, 208, 180->176, 188->192, 196->192, 204->208, 212->208,
+#   220->224, 228->224, 236->240, 154->160, 162->160, 178->176, 194->192, 210->208,
+#   226->224, 240, 190->192; divided by 4:
+_Q_BLOCK = [60, 40, 40, 40, 44, 44, 48, 48, 56, 60, 40, 40, 56, 48, 56, 52,
+            44, 48, 48, 52, 52, 56, 56, 60, 40, 40, 44, 48, 52, 56, 60, 48]
+# h = -q^2 over I: squares 3600, 1600, 1936, 2304, 2704, 3136. Block maximum 3600 =
+# 1.7578 * 2^11 (again above 1.75): X = 4 (448 * 8 = 3584 < 3600). |h| / 16 on the grid:
+# 225->224, 100->96 (tie between 96 = m4 and 104 = m5), 121->120, 144, 169->176, 196->192;
+# times 16:
+_HQ = {3600: 3584, 1600: 1536, 1936: 1920, 2304: 2304, 2704: 2816, 3136: 3072}
+
+
+def test_expert_ffn_mx_one_term_hand_derived():
+    """The one-term MX oracle mode on a signed identity expert: x is quantised per 32-block
+    with the scale rule above, h = -q^2 is quantised again along I before the down
+    projection; every value worked by hand. Catches an unquantised x or h, the OCP scale
+    rule (elements 0, 9, 23, 30 would give 56 instead of 60) and a wrong rounding tie."""
+    H = I = 32
+    codes, scales = _signed_identity_expert(H, I)
+    x = O.f64_to_bf16_bits(np.array([_X_BLOCK], dtype=np.float64))
+    assert np.array_equal(O.bf16_to_f64(x)[0], _X_BLOCK)  # every value exact in bf16
+    y = O.expert_ffn_mx(x, np.zeros((1, 1), np.int32), np.ones((1, 1)), lambda e: (codes, scales),
+                        1, H, I, "e4m3", 1)
+    expect = [-_HQ[q * q] for q in _Q_BLOCK]
+    assert y[0].tolist() == expect
+
+
+# A sparse block for the two-term case: x = [61, 41, 50, 60.5, 0 ...].
+#  x hi: 60, 40, 48, 60 (as above); residual 1, 1, 2, 0.5 has maximum 2, X = -7 (3.5 >= 2 >
+#  1.75), 2^7 r = 128, 128, 256, 64 all on the grid: x is reproduced exactly, so h = -x^2 =
+#  -3721, -1681, -2500, -3660.25.
+#  h hi: X = 4 (3721 > 3584); |h| / 16 = 232.5625 -> 240, 105.0625 -> 104, 156.25 -> 160,
+#  228.765625 -> 224: hi = -3840, -1664, -2560, -3584.
+#  h lo: residual 119, -17, 60, -76.25, maximum 119, X = -1 (112 < 119 <= 224); times 2:
+#  238 -> 240, -34 -> -32 (tie between 32 = m0 and 36 = m1), 120, -152.5 -> -160: lo = 120,
+#  -16, 60, -80. h = hi + lo = -3720, -1680, -2500, -3664.
+#  One term: q = 60, 40, 48, 60, h = -3600, -1600, -2304, -3600 -> -3584, -1536, -2304, -3584.
+_SPARSE_X = [61, 41, 50, 60.5]
+_SPARSE_Y = {1: [-3584, -1536, -2304, -3584], 2: [-3720, -1680, -2500, -3664]}
+
+
+@pytest.mark.parametrize("terms", [1, 2])
+def test_expert_ffn_mx_blocks_and_tokens_get_their_own_scales(terms):
+    """Two tokens, H = I = 64: token t holds the sparse block A in its first 32-block times
+    2^(20 t) and in its second times 2^(20 t + 20). Each 32-block along K (x) and along I (h)
+    of each token has its own scale, and power-of-two factors commute with the rounding, so
+    y of block b of token t is the hand-derived block result times 2^(40 (t + b)). A scale
+    shared across the two blocks, or blocks running along the token axis, would flush the
+    smaller block to zero (2^-20 lies below E4M3's smallest subnormal relative to 448)."""
+    H = I = 64
+    codes, scales = _signed_identity_expert(H, I)
+    blk = np.zeros(32)
+    blk[:4] = _SPARSE_X
+    x = np.stack([np.concatenate([blk * 2.0 ** (20 * t), blk * 2.0 ** (20 * t + 20)]) for t in range(2)])
+    xb = O.f64_to_bf16_bits(x)
+    assert np.array_equal(O.bf16_to_f64(xb), x)
+    y = O.expert_ffn_mx(xb, np.zeros((2, 1), np.int32), np.ones((2, 1)), lambda e: (codes, scales),
+                        1, H, I, "e4m3", terms)
+    for t in range(2):
+        for b in range(2):
+            expect = np.zeros(32)
+            expect[:4] = np.array(_SPARSE_Y[terms]) * 2.0 ** (40 * (t + b))
+            assert np.array_equal(y[t, 32 * b:32 * b + 32], expect), (t, b)
+
+
+def test_expert_ffn_mx_slot_weights_and_invalid_ids():
+    """The MX mode keeps the combine of the exact mode: weights scale each pair's result,
+    duplicate ids add, ids outside [0, E) contribute nothing (hand values from the sparse
+    block, one term)."""
+    H = I = 32
+    codes, scales = _signed_identity_expert(H, I)
+    blk = np.zeros(32)
+    blk[:4] = _SPARSE_X
+    xb = O.f64_to_bf16_bits(blk[None, :])
+    ids = np.array([[0, 0, 1, -1]], np.int32)
+    w = np.array([[0.5, 0.25, 9.0, 9.0]])
+    y = O.expert_ffn_mx(xb, ids, w, lambda e: (codes, scales), 1, H, I, "e4m3", 1)
+    assert y[0, :4].tolist() == [0.75 * v for v in _SPARSE_Y[1]]
+    assert np.all(y[0, 4:] == 0.0)
+
+
+# ------------------------------------------------------------------ dense FP8: one-hot columns
+
+def test_dense_fp8_one_hot_columns_hand_values():
+    """y = x W^T with x one-hot selects one column of W, times the input value: each element
+    is e4m3(code) times the multiplier of its own (row block, column block). W is 200 x 300
+    (row blocks 128 + 72, column blocks 128 + 128 + 44); token 0 is 2.0 at column 130
+    (column block 1), token 1 is -1.0 at column 5 (column block 0). A transposed product or
+    a multiplier indexed [column block, row block] fails."""
+    n, k = 200, 300
+    codes = np.full((n, k), 0x3A, dtype=np.uint8)           # 1.25 everywhere else
+    mult = np.array([[0.5, 3.0, 0.25], [1.5, 10.0, 0.125]], dtype=np.float32)
+    col = {0: 0x38, 127: 0x40, 128: 0xC4, 199: 0x7E, 5: 0x01, 6: 0x00}  # 1, 2, -3, 448, 2^-9, 0
+    for r, c in col.items():
+        codes[r, 130] = c
+    codes[:, 5] = 0x38                                      # column 5: all 1.0
+    codes[150, 5] = 0xB8                                    # -1.0
+    x = np.zeros((2, k))
+    x[0, 130] = 2.0
+    x[1, 5] = -1.0
+    y = O.dense_fp8(O.f64_to_bf16_bits(x), codes, mult)
+    # token 0: 2 * value * mult[row block, 1]
+    assert y[0, 0] == 2 * 1.0 * 3.0
+    assert y[0, 127] == 2 * 2.0 * 3.0
+    assert y[0, 128] == 2 * -3.0 * 10.0
+    assert y[0, 199] == 2 * 448.0 * 10.0
+    assert y[0, 5] == 2 * 2.0 ** -9 * 3.0
+    assert y[0, 6] == 0.0
+    assert y[0, 1] == 2 * 1.25 * 3.0 and y[0, 150] == 2 * 1.25 * 10.0
+    # token 1: -1 * value * mult[row block, 0]
+    assert y[1, 0] == -0.5 and y[1, 127] == -0.5
+    assert y[1, 128] == -1.5 and y[1, 150] == 1.5 and y[1, 199] == -1.5
+
+
+# ------------------------------------------------------------------ the parity checkers
+
+def test_cosine_hand_values():
+    assert O.cosine([1.0, 0.0], [0.0, 1.0]) == 0.0                 # orthogonal
+    assert O.cosine([1.0, 2.0, 3.0], [2.0, 4.0, 6.0]) == pytest.approx(1.0, abs=1e-15)
+    assert O.cosine([1.0, 2.0], [-1.0, -2.0]) == pytest.approx(-1.0, abs=1e-15)
+    assert O.cosine([3.0, 4.0], [4.0, 3.0]) == pytest.approx(24.0 / 25.0, abs=1e-15)
+    assert O.cosine([0.0, 0.0], [0.0, 0.0]) == 1.0                 # both zero: equal
+    assert O.cosine([0.0, 0.0], [1.0, 2.0]) == 0.0                 # one zero
+    assert O.cosine([[1.0, 0.0], [0.0, 1.0]], [[1.0, 0.0], [0.0, 1.0]]) == pytest.approx(1.0, abs=1e-15)
+
+
+def test_normwise_rel_err_hand_values():
+    assert O.normwise_rel_err([1.0, 2.0], [1.0, 4.0]) == 0.5       # max |diff| 2 / max |ref| 4
+    assert O.normwise_rel_err([-7.0, 2.0], [-8.0, 2.0]) == 0.125   # signs: |ref| max is 8
+    assert O.normwise_rel_err([3.0, -1.0], [2.0, -4.0]) == 0.75    # max diff 3 at another index
+    assert O.normwise_rel_err([5.0, 5.0], [5.0, 5.0]) == 0.0
+    assert O.normwise_rel_err([0.0], [0.0]) == 0.0                 # zero reference, zero output
+    assert O.normwise_rel_err([1.0], [0.0]) == math.inf            # zero reference, non-zero
