@@ -26,6 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix cores, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 (the f8f6f4 MFMA's rate with an FP8 operand)
 
 
 def log(msg: str) -> None:
@@ -77,6 +79,38 @@ def measured_traffic(kernel: str, workload: str = ""):
     return None
 
 
+TRACE_SUMMARIES = {"gate_up_kernel": os.path.join(ROOT, "profiles", "decode_layer_kernel_trace.md")}
+
+
+def traced_avg_us(kernel: str):
+    """Average duration (us) of `kernel` in the committed rocprofv3 kernel-trace summary of
+    the default bench command, or None when the summary is missing or was taken on another
+    version of the kernel's source (its recorded sha256/16 differs)."""
+    import hashlib
+    import re
+
+    try:
+        text = open(TRACE_SUMMARIES[kernel]).read()
+        src_name = KERNEL_SOURCES[kernel]
+        digest = hashlib.sha256(open(os.path.join(ROOT, "fp4_expert_ffn_amd", "csrc", src_name),
+                                     "rb").read()).hexdigest()[:16]
+    except (OSError, KeyError):
+        return None
+    if f"{src_name} sha256/16 {digest}" not in text:
+        return None
+    m = re.search(r"\|\s*`" + re.escape(kernel) + r"<[^`]*>`\s*\|\s*\d+\s*\|\s*(\d+)\s*\|", text)
+    return int(m.group(1)) / 1e3 if m else None
+
+
+def host_cpu_info() -> dict:
+    """The host cores this process may run on and the BLAS thread pools NumPy would use."""
+    from threadpoolctl import threadpool_info
+
+    blas = [{"api": d.get("internal_api"), "threads": d.get("num_threads")}
+            for d in threadpool_info() if d.get("user_api") == "blas"]
+    return {"host_cores_available": len(os.sched_getaffinity(0)), "blas_default_threads": blas}
+
+
 def cpu_baseline(wl, n_tokens: int, first_step: int):
     """Time the fp64 oracle (route + expert FFN) on the host for a bounded sample of the
     same workload: n_tokens tokens, one BLAS thread."""
@@ -98,9 +132,11 @@ def cpu_baseline(wl, n_tokens: int, first_step: int):
             ids, w, _ = O.route(x, wr, wl.k)
             O.expert_ffn(x, ids, w, src, wl.n_experts, wl.hidden, wl.inter)
         dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tokens} tokens of the same one-layer batch-1 decode workload "
-                      f"(route + expert FFN, fp64 NumPy, 1 thread), {dt:.1f} s"}
+    out = {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n_tokens} tokens of the same one-layer batch-1 decode workload "
+                     f"(route + expert FFN, fp64 NumPy, BLAS limited to 1 thread), {dt:.1f} s"}
+    out.update(host_cpu_info())
+    return out
 
 
 def measure_peaks(torch, C, dev) -> dict:
@@ -193,6 +229,8 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batched (grouped GEMM) half of the metric in the decode run")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-peak probes (streaming read, matrix-core loop)")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -323,13 +361,32 @@ def main() -> int:
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                         "traffic": measured_traffic("gate_up_kernel"), "kernel": "gate_up",
                         "bytes_per_launch": alg,
-                        "avg_launch_us": round(gu["avg_us"], 3)}
+                        "avg_launch_us": round(gu["avg_us"], 3),
+                        "avg_launch_us_source": "library HIP events on the launch stream, "
+                                                "stamped with the dispatch's start and end"}
+            tr = traced_avg_us("gate_up_kernel")
+            if tr:
+                roofline["trace_avg_launch_us"] = tr
+                roofline["trace_frac"] = round(alg / (tr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                roofline["trace_source"] = "profiles/decode_layer_kernel_trace.md (rocprofv3 --kernel-trace --stats)"
         log("kernels: " + json.dumps(kernels))
 
     pct = step_percentiles(torch, step, range(W + K, W + 2 * K))
     log(f"per-step us (stream): {json.dumps(pct)}")
     peaks = None if args.no_peaks else measure_peaks(torch, C, dev)
     roofline = with_measured_peak(roofline, peaks)
+
+    batched = None
+    if not args.no_batched:
+        # the other half of the metric: batched FP4 TFLOP/s of the grouped path on the same
+        # 384 experts (8192 tokens, and the matrix-core-bound 32768)
+        batched = {"metric": "batched FP4 TFLOP/s (algorithmic: 6 H I flops per (token, slot) "
+                             "pair, no hi/lo duplication)",
+                   "experts": "the decode layer's 384 experts"}
+        for name in ("prefill8192_uniform", "prefill32768_uniform"):
+            batched[name] = grouped_measure(torch, C, D, S, layer, S.WORKLOADS[name], dev,
+                                            K=10, W=2, terms=2)
+            log(f"batched {name}: " + json.dumps(batched[name]))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -360,10 +417,85 @@ def main() -> int:
         "kernels": kernels,
         "measured_peaks": peaks,
         "roofline": roofline,
+        "batched": batched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def grouped_measure(torch, C, D, S, layer, wl, dev, K: int, W: int, terms: int) -> dict:
+    """One grouped-path workload on a resident layer: K graph-replayed steps of top-k on the
+    workload's fresh router logits + moe_fp4_expert_ffn (the grouped GEMM path), then a
+    stream-launched pass with the library's kernel timing. Algorithmic flops are 6 H I per
+    (token, slot) pair (2 H I for each of gate, up and down; the two MXFP8 activation terms
+    are not counted twice); algorithmic bytes are each distinct expert once plus the
+    activations, logits and routing."""
+    H, I, E, k, T = wl.hidden, wl.inter, layer.n_experts, wl.k, wl.tokens
+    lgs = torch.stack([torch.from_numpy(S.router_logits(wl, 0, i)) for i in range(W + 2 * K)]).to(dev)
+    x = D.upload_bf16(S.activations(wl, 0, 0), dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    layer._workspace(T, k)
+    path = C.PATH_GROUPED if terms == 2 else C.PATH_GROUPED_FP8
+
+    def step(i: int) -> None:
+        C.moe_fp4_route_logits(lgs[i], T, E, k, ids, w)
+        layer.ffn(x, ids, w, y, path=path)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(W, W + K):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    step_s = ev0.elapsed_time(ev1) / 1e3 / K
+    del graph
+    distinct = []
+    for i in range(W, W + K):
+        C.moe_fp4_route_logits(lgs[i], T, E, k, ids, w)
+        distinct.append(int(torch.unique(ids).numel()))
+    d_avg = float(np.mean(distinct))
+    pairs = T * k
+    flops = pairs * 6.0 * H * I
+    step_bytes = d_avg * expert_bytes(H, I) + 2 * T * H * 2 + T * E * 4 + pairs * 8
+    C.moe_fp4_timing_reset()
+    C.moe_fp4_timing_enable(True)
+    for i in range(W + K, W + 2 * K):
+        step(i)
+    torch.cuda.synchronize()
+    C.moe_fp4_timing_enable(False)
+    kern = {}
+    for kind, name in enumerate(C.KERNEL_NAMES):
+        n, ms = C.moe_fp4_timing_read(kind)
+        if n:
+            kern[name] = round(ms * 1e3 / n, 2)
+    C.moe_fp4_timing_reset()
+    out = {"tokens": T, "steps": K, "ms_per_step": round(step_s * 1e3, 4),
+           "tflops": round(flops / step_s / 1e12, 1),
+           "frac_fp4_peak": round(flops / step_s / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4),
+           "algorithmic_gbps": round(step_bytes / step_s / 1e9, 1),
+           "frac_hbm": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+           "distinct_experts": round(d_avg, 1), "kernel_avg_us": kern}
+    gu = kern.get("grouped_gate_up")
+    if gu:
+        gflops = pairs * 4.0 * H * I  # gate and up
+        out["gate_up_tflops"] = round(gflops / (gu * 1e-6) / 1e12, 1)
+        out["gate_up_frac_fp4_peak"] = round(gflops / (gu * 1e-6) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4)
+    del lgs, x, ids, w, y
+    return out
 
 
 def run_stack(args) -> int:
@@ -388,8 +520,8 @@ def run_stack(args) -> int:
     layers = []
     for l in range(L):
         packed = torch.empty(stride * E, dtype=torch.uint8, device=dev)
-        for e0 in range(0, E, 32):
-            e1 = min(E, e0 + 32)
+        for e0 in range(0, E, S.STACK_CHUNK):
+            e1 = min(E, e0 + S.STACK_CHUNK)
             codes, scales = S.device_expert_blobs(wl, l, e0, e1, dev)
             C.moe_fp4_pack(codes, scales, e1 - e0, H, I, packed.data_ptr() + e0 * stride,
                            (e1 - e0) * stride)
@@ -639,7 +771,6 @@ def run_shared_expert(args) -> int:
     return 0
 
 
-MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 (the f8f6f4 MFMA runs at this rate with an FP8 operand)
 
 
 def run_batched(args) -> int:
@@ -748,8 +879,9 @@ def run_batched(args) -> int:
             t_s = gu["avg_us"] * 1e-6
             if wl.tokens >= 32768:  # enough tokens per expert for a matrix-core bound
                 achieved = pairs * 4.0 * H * I / t_s / 1e12
-                roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP4_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4),
+                            "frac_of_fp8_peak": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
                             "traffic": None, "kernel": "grouped_gate_up",
                             "flops_per_launch": pairs * 4.0 * H * I, "avg_launch_us": round(gu["avg_us"], 3)}
             else:

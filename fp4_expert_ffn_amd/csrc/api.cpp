@@ -178,8 +178,14 @@ int moe_fp4_route_residual(const float* residual_in, const uint16_t* y_prev, flo
       !aligned16(workspace))
     return MOE_FP4_ERR_MISALIGNED;
   if (workspace_bytes < moe_fp4_route_workspace_bytes(T, n_experts)) return MOE_FP4_ERR_WORKSPACE;
+  // At T == 1 every router workgroup reads the whole of residual_in and y_prev while the
+  // others write their slices of residual_out and x_out, so no output may overlap an input.
   const size_t rb = (size_t)T * (size_t)hidden * sizeof(float);
-  if (ranges_overlap(residual_in, rb, residual_out, rb)) return MOE_FP4_ERR_INVALID_ARG;
+  const size_t xb = (size_t)T * (size_t)hidden * sizeof(uint16_t);
+  if (ranges_overlap(residual_in, rb, residual_out, rb) || ranges_overlap(x_out, xb, y_prev, xb) ||
+      ranges_overlap(x_out, xb, residual_in, rb) || ranges_overlap(residual_out, rb, y_prev, xb) ||
+      ranges_overlap(x_out, xb, residual_out, rb))
+    return MOE_FP4_ERR_INVALID_ARG;
   if (T == 0) return MOE_FP4_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* sync = static_cast<uint32_t*>(workspace);
@@ -190,6 +196,28 @@ int moe_fp4_route_residual(const float* residual_in, const uint16_t* y_prev, flo
   if (launch_residual_rmsnorm(residual_in, y_prev, residual_out, x_out, T, hidden, eps, s) != hipSuccess)
     return MOE_FP4_ERR_HIP;
   return from_hip(route_impl(x_out, w_router, T, hidden, n_experts, k, topk_ids, topk_w, workspace, s));
+}
+
+int moe_fp4_route_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         void* stream) {
+  if (!workspace || !status) return MOE_FP4_ERR_INVALID_ARG;
+  if (!aligned16(workspace) || !aligned4(status)) return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < kRouteSyncBytes) return MOE_FP4_ERR_WORKSPACE;
+  return from_hip(launch_route_status(static_cast<const uint32_t*>(workspace), status,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_route_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return MOE_FP4_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return MOE_FP4_ERR_MISALIGNED;
+  if (workspace_bytes < kRouteSyncBytes) return MOE_FP4_ERR_WORKSPACE;
+  return from_hip(launch_route_reset(static_cast<uint32_t*>(workspace), kRouteSyncBytes,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int moe_fp4_debug_route_spin_limit(long long polls) {
+  set_route_spin_limit(polls);
+  return MOE_FP4_OK;
 }
 
 int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,

@@ -10,7 +10,7 @@
 // j = l % 16 of the MFMA, group g = l / 16) loads the 16 bytes of one 32-code block of
 // weight row (row0 + j), block 4 * chunk + g: a wavefront load covers 16 rows x 4 blocks.
 // The block is dequantised in registers by the hardware FP4 -> bf16 conversion, its ue8m0
-// scale applied in the same instruction (exact for scale bytes 2..252), and fed as the B
+// scale applied in the same instruction (exact for every scale byte; see scale_operand), and fed as the B
 // operand of v_mfma_f32_16x16x32_bf16; the token's activations are row 0 of the A operand
 // (read from LDS by the four lanes with l % 16 == 0, zeros elsewhere), so row 0 of the
 // 16 x 16 accumulator holds the 16 dot products. The weights are never expanded in memory:
@@ -366,8 +366,9 @@ __global__ __launch_bounds__(kDCThreads) void down_combine_kernel(
   }
 }
 
-// One thread per (row, block) of one matrix: the FP4 decode with the ue8m0 scale applied
-// in fp32 (exact for every scale byte), written out row-major [rows x K].
+// One thread per (row, block) of one matrix: the FP4 decode of the FFN kernels themselves
+// (fp4x8_to_bf16 with scale_operand, the conversion feeding their matrix-core B operands),
+// each bf16 result widened to fp32 (exactly) and written out row-major [rows x K].
 __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint4* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             int rows, int kb, float* __restrict__ out) {
@@ -377,29 +378,14 @@ __global__ __launch_bounds__(256) void debug_dequant_kernel(const uint4* __restr
   const int blk = (int)(b - (long)row * kb);
   const long v = (long)(row / 16) * 16 * kb + 64L * (blk / 4) + 16 * (blk % 4) + (row % 16);
   const uint4 c = codes[v];
-  const float s = ue8m0_to_f32(scales[v]);
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  const float s = scale_operand(scales[v]);
   float* o = out + b * kBlock;
-#define MOE_FP4_DQ_WORD(Q)                                                        \
-  {                                                                               \
-    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[Q], 1.0f, 0); \
-    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[Q], 1.0f, 1); \
-    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[Q], 1.0f, 2); \
-    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[Q], 1.0f, 3); \
-    o[Q * 8 + 0] = (float)p0.x * s;                                               \
-    o[Q * 8 + 1] = (float)p0.y * s;                                               \
-    o[Q * 8 + 2] = (float)p1.x * s;                                               \
-    o[Q * 8 + 3] = (float)p1.y * s;                                               \
-    o[Q * 8 + 4] = (float)p2.x * s;                                               \
-    o[Q * 8 + 5] = (float)p2.y * s;                                               \
-    o[Q * 8 + 6] = (float)p3.x * s;                                               \
-    o[Q * 8 + 7] = (float)p3.y * s;                                               \
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bf16x8_t d = fp4x8_to_bf16(dword(c, m), s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[8 * m + i] = (float)d[i];
   }
-  MOE_FP4_DQ_WORD(0)
-  MOE_FP4_DQ_WORD(1)
-  MOE_FP4_DQ_WORD(2)
-  MOE_FP4_DQ_WORD(3)
-#undef MOE_FP4_DQ_WORD
 }
 
 template <int XR>

@@ -3,6 +3,8 @@
 // expert on the indices was a measured cost; here there is none).
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_fp4_device.hpp"
 #include "moe_fp4_internal.hpp"
 
@@ -90,8 +92,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const V* __restrict__ lo
 // stores epoch + 1 as the next call's epoch once it has seen every record (so every
 // workgroup has read it). No atomic read-modify-write is needed (contended atomics across
 // the eight XCDs cost tens of microseconds at this width), and the initial contents of the
-// synchronisation words do not matter. The wait is bounded: after kSpinLimit polls
-// workgroup 0 proceeds, so the kernel always ends.
+// synchronisation words do not matter. The wait is bounded, so the kernel always ends: when
+// a record is still missing after spin_limit polls, workgroup 0 gives up, writes ids -1 and
+// weights 0 (ids that every FFN path skips and moe_fp4_validate_ids counts) and stores a
+// failure mark in the synchronisation area. A workgroup that starts after the give-up may
+// publish this call's logits under a key a later call would accept, so the mark is sticky:
+// every later call on the area writes ids -1 as well, until the area is cleared
+// (moe_fp4_route_reset), and moe_fp4_route_status reports it.
 // ---------------------------------------------------------------------------------------
 // Launch shape, measured on MI355X (H 4096, 384 experts): more workgroups with fewer bytes
 // each shorten the GEMV; overridable at build time.
@@ -113,6 +120,8 @@ static_assert(kRouteWaves >= 4 && kRouteWaves % kRouteKSplit == 0 && kRouteRowsP
               "route launch shape");
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kRouteRecOffset = 16;  // sync words before the logit records (64 bytes)
+constexpr int kRouteMarkWord = 2;    // 64-bit failure mark at sync words 2..3
+constexpr uint64_t kRouteFailMark = 0x4D4F4546344E4F47ull;  // a failed wait ("MOEF4NOG")
 
 // Epoch -> record key (the splitmix64 finaliser: consecutive epochs give unrelated keys).
 __device__ __forceinline__ uint64_t route_record_key(uint32_t epoch) {
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int H, int E, int k,
     uint32_t* __restrict__ sync, int32_t* __restrict__ ids,
     float* __restrict__ w, const float* __restrict__ r_in, const uint16_t* __restrict__ y_prev,
-    float* __restrict__ r_out, uint16_t* __restrict__ x_out, float eps) {
+    float* __restrict__ r_out, uint16_t* __restrict__ x_out, float eps, unsigned spin_limit) {
   const int G = gridDim.x;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
@@ -250,35 +259,73 @@ __global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
   }
   if (g != 0) return;
 
-  // workgroup 0: every record, checked, into LDS for the selection
+  // workgroup 0: the failure mark of an earlier call, then every record, checked, into LDS
+  // for the selection (at most spin_limit polls per record)
+  uint64_t* mark = reinterpret_cast<uint64_t*>(sync + kRouteMarkWord);
+  const bool failed_before =
+      __hip_atomic_load(mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kRouteFailMark;
   __shared__ double s_lg[64 * PER];
+  __shared__ int s_missing;
+  if (tid == 0) s_missing = 0;
+  __syncthreads();
+  bool missing = false;
   for (int f = tid; f < E; f += kRouteThreads) {
     unsigned n = 0;
-    uint64_t vb;
-    while (true) {
+    uint64_t vb = 0;
+    bool ok = false;
+    while (!failed_before && n < spin_limit) {
       const route_u32x4 r = ld_record(&rec[2 * f]);
       vb = ((uint64_t)r.y << 32) | r.x;
       const uint64_t ck = ((uint64_t)r.w << 32) | r.z;
-      if (ck == (vb ^ key)) break;
+      if (ck == (vb ^ key)) {
+        ok = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
-      if (++n > kSpinLimit) break;
+      ++n;
     }
+    missing |= !ok;
     s_lg[f] = __longlong_as_double((long long)vb);
   }
+  if (missing) s_missing = 1;  // any thread; a plain store of the same value
   __syncthreads();
+  const bool fail = failed_before || s_missing != 0;  // workgroup-uniform
   if (wv == 0) {
-    int sid[8];
-    float sw[8];
-    wave_topk<PER>(s_lg, E, k, lane, sid, sw);
+    if (!fail) {
+      int sid[8];
+      float sw[8];
+      wave_topk<PER>(s_lg, E, k, lane, sid, sw);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k && lane == j) {
-        ids[j] = sid[j];
-        w[j] = sw[j];
+      for (int j = 0; j < 8; ++j) {
+        if (j < k && lane == j) {
+          ids[j] = sid[j];
+          w[j] = sw[j];
+        }
       }
+      if (lane == 0) sync[0] = target;
+    } else {
+      if (lane < k) {
+        ids[lane] = -1;
+        w[lane] = 0.f;
+      }
+      if (lane == 0) __hip_atomic_store(mark, kRouteFailMark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (lane == 0) sync[0] = target;
   }
+}
+
+// moe_fp4_route_status: 1 if the synchronisation area holds the failure mark, else 0.
+__global__ void route_status_kernel(const uint32_t* __restrict__ sync, int32_t* __restrict__ status) {
+  if (threadIdx.x == 0) {
+    const uint64_t m = __hip_atomic_load(reinterpret_cast<const uint64_t*>(sync + kRouteMarkWord),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *status = m == kRouteFailMark ? 1 : 0;
+  }
+}
+
+// moe_fp4_route_reset: zero the synchronisation area (a fill kernel, so the call can be
+// captured in a graph).
+__global__ __launch_bounds__(256) void route_reset_kernel(uint4* __restrict__ sync, int n16) {
+  for (int i = threadIdx.x; i < n16; i += 256) sync[i] = make_uint4(0, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(1024) void validate_ids_kernel(const int32_t* __restrict__ ids,
@@ -336,7 +383,8 @@ hipError_t route_decode_launch(const uint16_t* x, const uint16_t* wr, int hidden
   const int per = (n_experts + 63) / 64;
 #define MOE_FP4_ROUTE_LAUNCH(P)                                                                   \
   return launch_kernel(kKindRouteDecode, route_decode_kernel<P, NIT>, grid, block, lds, s, x, wr,  \
-                       hidden, n_experts, k, sync, ids, w, r_in, y_prev, r_out, x_out, eps)
+                       hidden, n_experts, k, sync, ids, w, r_in, y_prev, r_out, x_out, eps,      \
+                       route_spin_limit())
   if (per <= 2) MOE_FP4_ROUTE_LAUNCH(2);
   if (per <= 4) MOE_FP4_ROUTE_LAUNCH(4);
   if (per <= 6) MOE_FP4_ROUTE_LAUNCH(6);
@@ -367,6 +415,26 @@ hipError_t launch_route_decode_norm(const float* r_in, const uint16_t* y_prev, f
   if (nit <= 4) MOE_FP4_RN(4);
   MOE_FP4_RN(8);
 #undef MOE_FP4_RN
+}
+
+namespace {
+unsigned g_route_spin_limit = kSpinLimit;
+}
+
+unsigned route_spin_limit() { return g_route_spin_limit; }
+
+void set_route_spin_limit(long long polls) {
+  g_route_spin_limit = polls < 0 ? kSpinLimit : (unsigned)std::min<long long>(polls, kSpinLimit);
+}
+
+hipError_t launch_route_status(const uint32_t* sync, int32_t* status, hipStream_t s) {
+  route_status_kernel<<<dim3(1), dim3(64), 0, s>>>(sync, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_reset(uint32_t* sync, size_t bytes, hipStream_t s) {
+  route_reset_kernel<<<dim3(1), dim3(256), 0, s>>>(reinterpret_cast<uint4*>(sync), (int)(bytes / 16));
+  return hipGetLastError();
 }
 
 int route_decode_sync_words(int n_experts) {

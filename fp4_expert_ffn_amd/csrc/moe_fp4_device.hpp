@@ -1,4 +1,5 @@
-// Device-side helpers: number formats, FP4 block dot products, wavefront reductions.
+// Device-side helpers: number formats, wavefront reductions, the router selection and the
+// residual + RMSNorm row helpers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,40 +20,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-// ue8m0 scale byte -> 2^(e - 127) in fp32 (2^-127 is an fp32 subnormal; e = 255 is NaN).
-__device__ __forceinline__ float ue8m0_to_f32(uint32_t e) {
-  const float s = __builtin_amdgcn_ldexpf(1.0f, (int)e - 127);
-  return e == 255u ? __builtin_nanf("") : s;
-}
-
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) {
-  return __builtin_bit_cast(bf16x2_t, v);
-}
-
-// Dot product of one 32-element FP4 block (16 bytes: byte b holds elements 2b (low nibble)
-// and 2b+1 (high nibble)) with 32 bf16 activations (64 bytes, natural order), unscaled.
-// Each byte becomes an exact bf16 pair (the conversion's scale operand is 1.0); v_dot2
-// multiplies it with the matching activation pair and accumulates in fp32.
-__device__ __forceinline__ float fp4_block_dot(const uint4 c, const uint4 a0, const uint4 a1,
-                                               const uint4 a2, const uint4 a3) {
-  float s0 = 0.f, s1 = 0.f;
-#define MOE_FP4_DOT_WORD(W, A)                                                              \
-  s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(W, 1.0f, 0), \
-                                       as_bf16x2((A).x), s0, false);                        \
-  s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(W, 1.0f, 1), \
-                                       as_bf16x2((A).y), s1, false);                        \
-  s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(W, 1.0f, 2), \
-                                       as_bf16x2((A).z), s0, false);                        \
-  s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(W, 1.0f, 3), \
-                                       as_bf16x2((A).w), s1, false);
-  MOE_FP4_DOT_WORD(c.x, a0)
-  MOE_FP4_DOT_WORD(c.y, a1)
-  MOE_FP4_DOT_WORD(c.z, a2)
-  MOE_FP4_DOT_WORD(c.w, a3)
-#undef MOE_FP4_DOT_WORD
-  return s0 + s1;
 }
 
 // fp64 value moved across lanes by a DPP pattern (both 32-bit halves alike).

@@ -40,8 +40,13 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
 // cache line in separate instructions; through the cache the line is fetched once).
 __device__ __forceinline__ uint32_t ld_scale(const uint8_t* p) { return *p; }
 
-// The scale operand of the FP4 conversion is a float whose exponent field is the ue8m0
-// byte: 2^(e-127) for e = 1..254, 2^-127 for e = 0, NaN for e = 255.
+// The scale operand of the FP4 conversion: a float whose exponent field is the ue8m0 byte.
+// The conversion reads only that field, as an E8M0 scale (measured on gfx950 for every code
+// pair and every byte): it multiplies by 2^(e-127) for every e = 0..254, keeping bf16
+// subnormal results (e = 0 and 1), and gives NaN for e = 255, zero codes included. A product
+// of magnitude 2^128 or more (e = 253 with |code| >= 4, e = 254 with |code| >= 2) is not
+// representable in bf16 and becomes +-inf. Every other result is exact: an E2M1 value times
+// a power of two has at most two significant bits.
 __device__ __forceinline__ float scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
 
 // Eight FP4 codes (one dword, element 2i in the low nibble of byte i) -> eight bf16 values

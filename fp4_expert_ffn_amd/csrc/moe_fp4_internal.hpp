@@ -104,6 +104,12 @@ hipError_t launch_route_decode(const uint16_t* x, const uint16_t* wr, int hidden
                                int k, uint32_t* sync, double* logits, int32_t* ids, float* w,
                                hipStream_t s);
 int route_decode_sync_words(int n_experts);
+// Bound of the batch-1 route's wait for each logit record (polls; the default unless set by
+// moe_fp4_debug_route_spin_limit), the failure-mark query and the clearing of the area.
+unsigned route_spin_limit();
+void set_route_spin_limit(long long polls);
+hipError_t launch_route_status(const uint32_t* sync, int32_t* status, hipStream_t s);
+hipError_t launch_route_reset(uint32_t* sync, size_t bytes, hipStream_t s);
 // The same with the router input computed in the kernel from a residual stream (one token):
 // r_out = r_in + y_prev, x_out = bf16(r_out / rms) with the standalone norm kernel's bits.
 hipError_t launch_route_decode_norm(const float* r_in, const uint16_t* y_prev, float* r_out,

@@ -54,6 +54,9 @@ _SIGNATURES = {
     "moe_fp4_route_workspace_bytes": (_Z, [_I, _I]),
     "moe_fp4_route": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "moe_fp4_route_logits": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_fp4_route_status": (_I, [_P, _Z, _P, _P]),
+    "moe_fp4_route_reset": (_I, [_P, _Z, _P]),
+    "moe_fp4_debug_route_spin_limit": (_I, [ctypes.c_longlong]),
     "moe_fp4_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_expert_ffn": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_fp4_expert_ffn_ex": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _Z, _I, _P]),
@@ -163,6 +166,25 @@ def moe_fp4_route(x, w_router, T: int, hidden: int, n_experts: int, k: int, topk
     _check(lib().moe_fp4_route(_ptr(x), _ptr(w_router), T, hidden, n_experts, k, _ptr(topk_ids),
                                _ptr(topk_w), _ptr(workspace), workspace_bytes, _stream(stream)),
            "moe_fp4_route")
+
+
+def _nbytes(t, given: Optional[int]) -> int:
+    return t.numel() * t.element_size() if given is None else given
+
+
+def moe_fp4_route_status(workspace, status, workspace_bytes: Optional[int] = None,
+                         stream=None) -> None:
+    _check(lib().moe_fp4_route_status(_ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                      _ptr(status), _stream(stream)), "moe_fp4_route_status")
+
+
+def moe_fp4_route_reset(workspace, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    _check(lib().moe_fp4_route_reset(_ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                     _stream(stream)), "moe_fp4_route_reset")
+
+
+def moe_fp4_debug_route_spin_limit(polls: int) -> None:
+    _check(lib().moe_fp4_debug_route_spin_limit(polls), "moe_fp4_debug_route_spin_limit")
 
 
 def moe_fp4_route_logits(logits, T: int, n_experts: int, k: int, topk_ids, topk_w,

@@ -110,6 +110,30 @@ int moe_fp4_route(const uint16_t* x, const uint16_t* w_router, int T, int hidden
                   int k, int32_t* topk_ids, float* topk_w, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* A batch-1 call waits, boundedly, for the router logits its other workgroups publish in
+ * the synchronisation area (about a second of polling; only a GPU that cannot run all of
+ * the call's workgroups meanwhile reaches the bound). If the bound is reached the call
+ * gives up: it writes topk_ids = -1 and topk_w = 0 (ids every FFN path skips and
+ * moe_fp4_validate_ids counts) and marks the area as failed. Workgroups that start after
+ * the give-up can leave records a later call would take for its own, so the mark is
+ * sticky: every later batch-1 call on that workspace (moe_fp4_route, moe_fp4_route_residual,
+ * moe_fp4_moe_forward) writes -1 / 0 as well until moe_fp4_route_reset clears the area.
+ * moe_fp4_route_status writes 1 to the device int32 *status if the area of `workspace`
+ * (the route or moe_fp4_moe_forward workspace, at least 16 KB) holds the mark, else 0.
+ * moe_fp4_route_reset zeroes the 16 KB area with a fill kernel on `stream` (no memset node,
+ * so it can be captured in a graph); the next call starts afresh. Both are stream-ordered.
+ * Errors: INVALID_ARG (null), MISALIGNED (workspace 16-byte, status 4-byte), WORKSPACE
+ * (workspace_bytes < 16384), HIP. */
+int moe_fp4_route_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         void* stream);
+int moe_fp4_route_reset(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug helper for tests of the give-up above: sets the number of polls per logit record
+ * after which later batch-1 route launches give up (0: at once, without polling; negative:
+ * the default bound). A host-side setting of this process, read at each launch; not
+ * thread-safe. */
+int moe_fp4_debug_route_spin_limit(long long polls);
+
 /* The selection and weighting of moe_fp4_route applied to given fp32 logits
  * [T x n_experts] (for workloads whose router logits are drawn directly). No workspace. */
 int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32_t* topk_ids,
@@ -122,8 +146,16 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
  * and y[t] = sum_j topk_w[t, j] * y_e, summed in ascending expert id (so permuting a
  * token's (id, weight) pairs does not change the result). Ids outside [0, n_experts)
  * contribute nothing; duplicate ids add up; weights are used as given.
+ * The pages state the problem this way: per token, 6 of 384 experts, each an FP4 blob of
+ * three adjacent matrices with a separate ue8m0 scale block, read and applied per token
+ * ([8GB-GPU], sections 每 token 字节数决定一切 and 方案：不重写模型，只迁移其存储); the FP4 codes
+ * meet the matrix cores without being expanded in memory ([A100-FP4], section
+ * 「FP4非対応」という言葉を疑う).
  * Numerics: FP4 weights are dequantised exactly in registers, products and sums are fp32,
- * h is rounded to bf16 before the down projection, y is rounded to bf16.
+ * h is rounded to bf16 before the down projection, y is rounded to bf16. Every ue8m0 byte is
+ * applied exactly (255 = NaN, which propagates to the outputs it reaches); a dequantised
+ * weight of magnitude 2^128 or more (byte 253 with |E2M1| >= 4, byte 254 with |E2M1| >= 2)
+ * is outside the bf16 operand range of the decode and small-M paths and becomes +-inf there.
  * ------------------------------------------------------------------------------------ */
 
 /* Workspace bytes moe_fp4_expert_ffn (any path) needs: the larger of h of every (token,
@@ -225,8 +257,11 @@ int moe_fp4_residual_init(const uint16_t* x, float* residual, int T, int hidden,
  * top-k routing of x_out exactly as moe_fp4_route. At T == 1 this is one launch: every
  * workgroup of the router kernel normalises the row itself, so the separate norm launch of
  * a decode step goes away ([A100-FP4], section 然后又发现每 token 启动 2000 次内核: per-token
- * launches cost more than their math). residual_in, residual_out [T x hidden] fp32 must not
- * overlap; y_prev, x_out [T x hidden] bf16; eps >= 0 and finite; the workspace as for
+ * launches cost more than their math). residual_in, residual_out [T x hidden] fp32;
+ * y_prev, x_out [T x hidden] bf16; no output (residual_out, x_out) may overlap an input
+ * (residual_in, y_prev) or the other output: at T == 1 every workgroup reads the whole
+ * input rows while the others write their slices of the outputs, so x_out cannot reuse
+ * y_prev's buffer (INVALID_ARG). eps >= 0 and finite; the workspace as for
  * moe_fp4_route (its first 16 KB carry the synchronisation words between calls). hidden % 32
  * == 0 and <= 16384; 16-byte alignment except topk_ids / topk_w (4).
  * Errors: INVALID_ARG (null, eps, overlap, T / k / n_experts as moe_fp4_route), BAD_SHAPE,
@@ -287,8 +322,14 @@ int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,
 
 /* Debug helper: dequantises matrix `matrix` (0 gate, 1 up, 2 down) of expert `expert` of
  * a packed buffer to fp32 out [rows x K] (gate/up: [inter x hidden], down: [hidden x
- * inter]) with the same in-register decode the FFN kernels use:
- * out = E2M1(code) * 2^(e-127), exact in fp32 unless it overflows (NaN for e = 255).
+ * inter]) with the in-register decode the decode and small-M FFN kernels feed to their
+ * matrix cores (the same device function): the FP4 -> bf16 conversion with the ue8m0 byte
+ * as its scale, each bf16 widened exactly to fp32. out = E2M1(code) * 2^(e-127) rounded to
+ * bf16, which is exact for every e = 0..254 (bf16 subnormals included) except where the
+ * magnitude reaches 2^128 (e = 253 with |E2M1| >= 4, e = 254 with |E2M1| >= 2: +-inf);
+ * NaN for e = 255 ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug: ue8m0 scales; 255 as
+ * NaN is the E8M0 reading). The grouped path hands the same bytes to the block-scaled
+ * matrix cores, which apply them as E8M0 scales themselves.
  * Errors: INVALID_ARG (null, expert or matrix out of range), BAD_SHAPE, MISALIGNED, HIP. */
 int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int inter, int expert,
                           int matrix, float* out, void* stream);

@@ -164,6 +164,12 @@ def random_codes(rng: np.random.Generator, rows: int, k: int) -> np.ndarray:
     return rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
 
 
+#: Experts per device-generator call when a stack's experts are drawn on the device: the
+#: draw of expert e depends on its chunk [e0, e0 + STACK_CHUNK) (the seed is the chunk's
+#: first expert), so the bench and the tests that regenerate an expert use this one size.
+STACK_CHUNK = 32
+
+
 def device_expert_blobs(wl: Workload, layer: int, e0: int, e1: int, device, root: int = 0):
     """Codes [e1 - e0, 3 H I / 2] and scales [e1 - e0, 3 H I / 32] (uint8, canonical layout)
     of experts e0 .. e1 - 1 drawn on the device with torch's counter-based Philox

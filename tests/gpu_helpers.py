@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import os
 import sys
 import time
 
@@ -44,3 +45,40 @@ def check_route(ids_gpu: np.ndarray, w_gpu: np.ndarray, ids_ref: np.ndarray, w_r
     assert bad.size == 0, f"{label}: ids differ at tokens {bad[:10].tolist()}"
     rel = np.abs(w_gpu.astype(np.float64) - w_ref) / np.abs(w_ref)
     assert float(rel.max()) <= WEIGHT_REL_TOL, f"{label}: weight rel err {rel.max():.3e}"
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle on large checks: the host cores this process may use, at most
+    16 (a GPU machine's CPU share per GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_ffn_parallel(x_bits, ids, w, src, n_experts, hidden, inter, workers=None):
+    """The oracle's expert_ffn for many tokens, run on disjoint expert ranges in threads
+    (NumPy releases the interpreter lock in its array work) and summed range by range.
+    Each range's call is the plain oracle with the other ranges' ids masked to -1 (ids
+    outside [0, E) contribute nothing), so the result is the oracle's up to fp64
+    reassociation of the per-token sum across ranges."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    workers = workers or oracle_workers()
+    ids = np.asarray(ids)
+    parts = max(1, min(workers, n_experts))
+
+    def run(r):
+        lo, hi = n_experts * r // parts, n_experts * (r + 1) // parts
+        idr = np.where((ids >= lo) & (ids < hi), ids, -1).astype(np.int32)
+        if not np.any(idr >= 0):
+            return None
+        with threadpool_limits(limits=1):
+            return O.expert_ffn(x_bits, idr, w, src, n_experts, hidden, inter)
+
+    with ThreadPoolExecutor(parts) as ex:
+        outs = list(ex.map(run, range(parts)))
+    y = np.zeros((np.asarray(x_bits).shape[0], hidden), dtype=np.float64)
+    for o in outs:
+        if o is not None:
+            y += o
+    return y

@@ -238,7 +238,8 @@ def test_route_residual_argument_checks(L):
     f = L.moe_fp4_route_residual
     B = 0x20000  # a second aligned fake address, far from A
     big = 1 << 20
-    args = lambda **kw: dict(dict(ri=A, y=A, ro=B, xo=A, eps=1e-6, wr=A, T=1, H=64, E=8, k=2,
+    Y, XO = 0x30000, 0x40000  # y_prev and x_out: distinct from every other buffer
+    args = lambda **kw: dict(dict(ri=A, y=Y, ro=B, xo=XO, eps=1e-6, wr=A, T=1, H=64, E=8, k=2,
                                   ids=A, w=A, ws=A, wsb=big), **kw)
     def call(**kw):
         a = args(**kw)
@@ -251,8 +252,27 @@ def test_route_residual_argument_checks(L):
     assert call(eps=float("nan")) == C.ERR_INVALID_ARG
     assert call(ro=A) == C.ERR_INVALID_ARG  # residual_in and residual_out overlap (checked before any launch)
     assert call(ro=A + 64 * 4 - 16, T=1) == C.ERR_INVALID_ARG
+    # no output may overlap an input or the other output (x_out in y_prev's buffer is the
+    # natural reuse, and a race at T == 1)
+    assert call(xo=Y) == C.ERR_INVALID_ARG
+    assert call(xo=Y + 64 * 2 - 16) == C.ERR_INVALID_ARG
+    assert call(xo=A + 16) == C.ERR_INVALID_ARG             # x_out inside residual_in
+    assert call(ro=Y - 64 * 4 + 16) == C.ERR_INVALID_ARG    # residual_out over y_prev
+    assert call(xo=B + 64) == C.ERR_INVALID_ARG             # x_out inside residual_out
     assert call(k=9) == C.ERR_INVALID_ARG
     assert call(H=100) == C.ERR_BAD_SHAPE
     assert call(ri=MIS) == C.ERR_MISALIGNED
     assert call(ids=MIS4) == C.ERR_MISALIGNED
     assert call(wsb=16) == C.ERR_WORKSPACE
+
+
+def test_route_status_reset_argument_checks(L):
+    assert L.moe_fp4_route_status(None, 1 << 14, A, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_route_status(A, 1 << 14, None, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_route_status(MIS, 1 << 14, A, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_route_status(A, 1 << 14, MIS4, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_route_status(A, (1 << 14) - 1, A, None) == C.ERR_WORKSPACE
+    assert L.moe_fp4_route_reset(None, 1 << 14, None) == C.ERR_INVALID_ARG
+    assert L.moe_fp4_route_reset(MIS, 1 << 14, None) == C.ERR_MISALIGNED
+    assert L.moe_fp4_route_reset(A, 100, None) == C.ERR_WORKSPACE
+    assert L.moe_fp4_debug_route_spin_limit(-1) == C.OK  # the default bound

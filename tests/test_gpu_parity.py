@@ -10,7 +10,7 @@ import pytest
 
 from oracle import moe_oracle as O
 from synth import moe_inputs as S
-from tests.gpu_helpers import check_ffn, check_route, log
+from tests.gpu_helpers import check_ffn, check_route, log, oracle_ffn_parallel
 
 pytestmark = pytest.mark.gpu
 
@@ -84,31 +84,46 @@ def _run_ffn(layer, x_bits, ids, w, dev, path=None):
 
 # ------------------------------------------------------------------------------ dequant
 
+def _bf16_dequant_ref(c, s):
+    """The oracle's exact value rounded to bf16 (the FFN kernels' operand format), as fp32:
+    exact except where the magnitude reaches 2^128 (+-inf); NaN for scale byte 255."""
+    return O.bf16_to_f64(O.f64_to_bf16_bits(O.dequant_fp4(c, s))).astype(np.float32)
+
+
+def _assert_same_bits(got, ref, label):
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), f"{label}: NaN positions differ"
+    gb, rb = got.view(np.uint32)[~nan_g], ref.view(np.uint32)[~nan_r]
+    bad = np.nonzero(gb != rb)[0]
+    assert bad.size == 0, f"{label}: {bad.size} mismatches, first {got[~nan_g][bad[:4]]} vs {ref[~nan_r][bad[:4]]}"
+
+
 def test_dequant_all_codes_and_scales_bit_exact(dev):
+    """moe_fp4_debug_dequant runs the FFN kernels' own decode (the FP4 -> bf16 conversion
+    with the ue8m0 byte as its scale operand). Every code pair meets every scale byte
+    0..255 in each of gate, up and down: bit-exact against the oracle rounded to bf16,
+    i.e. exact 2^(e-127) scaling including e = 0 and 1 (bf16 subnormals), +-inf where the
+    value reaches 2^128 (e = 253 with |v| >= 4, e = 254 with |v| >= 2), NaN for e = 255."""
     C, D = _mods()
     H, I = 256, 128
-    # gate: 1024 blocks; block b has bytes 16b..16b+15 (mod 256): every low nibble 0..15,
-    # and scale byte b mod 256: every (code, scale) pair occurs.
+    # gate and up: block b has bytes 16b..16b+15 (mod 256), so every code byte occurs, and
+    # scale byte b mod 256 (1024 blocks: every (code, scale) pair four times); down: the
+    # same pattern over its own 1024 blocks, shifted by one byte so the pairing differs.
     n = I * H // 2
-    gate_codes = (np.arange(n) % 256).astype(np.uint8)
-    gate_scales = (np.arange(I * H // 32) % 256).astype(np.uint8)
-    rng = np.random.default_rng(3)
-    codes = np.concatenate([gate_codes, rng.integers(0, 256, 2 * n, dtype=np.uint8)])
-    scales = np.concatenate([gate_scales, rng.integers(0, 255, 2 * I * H // 32, dtype=np.uint8)])
+    base_codes = (np.arange(n) % 256).astype(np.uint8)
+    base_scales = (np.arange(I * H // 32) % 256).astype(np.uint8)
+    codes = np.concatenate([base_codes, base_codes[::-1], (base_codes + 1).astype(np.uint8)])
+    scales = np.concatenate([base_scales, base_scales[::-1], (base_scales + 7).astype(np.uint8)])
     packed = D.upload_experts(lambda e: (codes, scales), 1, H, I, dev)
     mats = O.split_expert(codes, scales, H, I)
     for m, (c, s) in enumerate(mats):
+        assert set(np.unique(s).tolist()) == set(range(256))
         out = torch.empty(c.shape[0] * c.shape[1] * 2, dtype=torch.float32, device=dev)
         C.moe_fp4_debug_dequant(packed, 1, H, I, 0, m, out)
         torch.cuda.synchronize()
         got = out.cpu().numpy().reshape(c.shape[0], -1)
-        ref = O.dequant_fp4(c, s).astype(np.float32)
-        nan_g, nan_r = np.isnan(got), np.isnan(ref)
-        assert np.array_equal(nan_g, nan_r), f"matrix {m}: NaN positions differ"
-        gb, rb = got.view(np.uint32)[~nan_g], ref.view(np.uint32)[~nan_r]
-        bad = np.nonzero(gb != rb)[0]
-        assert bad.size == 0, f"matrix {m}: {bad.size} mismatches, first {got[~nan_g][bad[:4]]} vs {ref[~nan_r][bad[:4]]}"
-    log("dequant: all 16 codes x 256 scale bytes bit-exact")
+        _assert_same_bits(got, _bf16_dequant_ref(c, s), f"matrix {m}")
+    log("dequant: the FFN decode of all 16 codes x 256 scale bytes bit-exact (bf16)")
 
 
 @pytest.mark.parametrize("H,I,E", [(256, 128, 3), (4096, 2880, 2), (320, 96, 4)])
@@ -123,7 +138,7 @@ def test_pack_round_trip_bit_exact(dev, H, I, E):
             C.moe_fp4_debug_dequant(packed, E, H, I, e, m, out)
             torch.cuda.synchronize()
             got = out.cpu().numpy().reshape(c.shape[0], -1)
-            assert np.array_equal(got, O.dequant_fp4(c, s).astype(np.float32)), (e, m)
+            assert np.array_equal(got, _bf16_dequant_ref(c, s)), (e, m)
 
 
 # ------------------------------------------------------------------------------ activation quantiser
@@ -221,11 +236,89 @@ def test_route_batch1_record_area_edge(dev, n_experts):
         if step == 3:
             x_bits = wr_bits[0:1].copy()
         ids_ref, w_ref, _ = O.route(x_bits, wr_bits, k)
+        C.moe_fp4_timing_reset()
+        C.moe_fp4_timing_enable(True)
         ids, w = layer.route(D.upload_bf16(x_bits, dev))
         torch.cuda.synchronize()
+        C.moe_fp4_timing_enable(False)
+        launched = {n for kind, n in enumerate(C.KERNEL_NAMES) if C.moe_fp4_timing_read(kind)[0]}
+        C.moe_fp4_timing_reset()
+        # the kernels that ran: one launch up to 1020 experts, GEMV + selection above
+        expect = {"route_decode"} if n_experts <= 1020 else {"router_gemv", "topk"}
+        assert launched == expect, (n_experts, launched)
         check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"E {n_experts} step {step}")
         if step == 3:
             assert list(ids_ref[0][:2]) == [0, n_experts - 1]
+
+
+def test_route_batch1_give_up_is_reported_and_sticky(dev):
+    """A batch-1 route whose wait for the logit records gives up (forced from the host: a
+    spin bound of 0 polls, so every kernel still runs to its normal end) writes ids -1 and
+    weights 0, marks its workspace, and keeps doing so on later calls, also with the normal
+    bound, until moe_fp4_route_reset; the routed FFN then contributes nothing (y = 0), and
+    after the reset the route matches the oracle again."""
+    C, D = _mods()
+    wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
+    wr_bits = S.router_weights(wl, 0)[:64].copy()
+    k = 6
+    layer = D.MoeFp4Layer(torch.empty(256, dtype=torch.uint8, device=dev), 64, wl.hidden,
+                          wl.inter, k, D.upload_bf16(wr_bits, dev))
+    status = torch.full((1,), 7, dtype=torch.int32, device=dev)
+
+    def route_and_status(step):
+        x_bits = S.activations(wl, 0, 2000 + step)
+        ids, w = layer.route(D.upload_bf16(x_bits, dev))
+        C.moe_fp4_route_status(layer._rws, status)
+        torch.cuda.synchronize()
+        return x_bits, ids.cpu().numpy(), w.cpu().numpy(), int(status.item())
+
+    try:
+        x_bits, ids, w, st = route_and_status(0)
+        ids_ref, w_ref, _ = O.route(x_bits, wr_bits, k)
+        check_route(ids, w, ids_ref, w_ref, "before")
+        assert st == 0
+        C.moe_fp4_debug_route_spin_limit(0)
+        _, ids, w, st = route_and_status(1)
+        assert np.all(ids == -1) and np.all(w == 0.0) and st == 1, (ids, w, st)
+        C.moe_fp4_debug_route_spin_limit(-1)  # the normal bound again: still failed
+        _, ids, w, st = route_and_status(2)
+        assert np.all(ids == -1) and np.all(w == 0.0) and st == 1
+        bad = torch.zeros(1, dtype=torch.int32, device=dev)
+        C.moe_fp4_validate_ids(torch.from_numpy(ids).to(dev), 1, k, 64, bad)
+        torch.cuda.synchronize()
+        assert int(bad.item()) == k
+        C.moe_fp4_route_reset(layer._rws)
+        for step in (3, 4, 5):
+            x_bits, ids, w, st = route_and_status(step)
+            ids_ref, w_ref, _ = O.route(x_bits, wr_bits, k)
+            check_route(ids, w, ids_ref, w_ref, f"after reset, step {step}")
+            assert st == 0
+    finally:
+        C.moe_fp4_debug_route_spin_limit(-1)
+
+
+def test_moe_forward_give_up_outputs_zero(dev):
+    """The one-call layer on a workspace whose batch-1 route gave up: ids -1, weights 0 and
+    y exactly 0 (the FFN skips every slot), then correct again after moe_fp4_route_reset."""
+    C, D = _mods()
+    wl = S.small_workload(256, 128, 8, 2, 1, wid=960)
+    layer = _layer(wl, dev)
+    x_bits = S.activations(wl, 0, 0)
+    x = D.upload_bf16(x_bits, dev)
+    try:
+        C.moe_fp4_debug_route_spin_limit(0)
+        y, ids, w = layer.forward_fused(x)
+        torch.cuda.synchronize()
+        assert torch.all(ids == -1) and torch.all(w == 0) and torch.all(y.float() == 0)
+    finally:
+        C.moe_fp4_debug_route_spin_limit(-1)
+    C.moe_fp4_route_reset(layer._fws)
+    y, ids, w = layer.forward_fused(x)
+    torch.cuda.synchronize()
+    ids_ref, w_ref, _ = O.route(x_bits, S.router_weights(wl, 0), wl.k)
+    check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, "forward after reset")
+    ref = O.expert_ffn(x_bits, ids_ref, w_ref, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
+    check_ffn(D.bf16_bits(y), ref, "forward after reset")
 
 
 @pytest.mark.parametrize("routing", ["zipf", "uniform", "ties"])
@@ -296,6 +389,97 @@ def test_ffn_small_shapes(dev, H, I, E, k, T, path):
     log(f"path {path} H{H} I{I} E{E} k{k} T{T}: normwise {err:.2e} cosine {cos:.7f}")
 
 
+def _restrict_codes(byte_row, scale_byte):
+    """Limit the 32 codes of one block so that code * 2^(e-127) stays below 2^128, the bf16
+    range: |code| <= 1.5 for e = 254, <= 3 for e = 253 (the codes' magnitude bits)."""
+    lo, hi = byte_row & 0x0F, byte_row >> 4
+    def fix(n):
+        if scale_byte == 254:
+            return n & 0xB                       # magnitude 0, 0.5, 1, 1.5
+        if scale_byte == 253:
+            return np.where((n & 0x6) == 0x6, n ^ 0x2, n)  # 4 -> 2, 6 -> 3
+        return n
+    return (fix(lo) | (fix(hi) << 4)).astype(np.uint8)
+
+
+def _extreme_scale_experts(H, I):
+    """Five experts with extreme ue8m0 bytes (codes uniform, other scale bytes 120..130):
+     0: a quarter of the blocks of every matrix at bytes 0, 1 or 2 (bf16 subnormal weights);
+     1: K-block 3 of every gate and up row at 252, 253 or 254 (codes kept below 2^128);
+        the inputs' K-block 3 is scaled by 2^-112, so these blocks weigh like the others;
+     2: I-block 2 of every down row at 252, 253 or 254; gate and up rows 64..95 at byte 67,
+        so the h entries they meet are about 2^-110;
+     3: gate row 5, K-block 1 at byte 255 (NaN): h[5] is NaN, so every output is NaN;
+     4: down row 7, K-block 0 at byte 255: output row 7 is NaN, the rest finite."""
+    wl = S.small_workload(H, I, 5, 2, 14, wid=950)
+    rng = np.random.default_rng(950)
+    experts = []
+    for e in range(5):
+        codes, scales = S.expert_blob(wl, 0, e)
+        (gc, gs), (uc, us), (dc, ds) = O.split_expert(codes, scales, H, I)  # views
+        if e == 0:
+            for c, s in ((gc, gs), (uc, us), (dc, ds)):
+                sel = rng.random(s.shape) < 0.25
+                s[sel] = rng.integers(0, 3, size=int(sel.sum()), dtype=np.uint8)
+        elif e == 1:
+            for c, s in ((gc, gs), (uc, us)):
+                for r in range(s.shape[0]):
+                    s[r, 3] = rng.integers(252, 255)
+                    c[r, 48:64] = _restrict_codes(c[r, 48:64], int(s[r, 3]))
+        elif e == 2:
+            for r in range(ds.shape[0]):
+                ds[r, 2] = rng.integers(252, 255)
+                dc[r, 32:48] = _restrict_codes(dc[r, 32:48], int(ds[r, 2]))
+            gs[64:96, :] = 67
+            us[64:96, :] = 67
+        elif e == 3:
+            gs[5, 1] = 255
+        else:
+            ds[7, 0] = 255
+        w = np.concatenate([O.dequant_fp4(c, s).ravel() for c, s in ((gc, gs), (uc, us), (dc, ds))])
+        assert np.nanmax(np.abs(w)) < 2.0 ** 128
+        experts.append((codes, scales))
+    return wl, experts
+
+
+def _check_ffn_nan_aware(y_bits, ref, label):
+    """NaN positions equal to the oracle's; the finite part of each token within the bar."""
+    y = O.bf16_to_f64(y_bits)
+    for t in range(y.shape[0]):
+        nan_y, nan_r = np.isnan(y[t]), np.isnan(ref[t])
+        assert np.array_equal(nan_y, nan_r), f"{label} token {t}: NaN positions differ " \
+            f"({int(nan_y.sum())} vs {int(nan_r.sum())})"
+        fin = ~nan_r
+        if fin.any():
+            check_ffn(O.f64_to_bf16_bits(y[t][fin])[None, :], ref[t][fin][None, :], f"{label} token {t}")
+
+
+@PATHS
+def test_ffn_extreme_scale_bytes(dev, path):
+    """FFN parity with scale bytes 0, 1, 2, 252, 253, 254 and 255 in the weights, on every
+    path: tiny blocks change nothing visible, huge blocks (balanced by tiny inputs) carry
+    their exact power of two, and a NaN block poisons exactly the outputs it reaches."""
+    C, D = _mods()
+    H, I = 256, 128
+    wl, experts = _extreme_scale_experts(H, I)
+    src = lambda e: experts[e]  # noqa: E731
+    packed = D.upload_experts(src, 5, H, I, dev)
+    layer = D.MoeFp4Layer(packed, 5, H, I, 2)
+    x = O.bf16_to_f64(S.activations(wl, 0, 0))
+    x[:, 96:128] *= 2.0 ** -112
+    x_bits = O.f64_to_bf16_bits(x)
+    ids = np.array([[0, -1], [0, 1], [1, -1], [1, 2], [2, -1], [2, 0], [3, -1], [3, 0],
+                    [4, -1], [4, 1], [0, 2], [1, 0], [2, 1], [0, 0]], np.int32)
+    w = (np.random.default_rng(951).random(ids.shape) + 0.05).astype(np.float32)
+    keep = np.arange(14) if path != GROUPED_FP8 else np.array([0, 1, 2, 3, 4, 5, 10, 11, 12, 13])
+    y = _run_ffn(layer, x_bits, ids, w, dev, path)
+    ref = _ref(path, x_bits[keep], ids[keep], w[keep], src, 5, H, I)
+    _check_ffn_nan_aware(y[keep], ref, f"extreme scales, path {path}")
+    if path != GROUPED_FP8:
+        assert np.all(np.isnan(O.bf16_to_f64(y[6]))) and np.isnan(O.bf16_to_f64(y[8][7]))
+    log(f"extreme scale bytes, path {path}: NaN positions equal, finite parts within the bar")
+
+
 @pytest.fixture(scope="module")
 def decode_layer(dev):
     wl = S.WORKLOADS["layer_decode_h4096_i2880_e384"]
@@ -303,25 +487,33 @@ def decode_layer(dev):
     return wl, _layer(wl, dev)
 
 
+@pytest.mark.timeout(900)
 def test_layer_decode_full_size_route_and_ffn(dev, decode_layer):
-    """One 384-expert layer at full size, batch 1, token by token: route on the GPU (ids
-    bit-exact against the oracle) then the expert FFN (tolerance against the oracle)."""
+    """One 384-expert layer at full size, batch 1, 100 tokens one call at a time, as the
+    bench runs them (moe_fp4_moe_forward: the one-launch route, then the decode FFN kernels):
+    ids bit-exact and weights against the oracle's routing of each token, outputs within
+    the bar of the oracle's FFN."""
     _, D = _mods()
     wl, layer = decode_layer
-    n_tok = 16
+    n_tok = 100
     wr_bits = S.router_weights(wl, 0)
-    src = S.expert_source(wl)
+    x_all = np.concatenate([S.activations(wl, 0, s) for s in range(n_tok)])
+    xd = D.upload_bf16(x_all, dev)
+    ys, idss, ws = [], [], []
     for s in range(n_tok):
-        x_bits = S.activations(wl, 0, s)
-        x = D.upload_bf16(x_bits, dev)
-        y, ids, w = layer.forward(x)
-        torch.cuda.synchronize()
-        ids_ref, w_ref, _ = O.route(x_bits, wr_bits, wl.k)
-        check_route(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref, f"token {s}")
-        ref = O.expert_ffn(x_bits, ids_ref, w_ref, src, wl.n_experts, wl.hidden, wl.inter)
-        err, cos = check_ffn(D.bf16_bits(y), ref, f"token {s}")
-        if s % 4 == 0:
-            log(f"decode token {s}: normwise {err:.2e} cosine {cos:.7f}")
+        y, ids, w = layer.forward_fused(xd[s:s + 1])
+        ys.append(y.clone()), idss.append(ids.clone()), ws.append(w.clone())
+    torch.cuda.synchronize()
+    ids_g = torch.cat(idss).cpu().numpy()
+    w_g = torch.cat(ws).cpu().numpy()
+    y_g = D.bf16_bits(torch.cat(ys))
+    ids_ref, w_ref, _ = O.route(x_all, wr_bits, wl.k)
+    check_route(ids_g, w_g, ids_ref, w_ref, "decode 100 tokens")
+    ref = oracle_ffn_parallel(x_all, ids_ref, w_ref, S.expert_source(wl), wl.n_experts,
+                              wl.hidden, wl.inter)
+    err, cos = check_ffn(y_g, ref, "decode 100 tokens")
+    log(f"decode, 100 tokens ({len(np.unique(ids_ref))} distinct experts): worst normwise "
+        f"{err:.2e}, worst cosine {cos:.7f}")
 
 
 def test_moe_forward_matches_route_then_ffn(dev, decode_layer):
@@ -405,25 +597,57 @@ def test_layer_multi_token_full_size(dev, decode_layer, name):
     log(f"{name}: {len(np.unique(ids_ref))} distinct experts, small-M normwise {err:.2e} cosine {cos:.7f}")
 
 
-def test_layer_prefill8192_sampled(dev, decode_layer):
-    """8192 tokens with uniform logits; the oracle checks a seeded sample of tokens."""
+def _prefill_sampled(dev, layer, wl_l, wl, n_sample, seed, paths):
     _, D = _mods()
-    wl_l, layer = decode_layer
-    wl = S.WORKLOADS["prefill8192_uniform"]
     lg = S.router_logits(wl, 0, 0)
     ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
     x_bits = S.activations(wl, 0, 0)
-    sample = np.sort(np.random.default_rng(55).choice(8192, size=24, replace=False))
+    T = x_bits.shape[0]
+    sample = np.sort(np.random.default_rng(seed).choice(T, size=n_sample, replace=False))
     ids_ref, w_ref = O.topk_softmax(lg[sample].astype(np.float64), 6)
-    check_route(ids.cpu().numpy()[sample], w.cpu().numpy()[sample], ids_ref, w_ref, "prefill")
-    ref = O.expert_ffn(x_bits[sample], ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
-    for path in (DECODE, GROUPED):
-        y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w, path=path)
+    check_route(ids.cpu().numpy()[sample], w.cpu().numpy()[sample], ids_ref, w_ref, wl.name)
+    xd = D.upload_bf16(x_bits, dev)
+    ref = oracle_ffn_parallel(x_bits[sample], ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880)
+    for path in paths:
+        y = layer.ffn(xd, ids, w, path=path)
         torch.cuda.synchronize()
         yb = D.bf16_bits(y)
-        assert np.all(np.isfinite(O.bf16_to_f64(yb))), f"path {path}"
-        err, cos = check_ffn(yb[sample], ref, f"prefill8192 path {path}")
-        log(f"prefill8192 path {path}, sample of 24: normwise {err:.2e} cosine {cos:.7f}")
+        assert np.all(np.isfinite(O.bf16_to_f64(yb))), f"{wl.name} path {path}"
+        err, cos = check_ffn(yb[sample], ref, f"{wl.name} path {path}")
+        log(f"{wl.name} path {path}, sample of {n_sample} ({len(np.unique(ids_ref))} experts): "
+            f"normwise {err:.2e} cosine {cos:.7f}")
+        del y
+
+
+@pytest.mark.timeout(900)
+def test_layer_prefill8192_sampled(dev, decode_layer):
+    """8192 tokens with uniform logits through the full-size layer on the grouped path (the
+    automatic choice) and the decode kernels; the oracle checks a seeded sample of 512
+    tokens, which between them use nearly all 384 experts."""
+    wl_l, layer = decode_layer
+    _prefill_sampled(dev, layer, wl_l, S.WORKLOADS["prefill8192_uniform"], 512, 55, (None, DECODE))
+
+
+@pytest.mark.timeout(900)
+def test_layer_prefill32768_sampled(dev, decode_layer):
+    """The 32768-token matrix-core-bound shape (512 tokens per expert) on the grouped path,
+    as the bench runs it; the oracle checks a seeded sample of 64 tokens, and the one-term
+    FP8 mode is held to its own oracle mode on 16 of them."""
+    _, D = _mods()
+    wl_l, layer = decode_layer
+    wl = S.WORKLOADS["prefill32768_uniform"]
+    _prefill_sampled(dev, layer, wl_l, wl, 64, 77, (None,))
+    lg = S.router_logits(wl, 0, 0)
+    ids, w = layer.route_logits(torch.from_numpy(lg).to(dev))
+    x_bits = S.activations(wl, 0, 0)
+    sample = np.sort(np.random.default_rng(78).choice(x_bits.shape[0], size=16, replace=False))
+    ids_ref, w_ref = O.topk_softmax(lg[sample].astype(np.float64), 6)
+    y = layer.ffn(D.upload_bf16(x_bits, dev), ids, w, path=GROUPED_FP8)
+    torch.cuda.synchronize()
+    ref8 = O.expert_ffn_mx(x_bits[sample], ids_ref, w_ref, S.expert_source(wl_l), 384, 4096, 2880,
+                           "e4m3", 1)
+    err, cos = check_ffn(D.bf16_bits(y)[sample], ref8, "prefill32768 grouped_fp8")
+    log(f"prefill32768 grouped_fp8, sample of 16: normwise {err:.2e} cosine {cos:.7f}")
 
 
 # ------------------------------------------------------------------------------ edge cases
