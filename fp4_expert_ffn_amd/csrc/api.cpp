@@ -87,6 +87,7 @@ const char* moe_fp4_strerror(int status) {
     case MOE_FP4_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
     case MOE_FP4_ERR_WORKSPACE: return "workspace or packed buffer too small";
     case MOE_FP4_ERR_HIP: return "HIP runtime or launch error";
+    case MOE_FP4_ERR_TOO_LARGE: return "the call needs more memory than the static scratch of the no-allocation entry point (MOE_FP4_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -343,6 +344,55 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
   void* ffn_ws = static_cast<uint8_t*>(workspace) + moe_fp4_route_workspace_bytes(T, n_experts);
   return from_hip(ffn_impl(x, topk_ids, topk_w, T, k, static_cast<const uint8_t*>(packed),
                            n_experts, hidden, inter, y, ffn_ws, chosen, s));
+}
+
+// ---------------------------------------------------------------------------------------
+// The no-allocation variant of moe_fp4_moe_forward: its workspace is this file-scope device
+// array (each GPU the library runs on holds its own copy until the process ends). In host
+// code `scratch` names a host-side stand-in, not the device memory, so host code uses only
+// the per-device address that hipGetSymbolAddress returns, taken once per device on the
+// entry point's first call there (with that device current) and kept here.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = MOE_FP4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (nullptr when the device or the call fails).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+int moe_fp4_moe_forward_noalloc(const uint16_t* x, const uint16_t* w_router, int T, int hidden,
+                                int n_experts, int k, const void* packed, int inter,
+                                int32_t* topk_ids, float* topk_w, uint16_t* y, void* stream) {
+  if (!x || !w_router || !packed || !topk_ids || !topk_w || !y) return MOE_FP4_ERR_INVALID_ARG;
+  int st = check_topk_args(T, n_experts, k);
+  if (st != MOE_FP4_OK) return st;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (choose_path(MOE_FP4_PATH_AUTO, T, k, n_experts, hidden, inter) < 0) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(packed) || !aligned4(topk_ids) ||
+      !aligned4(topk_w) || !aligned16(y))
+    return MOE_FP4_ERR_MISALIGNED;
+  if (T == 0) return MOE_FP4_OK;
+  const size_t need = moe_fp4_moe_forward_workspace_bytes(T, k, n_experts, hidden, inter);
+  if (need == 0 || need > kNoAllocScratchBytes) return MOE_FP4_ERR_TOO_LARGE;
+  void* ws = scratch_address();
+  if (!ws) return MOE_FP4_ERR_HIP;
+  return moe_fp4_moe_forward(x, w_router, T, hidden, n_experts, k, packed, inter, topk_ids, topk_w,
+                             y, ws, kNoAllocScratchBytes, stream);
 }
 
 int moe_fp4_residual_init(const uint16_t* x, float* residual, int T, int hidden, void* stream) {

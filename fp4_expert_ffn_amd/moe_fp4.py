@@ -25,6 +25,8 @@ ERR_BAD_SHAPE = -2
 ERR_MISALIGNED = -3
 ERR_WORKSPACE = -4
 ERR_HIP = -5
+ERR_TOO_LARGE = -6
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_FP4_NOALLOC_SCRATCH_BYTES
 
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
 KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
@@ -66,6 +68,7 @@ _SIGNATURES = {
                                     _Z, _P]),
     "moe_fp4_moe_forward_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
+    "moe_fp4_moe_forward_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_act_quant_bytes": (ctypes.c_size_t, [_I, _I]),
@@ -255,6 +258,13 @@ def moe_fp4_moe_forward(x, w_router, T: int, hidden: int, n_experts: int, k: int
     _check(lib().moe_fp4_moe_forward(_ptr(x), _ptr(w_router), T, hidden, n_experts, k, _ptr(packed),
                                      inter, _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(workspace),
                                      workspace_bytes, _stream(stream)), "moe_fp4_moe_forward")
+
+
+def moe_fp4_moe_forward_noalloc(x, w_router, T: int, hidden: int, n_experts: int, k: int, packed,
+                                inter: int, topk_ids, topk_w, y, stream=None) -> None:
+    _check(lib().moe_fp4_moe_forward_noalloc(_ptr(x), _ptr(w_router), T, hidden, n_experts, k,
+                                             _ptr(packed), inter, _ptr(topk_ids), _ptr(topk_w),
+                                             _ptr(y), _stream(stream)), "moe_fp4_moe_forward_noalloc")
 
 
 def moe_fp4_validate_ids(topk_ids, T: int, k: int, n_experts: int, bad_count, stream=None) -> None:

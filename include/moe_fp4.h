@@ -14,8 +14,10 @@
  *
  * Conventions for every call:
  *  - All array arguments are DEVICE pointers (hipMalloc'd or equivalent) unless stated.
- *    The caller allocates and owns every buffer; the library allocates no device memory
- *    and keeps no per-call state.
+ *    The caller allocates and owns every buffer; no call allocates device memory, and
+ *    apart from the static scratch array of moe_fp4_moe_forward_noalloc (part of the
+ *    library's code object, MOE_FP4_NOALLOC_SCRATCH_BYTES per GPU) the library keeps no
+ *    state between calls.
  *  - bfloat16 values are passed as uint16_t bit patterns.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
  *    only enqueues work on that stream and returns; none synchronises with the host, so
@@ -48,6 +50,7 @@ extern "C" {
 #define MOE_FP4_ERR_MISALIGNED (-3)    /* a device pointer breaks the alignment rule above */
 #define MOE_FP4_ERR_WORKSPACE (-4)     /* workspace or packed buffer smaller than required */
 #define MOE_FP4_ERR_HIP (-5)           /* a HIP launch or runtime call failed */
+#define MOE_FP4_ERR_TOO_LARGE (-6)     /* needs more than the no-allocation entry point's scratch */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int moe_fp4_version(void);
@@ -235,6 +238,30 @@ int moe_fp4_moe_forward(const uint16_t* x, const uint16_t* w_router, int T, int 
                         int n_experts, int k, const void* packed, int inter, int32_t* topk_ids,
                         float* topk_w, uint16_t* y, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* For callers that cannot allocate device memory (code under stream or graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_fp4_moe_forward with no
+ * workspace argument. Its workspace is a static device array of
+ * MOE_FP4_NOALLOC_SCRATCH_BYTES bytes inside the library; every GPU the call runs on holds
+ * its own copy from the first call there until the process ends. The call allocates
+ * nothing (no hipMalloc, no allocating library routine); the caller still owns x, the
+ * router, the packed experts and the outputs, under the rules of moe_fp4_moe_forward, and
+ * gets the same results (the same kernels on the same workspace layout).
+ * The limit: moe_fp4_moe_forward_workspace_bytes(T, k, n_experts, hidden, inter) must not
+ * exceed MOE_FP4_NOALLOC_SCRATCH_BYTES, else MOE_FP4_ERR_TOO_LARGE and nothing is enqueued
+ * (at hidden 4096, inter 2880, 384 experts, top-6: up to 114 tokens per call).
+ * All calls on one GPU share that GPU's array, which keeps the last call's state (the
+ * route's synchronisation words carry from call to call as in moe_fp4_route): calls that
+ * may overlap on one GPU (different streams, different host threads) race and must be
+ * serialised by the caller. A batch-1 route give-up (see moe_fp4_route) marks the shared
+ * array as failed for the rest of the process: every later call then returns ids -1,
+ * weights 0 and y = 0.
+ * Errors: as moe_fp4_moe_forward, and TOO_LARGE; HIP if the array's address cannot be
+ * obtained on the current device. */
+#define MOE_FP4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_fp4_moe_forward_noalloc(const uint16_t* x, const uint16_t* w_router, int T, int hidden,
+                                int n_experts, int k, const void* packed, int inter,
+                                int32_t* topk_ids, float* topk_w, uint16_t* y, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Layer chaining, for stacks of MoE layers (a harness step of the multi-layer decode
