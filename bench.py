@@ -229,6 +229,14 @@ def main() -> int:
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-pass", action="store_true")
+    ap.add_argument("--prefetch", choices=["none", "oracle", "router"], default="none",
+                    help="stack16_decode: prefetch the next layer's experts into the memory-side "
+                         "cache on a side stream (oracle: true ids from a prior pass; router: the "
+                         "next layer's router on this layer's input)")
+    ap.add_argument("--prefetch-top", type=int, default=2,
+                    help="experts prefetched per layer (the top of the prediction)")
+    ap.add_argument("--prefetch-mats", type=int, default=3,
+                    help="matrices prefetched: bit 0 gate, 1 up, 2 down")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched (grouped GEMM) half of the metric in the decode run")
     ap.add_argument("--no-peaks", action="store_true",
@@ -542,9 +550,70 @@ def run_stack(args) -> int:
     w = torch.empty((1, k), dtype=torch.float32, device=dev)
     y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
 
+    # Speculative prefetch of layer l + 1's experts into the memory-side cache
+    # (moe_fp4_prefetch_experts on a side stream, forked once layer l's FFN is enqueued, so it
+    # runs while layer l + 1 routes): "oracle" prefetches the true top experts of the next
+    # layer (recorded in an untimed pass over the same tokens), "router" the top experts of
+    # the next layer's router applied to this layer's input, computed on the side stream.
+    pf = args.prefetch
+    top = max(1, min(k, args.prefetch_top))
+    side = torch.cuda.Stream() if pf != "none" else None
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    true_ids = None
+    pred_ids = torch.empty((L, k), dtype=torch.int32, device=dev)
+    pred_w = torch.empty((L, k), dtype=torch.float32, device=dev)
+    pred_ws = torch.empty(C.moe_fp4_route_workspace_bytes(1, E), dtype=torch.uint8, device=dev)
+
+    def prefetch_next(l: int, t: int, x_l) -> None:
+        """Enqueue the prefetch of layer l + 1's experts (and, for the router predictor, the
+        prediction on x_l) on the side stream; returns the event main must wait on before
+        overwriting x_l."""
+        if pf == "none" or l + 1 >= L:
+            return None
+        main = torch.cuda.current_stream()
+        ev_x = main.record_event()
+        ev_pred = None
+        if pf == "router":
+            side.wait_event(ev_x)
+            with torch.cuda.stream(side):  # its own route workspace: it runs beside the stack's
+                C.moe_fp4_route(x_l, layers[l + 1].w_router, 1, H, E, k, pred_ids[l + 1:l + 2],
+                                pred_w[l + 1:l + 2], pred_ws)
+            ev_pred = side.record_event()
+        return ev_pred
+
+    def prefetch_issue(l: int, t: int) -> None:
+        if pf == "none" or l + 1 >= L:
+            return
+        side.wait_stream(torch.cuda.current_stream())  # after layer l's FFN
+        ids_src = true_ids[t, l + 1] if pf == "oracle" else pred_ids[l + 1]
+        with torch.cuda.stream(side):
+            C.moe_fp4_prefetch_experts(ids_src, top, layers[l + 1].packed, E, H, I,
+                                       args.prefetch_mats, sink)
+
     def step(t: int) -> None:
         x = xs[t:t + 1]
         C.moe_fp4_residual_init(x, r, 1, H)
+        if pf != "none":
+            rc, rn = r, r2
+            pending = {}
+            for l, lay in enumerate(layers):
+                if l == 0:
+                    x_l = x
+                    lay.forward_fused(x, ids, w, y)
+                else:
+                    xn = xa if l % 2 == 0 else xb
+                    if l - 2 in pending and pending[l - 2] is not None:
+                        torch.cuda.current_stream().wait_event(pending[l - 2])
+                    lay.route_residual(rc, y, rn, xn, 1e-6, ids, w)
+                    x_l = xn
+                pending[l] = prefetch_next(l, t, x_l)
+                if l > 0:
+                    lay.ffn(x_l, ids, w, y)
+                    rc, rn = rn, rc
+                prefetch_issue(l, t)
+            C.moe_fp4_residual_rmsnorm(rc, y, xa, 1, H, 1e-6)
+            torch.cuda.current_stream().wait_stream(side)
+            return
         if args.stack_route == "separate":
             for l, lay in enumerate(layers):
                 lay.forward_fused(x, ids, w, y)
@@ -565,15 +634,37 @@ def run_stack(args) -> int:
             rc, rn = rn, rc
         C.moe_fp4_residual_rmsnorm(rc, y, xa, 1, H, 1e-6)  # the last layer's residual + norm
 
+    if pf == "oracle":
+        # the true ids of every (token, layer) of the timed tokens, from one untimed pass of
+        # the same stack without prefetch
+        true_ids = torch.empty((W + 2 * K, L, k), dtype=torch.int32, device=dev)
+        pf_saved, pf = pf, "none"
+        for t in range(W + 2 * K):
+            x = xs[t:t + 1]
+            C.moe_fp4_residual_init(x, r, 1, H)
+            rc, rn = r, r2
+            for l, lay in enumerate(layers):
+                if l == 0:
+                    lay.forward_fused(x, ids, w, y)
+                else:
+                    xn = xa if l % 2 == 0 else xb
+                    lay.route_residual(rc, y, rn, xn, 1e-6, ids, w)
+                    lay.ffn(xn, ids, w, y)
+                    rc, rn = rn, rc
+                true_ids[t, l].copy_(ids[0])
+        torch.cuda.synchronize()
+        pf = pf_saved
+        log("oracle predictor: true ids recorded")
+
     for t in range(W):
         step(t)
     torch.cuda.synchronize()
     graph = None
     if args.mode == "graph":
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
+        with torch.cuda.graph(graph, stream=cap):
             for t in range(W, W + K):
                 step(t)
         torch.cuda.synchronize()
@@ -624,12 +715,42 @@ def run_stack(args) -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": L, "stack_route": args.stack_route, "hidden": H,
                    "intermediate": I, "experts": E,
-                   "top_k": k, "batch_tokens": 1, "launch": args.mode, "parallelism": "none (1 GPU)"},
+                   "top_k": k, "batch_tokens": 1, "launch": args.mode, "parallelism": "none (1 GPU)",
+                   "prefetch": pf, "prefetch_top": top if pf != "none" else 0,
+                   "prefetch_matrices": args.prefetch_mats if pf != "none" else 0},
         "algorithmic_gbps": round(token_bytes * K / elapsed_s / 1e9, 1),
         "hbm_frac_step": round(token_bytes * K / elapsed_s / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_step": token_bytes,
         "kernels": kernels,
     }
+    if pf == "router":
+        # how often the next layer's router on this layer's input names one of the next
+        # layer's true experts (untimed, 20 tokens, everything on one stream)
+        hits = total = 0
+        for t in range(20):
+            x = xs[t:t + 1]
+            C.moe_fp4_residual_init(x, r, 1, H)
+            rc, rn = r, r2
+            x_l = x
+            for l, lay in enumerate(layers):
+                if l > 0:
+                    xn = xa if l % 2 == 0 else xb
+                    lay.route_residual(rc, y, rn, xn, 1e-6, ids, w)
+                    x_l = xn
+                else:
+                    lay.route(x, ids, w)
+                if l > 0:
+                    truth = set(ids[0].tolist())
+                    hits += len(truth & set(pred_ids[l, :top].tolist()))
+                    total += top
+                lay.ffn(x_l, ids, w, y)
+                if l > 0:
+                    rc, rn = rn, rc
+                if l + 1 < L:
+                    C.moe_fp4_route(x_l, layers[l + 1].w_router, 1, H, E, k, pred_ids[l + 1:l + 2],
+                                    pred_w[l + 1:l + 2], pred_ws)
+        out["prefetch_hit_rate"] = round(hits / max(total, 1), 4)
+        log(f"router predictor: {hits} of {total} predicted experts were among the next layer's top-{k}")
     print(json.dumps(out), flush=True)
     return 0
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["api.cpp", "kernels_pack.hip", "kernels_route.hip", "kernels_ffn.hip",
            "kernels_batched.hip", "kernels_norm.hip", "kernels_probe.hip", "kernels_small_m.hip",
-           "kernels_fp8.hip"]
+           "kernels_fp8.hip", "kernels_prefetch.hip"]
 
 # Packed-fp32 VALU ops are switched off for the device code: the compiler otherwise forms
 # them from ordinary float code, and this library does not rely on them.

@@ -412,6 +412,19 @@ int moe_fp4_residual_rmsnorm(float* residual, const uint16_t* y, uint16_t* x_out
                                           static_cast<hipStream_t>(stream)));
 }
 
+int moe_fp4_prefetch_experts(const int32_t* ids, int n_ids, const void* packed, int n_experts,
+                             int hidden, int inter, int matrices, uint32_t* sink, void* stream) {
+  if (!ids || !packed || !sink || n_ids < 0 || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;
+  if (matrices < 1 || matrices > 7) return MOE_FP4_ERR_INVALID_ARG;
+  if (n_ids > (1 << 16)) return MOE_FP4_ERR_INVALID_ARG;
+  if (!valid_dim(hidden) || !valid_dim(inter)) return MOE_FP4_ERR_BAD_SHAPE;
+  if (!aligned4(ids) || !aligned16(packed) || !aligned4(sink)) return MOE_FP4_ERR_MISALIGNED;
+  if (n_ids == 0) return MOE_FP4_OK;
+  return from_hip(launch_prefetch_experts(ids, n_ids, static_cast<const uint8_t*>(packed), n_experts,
+                                          hidden, inter, matrices, sink,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts, int32_t* bad_count,
                          void* stream) {
   if (!topk_ids || !bad_count || T < 0 || k < 1 || n_experts <= 0) return MOE_FP4_ERR_INVALID_ARG;

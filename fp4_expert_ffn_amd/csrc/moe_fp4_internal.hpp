@@ -22,7 +22,7 @@ enum KernelKind { kKindPack = 0, kKindRouterGemv = 1, kKindTopk = 2, kKindGateUp
                   kKindBatchedQuant = 7, kKindBatchedGateUp = 8, kKindBatchedDown = 9,
                   kKindBatchedCombine = 10, kKindNorm = 11,
                   kKindProbeStream = 12, kKindProbeMfma = 13, kKindSmallGateUp = 14,
-                  kKindSmallDown = 15, kKindFp8Gemv = 16 };
+                  kKindSmallDown = 15, kKindFp8Gemv = 16, kKindPrefetch = 17 };
 
 // ----------------------------------------------------------------------------------------
 // Packed expert layout (the output of moe_fp4_pack). An expert is three matrices (gate
@@ -197,6 +197,13 @@ hipError_t launch_debug_act_quant(const uint16_t* x, int T, int H, int terms, vo
 
 hipError_t launch_debug_dequant(const uint8_t* packed, int hidden, int inter, int expert,
                                 int matrix, float* out, hipStream_t s);
+
+// Reads the chosen matrices (bit 0 gate, 1 up, 2 down; codes and scales) of the experts
+// ids[0 .. n_ids - 1] of a packed buffer with cached loads (ids outside [0, n_experts)
+// skipped); writes nothing except, practically never, one word of sink.
+hipError_t launch_prefetch_experts(const int32_t* ids, int n_ids, const uint8_t* packed,
+                                   int n_experts, int hidden, int inter, int matrices,
+                                   uint32_t* sink, hipStream_t s);
 
 hipError_t launch_validate_ids(const int32_t* ids, int T, int k, int n_experts, int32_t* bad,
                                hipStream_t s);

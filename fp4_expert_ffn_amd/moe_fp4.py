@@ -31,7 +31,8 @@ NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_FP4_NOALLOC_SCRATCH_BYTES
 KERNEL_PACK, KERNEL_ROUTER_GEMV, KERNEL_TOPK, KERNEL_GATE_UP, KERNEL_DOWN_COMBINE = range(5)
 KERNEL_NAMES = ("pack", "router_gemv", "topk", "gate_up", "down_combine", "route_decode",
                 "grouped_sort", "grouped_quant", "grouped_gate_up", "grouped_down", "grouped_combine",
-                "norm", "probe_stream", "probe_mfma", "small_m_gate_up", "small_m_down", "fp8_gemv")
+                "norm", "probe_stream", "probe_mfma", "small_m_gate_up", "small_m_down", "fp8_gemv",
+                "prefetch")
 PROBE_MFMA_CHAINS = 8  # independent block-scaled MFMAs per wavefront per loop iteration
 
 
@@ -70,6 +71,7 @@ _SIGNATURES = {
     "moe_fp4_moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _Z, _P]),
     "moe_fp4_moe_forward_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P]),
     "moe_fp4_validate_ids": (_I, [_P, _I, _I, _I, _P, _P]),
+    "moe_fp4_prefetch_experts": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_dequant": (_I, [_P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_fp4_debug_act_quant_bytes": (ctypes.c_size_t, [_I, _I]),
     "moe_fp4_fp8_packed_bytes": (ctypes.c_size_t, [_I, _I]),
@@ -265,6 +267,13 @@ def moe_fp4_moe_forward_noalloc(x, w_router, T: int, hidden: int, n_experts: int
     _check(lib().moe_fp4_moe_forward_noalloc(_ptr(x), _ptr(w_router), T, hidden, n_experts, k,
                                              _ptr(packed), inter, _ptr(topk_ids), _ptr(topk_w),
                                              _ptr(y), _stream(stream)), "moe_fp4_moe_forward_noalloc")
+
+
+def moe_fp4_prefetch_experts(ids, n_ids: int, packed, n_experts: int, hidden: int, inter: int,
+                             matrices: int, sink, stream=None) -> None:
+    _check(lib().moe_fp4_prefetch_experts(_ptr(ids), n_ids, _ptr(packed), n_experts, hidden, inter,
+                                          matrices, _ptr(sink), _stream(stream)),
+           "moe_fp4_prefetch_experts")
 
 
 def moe_fp4_validate_ids(topk_ids, T: int, k: int, n_experts: int, bad_count, stream=None) -> None:

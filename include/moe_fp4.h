@@ -342,6 +342,21 @@ int moe_fp4_shared_expert(const uint16_t* x, int T, const void* gate, const void
                           const void* down, int hidden, int inter, uint16_t* y, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Speculative expert prefetch, opt-in ([8GB-GPU], section 提速之路：v1 到 v4, v4: the router
+ * of layer l + 1 applied to layer l's input predicts the next layer's experts, which are
+ * fetched ahead of need). The experts are resident in HBM here, so this reads the chosen
+ * matrices of the experts ids[0 .. n_ids - 1] (device int32; ids outside [0, n_experts)
+ * skipped) of a packed buffer with cached loads, which leaves them in the memory-side cache
+ * every HBM read passes through (256 MB on MI355X), for a later FFN call to read from there.
+ * matrices: bit 0 gate, bit 1 up, bit 2 down (codes and scales of each). Nothing is written
+ * except, practically never, the device uint32 *sink (it keeps the loads alive; its
+ * contents carry no meaning). Meant to run on a second stream while the HBM is idle (the
+ * batch-1 route); the FFN's results do not depend on it. n_ids = 0 is a no-op.
+ * Errors: INVALID_ARG (null, n_ids < 0 or > 65536, matrices not in 1..7), BAD_SHAPE,
+ * MISALIGNED (ids and sink 4-byte, packed 16-byte), HIP. */
+int moe_fp4_prefetch_experts(const int32_t* ids, int n_ids, const void* packed, int n_experts,
+                             int hidden, int inter, int matrices, uint32_t* sink, void* stream);
+
 /* Debug helper: counts the entries of topk_ids [T x k] outside [0, n_experts) into
  * *bad_count (a device int32 that this call overwrites). */
 int moe_fp4_validate_ids(const int32_t* topk_ids, int T, int k, int n_experts,
@@ -422,7 +437,8 @@ int moe_fp4_debug_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32_t* si
 #define MOE_FP4_KERNEL_SMALL_M_GATE_UP 14
 #define MOE_FP4_KERNEL_SMALL_M_DOWN 15
 #define MOE_FP4_KERNEL_FP8_GEMV 16     /* moe_fp4_fp8_linear, _swiglu, _shared_expert */
-#define MOE_FP4_KERNEL_KINDS 17
+#define MOE_FP4_KERNEL_PREFETCH 17     /* moe_fp4_prefetch_experts */
+#define MOE_FP4_KERNEL_KINDS 18
 
 int moe_fp4_timing_enable(int enable);
 int moe_fp4_timing_reset(void);

@@ -231,7 +231,8 @@ def test_probe_helpers_argument_checks(L):
     assert g(0, 1, (1 << 20) + 1, A, None) == C.ERR_INVALID_ARG
     assert g(4, 1, 1, MIS4, None) == C.ERR_MISALIGNED
     assert C.PROBE_MFMA_CHAINS == 8
-    assert len(C.KERNEL_NAMES) == 17
+    kinds = int(re.search(r"#define MOE_FP4_KERNEL_KINDS (\d+)", open(HEADER).read()).group(1))
+    assert len(C.KERNEL_NAMES) == kinds
 
 
 def test_route_residual_argument_checks(L):
@@ -276,3 +277,15 @@ def test_route_status_reset_argument_checks(L):
     assert L.moe_fp4_route_reset(MIS, 1 << 14, None) == C.ERR_MISALIGNED
     assert L.moe_fp4_route_reset(A, 100, None) == C.ERR_WORKSPACE
     assert L.moe_fp4_debug_route_spin_limit(-1) == C.OK  # the default bound
+
+
+def test_prefetch_argument_checks(L):
+    f = L.moe_fp4_prefetch_experts
+    assert f(A, 0, A, 384, 4096, 2880, 3, A, None) == C.OK          # no ids: nothing enqueued
+    assert f(None, 2, A, 384, 4096, 2880, 3, A, None) == C.ERR_INVALID_ARG
+    assert f(A, -1, A, 384, 4096, 2880, 3, A, None) == C.ERR_INVALID_ARG
+    assert f(A, 2, A, 384, 4096, 2880, 0, A, None) == C.ERR_INVALID_ARG
+    assert f(A, 2, A, 384, 4096, 2880, 8, A, None) == C.ERR_INVALID_ARG
+    assert f(A, 2, A, 384, 4100, 2880, 3, A, None) == C.ERR_BAD_SHAPE   # 4100 % 32 != 0
+    assert f(MIS4, 2, A, 384, 4096, 2880, 3, A, None) == C.ERR_MISALIGNED
+    assert f(A, 2, MIS, 384, 4096, 2880, 3, A, None) == C.ERR_MISALIGNED

@@ -62,3 +62,32 @@ def test_mfma_loop_runs(C, fmt):
     C.moe_fp4_timing_reset()
     assert n == 1 and ms > 0
     assert int(sink[0]) == 7
+
+
+def test_prefetch_experts_reads_only(C):
+    """moe_fp4_prefetch_experts only reads: the packed weights, the FFN's results on them and
+    the sink are unchanged, for every matrix selection, with invalid ids skipped."""
+    import numpy as np
+
+    from fp4_expert_ffn_amd import device as D
+    from synth import moe_inputs as S
+
+    dev = torch.device("cuda:0")
+    wl = S.small_workload(512, 384, 12, 6, 3, wid=990)
+    packed = D.upload_experts(S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter, dev)
+    before = packed.clone()
+    layer = D.MoeFp4Layer(packed, wl.n_experts, wl.hidden, wl.inter, wl.k)
+    rng = np.random.default_rng(990)
+    ids = torch.from_numpy(np.stack([rng.permutation(12)[:6] for _ in range(3)]).astype(np.int32)).to(dev)
+    w = torch.from_numpy(rng.random((3, 6)).astype(np.float32)).to(dev)
+    x = D.upload_bf16(S.activations(wl, 0, 0), dev)
+    y0 = layer.ffn(x, ids, w).clone()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    pf_ids = torch.tensor([3, -1, 11, 12, 0], dtype=torch.int32, device=dev)
+    for mats in range(1, 8):
+        C.moe_fp4_prefetch_experts(pf_ids, 5, packed, 12, wl.hidden, wl.inter, mats, sink)
+    y1 = layer.ffn(x, ids, w)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, before)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.all(sink == 0)
