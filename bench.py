@@ -485,18 +485,18 @@ def grouped_measure(torch, C, D, S, layer, wl, dev, K: int, W: int, terms: int) 
         step(i)
     torch.cuda.synchronize()
     C.moe_fp4_timing_enable(False)
-    kern = {}
+    kern = {}  # GPU time per step of each kernel kind (the split sort is three launches)
     for kind, name in enumerate(C.KERNEL_NAMES):
         n, ms = C.moe_fp4_timing_read(kind)
         if n:
-            kern[name] = round(ms * 1e3 / n, 2)
+            kern[name] = round(ms * 1e3 / K, 2)
     C.moe_fp4_timing_reset()
     out = {"tokens": T, "steps": K, "ms_per_step": round(step_s * 1e3, 4),
            "tflops": round(flops / step_s / 1e12, 1),
            "frac_fp4_peak": round(flops / step_s / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4),
            "algorithmic_gbps": round(step_bytes / step_s / 1e9, 1),
            "frac_hbm": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
-           "distinct_experts": round(d_avg, 1), "kernel_avg_us": kern}
+           "distinct_experts": round(d_avg, 1), "kernel_us_per_step": kern}
     gu = kern.get("grouped_gate_up")
     if gu:
         gflops = pairs * 4.0 * H * I  # gate and up

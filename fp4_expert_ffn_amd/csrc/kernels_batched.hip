@@ -77,6 +77,8 @@ constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
 constexpr int kMSub = kBlockRows / 16;  // 16-row MFMA subtiles per M-block
 constexpr int kAPitch = 272;            // LDS bytes per staged A row: hi 128 | lo 128 | pad 16
 constexpr int kSortThreads = 1024;
+constexpr int kSortMaxGroups = 256;        // workgroups of the split sort
+constexpr long kSortSplitMinPairs = 8192;  // pairs from which the sort is split (measured)
 
 // ---------------------------------------------------------------------------------------
 // MXFP8 (E4M3) encoding of one 32-element block, two terms.
@@ -221,6 +223,100 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(
   for (int p = tid; p < P; p += kSortThreads) {
     const int e = ids[p];
     if (e >= 0 && e < E) perm[atomicAdd(&cur[e], 1)] = p;
+  }
+}
+
+// The same sort over many workgroups, for large batches (the one-workgroup sort reads every
+// id and writes every perm entry from one compute unit: 175 us at 196,608 pairs). Three
+// launches: each of G workgroups histograms a contiguous range of `chunk` pairs into
+// cnt[g][E]; one workgroup sums the histograms per expert, scans, writes the offsets and the
+// block table (as sort_kernel) and turns cnt[g][e] into workgroup g's first sorted row for
+// expert e; each workgroup then scatters its range through LDS cursors starting there.
+constexpr int kSortWGThreads = 256;
+
+__global__ __launch_bounds__(kSortWGThreads) void sort_count_kernel(const int32_t* __restrict__ ids,
+                                                                    int P, int E, int chunk,
+                                                                    int32_t* __restrict__ cnt) {
+  extern __shared__ int hist[];  // E
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortWGThreads) hist[e] = 0;
+  __syncthreads();
+  const long p0 = (long)blockIdx.x * chunk;
+  const long p1 = min((long)P, p0 + chunk);
+  for (long p = p0 + tid; p < p1; p += kSortWGThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kSortWGThreads) cnt[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(
+    int G, int E, int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ blk_expert, int32_t* __restrict__ blk_row0,
+    int32_t* __restrict__ blk_rows, int32_t* __restrict__ n_blocks) {
+  extern __shared__ int sm[];
+  int* tot = sm;              // E
+  int* sbuf = sm + E;         // kSortThreads
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) {
+    int t = 0;
+    for (int g = 0; g < G; ++g) t += cnt[(size_t)g * E + e];
+    tot[e] = t;
+  }
+  __syncthreads();
+  const int per = (E + kSortThreads - 1) / kSortThreads;
+  int rows = 0, blks = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      rows += tot[e];
+      blks += (tot[e] + kBlockRows - 1) / kBlockRows;
+    }
+  }
+  int row_base = block_exclusive_scan(rows, sbuf);
+  int blk_base = block_exclusive_scan(blks, sbuf);
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      offsets[e] = row_base;
+      const int n = tot[e];
+      const int nb = (n + kBlockRows - 1) / kBlockRows;
+      for (int b = 0; b < nb; ++b) {
+        blk_expert[blk_base + b] = e;
+        blk_row0[blk_base + b] = row_base + b * kBlockRows;
+        blk_rows[blk_base + b] = min(kBlockRows, n - b * kBlockRows);
+      }
+      // workgroup g's first row for expert e: after the rows of the workgroups before it
+      int start = row_base;
+      for (int g = 0; g < G; ++g) {
+        const int c = cnt[(size_t)g * E + e];
+        cnt[(size_t)g * E + e] = start;
+        start += c;
+      }
+      row_base += n;
+      blk_base += nb;
+    }
+  }
+  if (tid == kSortThreads - 1) {
+    offsets[E] = row_base;
+    n_blocks[0] = blk_base;
+  }
+}
+
+__global__ __launch_bounds__(kSortWGThreads) void sort_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                      int P, int E, int chunk,
+                                                                      const int32_t* __restrict__ start,
+                                                                      int32_t* __restrict__ perm) {
+  extern __shared__ int cur[];  // E
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortWGThreads) cur[e] = start[(size_t)blockIdx.x * E + e];
+  __syncthreads();
+  const long p0 = (long)blockIdx.x * chunk;
+  const long p1 = min((long)P, p0 + chunk);
+  for (long p = p0 + tid; p < p1; p += kSortWGThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) perm[atomicAdd(&cur[e], 1)] = (int32_t)p;
   }
 }
 
@@ -894,6 +990,7 @@ BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter)
   L.blk_row0 = take(nb_max * 4);
   L.blk_rows = take(nb_max * 4);
   L.n_blocks = take(4);
+  L.sort_cnt = (long)P >= kSortSplitMinPairs ? take((size_t)kSortMaxGroups * (size_t)n_experts * 4) : 0;
   L.xhi = take((size_t)T * Hp);
   L.xlo = take((size_t)T * Hp);
   L.xshi = take((size_t)T * Hp / kBlock);
@@ -926,10 +1023,28 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
   const long P = (long)T * k;
   if (P > 0x7fffffffL) return hipErrorInvalidValue;
 
-  const uint32_t sort_lds = (uint32_t)((3 * n_experts + kSortThreads) * sizeof(int));
-  hipError_t e = launch_kernel(kKindBatchedSort, sort_kernel, dim3(1), dim3(kSortThreads), sort_lds, s,
-                               ids, (int)P, n_experts, offsets, perm, bexp, brow0, brows, nblk);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (P < kSortSplitMinPairs) {
+    const uint32_t sort_lds = (uint32_t)((3 * n_experts + kSortThreads) * sizeof(int));
+    e = launch_kernel(kKindBatchedSort, sort_kernel, dim3(1), dim3(kSortThreads), sort_lds, s, ids,
+                      (int)P, n_experts, offsets, perm, bexp, brow0, brows, nblk);
+    if (e != hipSuccess) return e;
+  } else {  // many workgroups, each over `chunk` consecutive pairs
+    const int G = (int)std::min<long>(kSortMaxGroups, (P + 1023) / 1024);
+    const int chunk = (int)((P + G - 1) / G);
+    int32_t* cnt = reinterpret_cast<int32_t*>(ws + B.sort_cnt);
+    const uint32_t hist_lds = (uint32_t)(n_experts * sizeof(int));
+    e = launch_kernel(kKindBatchedSort, sort_count_kernel, dim3(G), dim3(kSortWGThreads), hist_lds, s,
+                      ids, (int)P, n_experts, chunk, cnt);
+    if (e != hipSuccess) return e;
+    const uint32_t scan_lds = (uint32_t)((n_experts + kSortThreads) * sizeof(int));
+    e = launch_kernel(kKindBatchedSort, sort_scan_kernel, dim3(1), dim3(kSortThreads), scan_lds, s, G,
+                      n_experts, cnt, offsets, bexp, brow0, brows, nblk);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(kKindBatchedSort, sort_scatter_kernel, dim3(G), dim3(kSortWGThreads), hist_lds,
+                      s, ids, (int)P, n_experts, chunk, cnt, perm);
+    if (e != hipSuccess) return e;
+  }
 
   const long qn = (long)T * (B.Hp / kBlock);
   e = launch_kernel(kKindBatchedQuant, quant_x_kernel<TERMS>, dim3((unsigned)((qn + 255) / 256)), dim3(256), 0,

@@ -739,7 +739,7 @@ def test_slot_permutation_is_bit_identical(dev, small_layer, path):
 
 @pytest.mark.parametrize("path", [None, DECODE, GROUPED, SMALL_M, GROUPED_FP8],
                          ids=["auto", "decode", "grouped", "small_m", "grouped_fp8"])
-@pytest.mark.parametrize("T", [1, 17, 64, 65, 300, 1024])
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 300, 1024, 1400])
 def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
     """Same input five times: bit-identical outputs and no NaN/Inf, at token counts on both
     sides of 64."""
