@@ -32,7 +32,7 @@ namespace {
 #define MOE_FP4_DC_WAVES 16     // wavefronts per down/combine tile
 #endif
 #ifndef MOE_FP4_DC_BATCH
-#define MOE_FP4_DC_BATCH 5      // (expert, chunk) steps loaded per wave before use
+#define MOE_FP4_DC_BATCH 3      // (expert, chunk) steps loaded per wave before use
 #endif
 
 constexpr int kDCWaves = MOE_FP4_DC_WAVES;
