@@ -463,8 +463,12 @@ __device__ __forceinline__ i32x8_t b_operand(uint4 w) {
   return i32x8_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
 }
 
-// One B word for this lane: 16 code bytes and the scale byte (zero / 1 past K or past the
-// matrix rows).
+// One B word for this lane: 16 code bytes and the scale byte. Past K the lane reads another
+// word of the tile and its values are not masked here: a select at load time would wait for
+// the load at once (every chunk would then wait for the B loads it has just issued). They
+// need no masking: the A data of those K blocks is zero, FP4 codes are finite, and the
+// scale is replaced by 1 where it is used (a NaN scale byte would poison the zero products).
+// Tiles past the matrix rows read the last tile; their columns are never stored.
 struct BWord {
   uint4 w;
   uint32_t s;
@@ -472,18 +476,13 @@ struct BWord {
 
 template <bool NT>
 __device__ __forceinline__ BWord load_b(const uint8_t* codes, const uint8_t* scales, int c,
-                                        int KB, bool on) {
+                                        int KB) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const bool ok = on && 4 * c + g < KB;
   const long w = (4 * c + g < KB) ? 64L * c + lane : 64L * c;  // past K: any valid word
   BWord b;
   b.w = ld_w16<NT>(codes + 16 * w);
   b.s = scales[w];
-  if (!ok) {
-    b.w = make_uint4(0, 0, 0, 0);
-    b.s = 127u;
-  }
   return b;
 }
 
@@ -503,13 +502,13 @@ struct BSet {
 template <int NB, bool NT>
 __device__ __forceinline__ BSet<NB> load_bset(const BPtrs& p, int c, int KB) {
   BSet<NB> r;
-  r.w0 = load_b<NT>(p.c0, p.s0, c, KB, p.on0);
+  r.w0 = load_b<NT>(p.c0, p.s0, c, KB);
   r.w1 = r.w0;
   r.w2 = r.w0;
   r.w3 = r.w0;
-  if constexpr (NB > 1) r.w1 = load_b<NT>(p.c1, p.s1, c, KB, p.on1);
-  if constexpr (NB > 2) r.w2 = load_b<NT>(p.c2, p.s2, c, KB, p.on2);
-  if constexpr (NB > 3) r.w3 = load_b<NT>(p.c3, p.s3, c, KB, p.on3);
+  if constexpr (NB > 1) r.w1 = load_b<NT>(p.c1, p.s1, c, KB);
+  if constexpr (NB > 2) r.w2 = load_b<NT>(p.c2, p.s2, c, KB);
+  if constexpr (NB > 3) r.w3 = load_b<NT>(p.c3, p.s3, c, KB);
   return r;
 }
 
@@ -519,16 +518,17 @@ struct Acc {
   f32x4_t a[kMSub][NB];
 };
 
+// sb: the B word's scale byte, or 127 (scale 1) past K.
 __device__ __forceinline__ void mfma2(f32x4_t& acc, const i32x8_t& ahi, const i32x8_t& alo,
-                                      const BWord& b, int sw_hi, int sw_lo) {
+                                      const BWord& b, int sw_hi, int sw_lo, int sb) {
   const i32x8_t bq = b_operand(b.w);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bq, acc, 0, 4, 0, sw_hi, 0, (int)b.s);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, (int)b.s);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bq, acc, 0, 4, 0, sw_hi, 0, sb);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, sb);
 }
 
-__device__ __forceinline__ void mfma1(f32x4_t& acc, const i32x8_t& ahi, const BWord& b, int sw_hi) {
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, b_operand(b.w), acc, 0, 4, 0, sw_hi, 0,
-                                                         (int)b.s);
+__device__ __forceinline__ void mfma1(f32x4_t& acc, const i32x8_t& ahi, const BWord& b, int sw_hi,
+                                      int sb) {
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, b_operand(b.w), acc, 0, 4, 0, sw_hi, 0, sb);
 }
 
 // BSETS 2 or 3: the K loop runs BSETS chunks per trip with BSETS B sets used in turn and
@@ -576,6 +576,8 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
     const uint32_t h0 = 4 * (C) + (g >> 1) < cx.KB ? ~0u : 0u;                                  \
     const uint32_t h1 = 4 * (C) + 2 + (g >> 1) < cx.KB ? ~0u : 0u;                              \
     const bool s_ok = 4 * (C) + g < cx.KB;                                                      \
+    const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;                 \
+    const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;                 \
     if (any_on) {                                                                               \
       _Pragma("unroll") for (int m = 0; m < kMSub; ++m) {                                       \
         if (16 * m < rows) { /* wave-uniform */                                                 \
@@ -586,15 +588,15 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
             const i32x8_t alo = PAIR ? a_operand(A, m, lane, true, h0, h1)                      \
                                      : a_operand_br(A, m, lane, true, h0, h1);                  \
             const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;                   \
-            mfma2(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo);                                  \
-            if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo);            \
-            if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo);            \
-            if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo);            \
+            mfma2(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo, sb0);                             \
+            if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo, sb1);       \
+            if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo, sb2);       \
+            if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo, sb3);       \
           } else {                                                                              \
-            mfma1(acc.a[m][0], ahi, BS.w0, sw_hi);                                              \
-            if constexpr (NB > 1) mfma1(acc.a[m][1], ahi, BS.w1, sw_hi);                        \
-            if constexpr (NB > 2) mfma1(acc.a[m][2], ahi, BS.w2, sw_hi);                        \
-            if constexpr (NB > 3) mfma1(acc.a[m][3], ahi, BS.w3, sw_hi);                        \
+            mfma1(acc.a[m][0], ahi, BS.w0, sw_hi, sb0);                                         \
+            if constexpr (NB > 1) mfma1(acc.a[m][1], ahi, BS.w1, sw_hi, sb1);                   \
+            if constexpr (NB > 2) mfma1(acc.a[m][2], ahi, BS.w2, sw_hi, sb2);                   \
+            if constexpr (NB > 3) mfma1(acc.a[m][3], ahi, BS.w3, sw_hi, sb3);                   \
           }                                                                                     \
         }                                                                                       \
       }                                                                                         \
