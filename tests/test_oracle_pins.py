@@ -376,6 +376,43 @@ def test_mx_round_e4m3_matches_torch_float8():
     assert np.array_equal(O.mx_round(vals, "e4m3"), ref)
 
 
+def test_mx_round_e2m3_hand_derived_midpoints():
+    """E2M3 (FP6) rounding on hand-derived values: grid points stay, the midpoint between two
+    neighbouring codes goes to the even code (0.0625 -> 0, 0.1875 -> 0.25, 0.9375 -> 1,
+    1.9375 -> 2, 2.125 -> 2, 2.375 -> 2.5, 3.875 -> 4, 4.25 -> 4, 4.75 -> 5, 7.25 -> 7), values
+    just off a midpoint go to the nearer code, and negative values mirror."""
+    g = O.mx_grid("e2m3")
+    assert np.array_equal(O.mx_round(g, "e2m3"), g)
+    mids = np.array([0.0625, 0.1875, 0.9375, 1.9375, 2.125, 2.375, 3.875, 4.25, 4.75, 7.25])
+    want = np.array([0.0, 0.25, 1.0, 2.0, 2.0, 2.5, 4.0, 4.0, 5.0, 7.0])
+    assert np.array_equal(O.mx_round(mids, "e2m3"), want)
+    assert np.array_equal(O.mx_round(-mids, "e2m3"), -want)
+    up = np.array([0.0625, 2.125, 7.25]) * (1 + 2.0 ** -20)
+    assert np.array_equal(O.mx_round(up, "e2m3"), [0.125, 2.25, 7.5])
+    down = np.array([0.1875, 2.375, 4.75]) * (1 - 2.0 ** -20)
+    assert np.array_equal(O.mx_round(down, "e2m3"), [0.125, 2.25, 4.5])
+    assert np.array_equal(O.mx_round(np.array([1.2, 5.2, 0.3]), "e2m3"), [1.25, 5.0, 0.25])
+
+
+def test_mx_e2m3_scale_rule_and_two_terms_hand_derived():
+    """The scale rule for E2M3 (largest value 7.5 = 1.875 * 4) and one two-term block worked
+    by hand: the block [1.0, 0.3, 0, ...] takes 2^-2 (7.5 / 4 = 1.875 >= 1 > 0.9375), 0.3 / 0.25
+    = 1.2 rounds to 1.25, so hi = 0.3125; the residual -0.0125 takes 2^-9 (7.5 * 2^-9 >= 0.0125
+    > 7.5 * 2^-10) and -0.0125 * 2^9 = -6.4 rounds to -6.5, so lo = -6.5 * 2^-9."""
+    assert O.mx_scale_exponent(7.5, 7.5) == 0
+    assert O.mx_scale_exponent(7.6, 7.5) == 1
+    assert O.mx_scale_exponent(1.0, 7.5) == -2
+    assert O.mx_scale_exponent(1.875, 7.5) == -2
+    assert O.mx_scale_exponent(1.876, 7.5) == -1
+    assert O.mx_scale_exponent(0.9375, 7.5) == -3
+    v = np.zeros((1, 32))
+    v[0, 0], v[0, 1] = 1.0, 0.3
+    q1 = O.mx_quantize(v, "e2m3", 1)
+    assert q1[0, 0] == 1.0 and q1[0, 1] == 0.3125 and np.all(q1[0, 2:] == 0.0)
+    q2 = O.mx_quantize(v, "e2m3", 2)
+    assert q2[0, 0] == 1.0 and q2[0, 1] == 0.3125 - 6.5 * 2.0 ** -9
+
+
 def test_mx_scale_exponent_is_the_smallest_fitting_power():
     for n in (-20, -8, 0, 7):
         top = np.ldexp(448.0, n)
