@@ -75,7 +75,6 @@ constexpr int kBThreads = kBWaves * 64;
 constexpr int kNS = 2;                  // 16-row weight tiles per wave (per matrix)
 constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
 constexpr int kMSub = kBlockRows / 16;  // 16-row MFMA subtiles per M-block
-constexpr int kAPitch = 272;            // LDS bytes per staged A row: hi 128 | lo 128 | pad 16
 constexpr int kSortThreads = 1024;
 constexpr int kSortMaxGroups = 256;        // workgroups of the split sort
 constexpr long kSortSplitMinPairs = 8192;  // pairs from which the sort is split (measured)
@@ -148,6 +147,109 @@ __device__ __forceinline__ void mx8_encode_block(const float (&v)[32], uint4& h0
   l0 = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   l1 = make_uint4(lw[4], lw[5], lw[6], lw[7]);
   sl = (uint32_t)(Xl + 127);
+}
+
+// ---------------------------------------------------------------------------------------
+// MXFP6 (E2M3) encoding of one 32-element block, two terms: the default activation format
+// of the two-term grouped path. E2M3 codes enter the block-scaled MFMA at the FP4 rate
+// (twice the FP8 rate), and take 24 bytes per block instead of 32.
+// ---------------------------------------------------------------------------------------
+constexpr int kFmtE4M3 = 0;  // activation formats: the MFMA's A-format codes
+constexpr int kFmtE2M3 = 2;
+#ifndef MOE_FP4_GROUPED_FMT
+#define MOE_FP4_GROUPED_FMT 2  // two-term grouped path: 2 = E2M3 (FP6), 0 = E4M3 (FP8)
+#endif
+// format of a path: TERMS = 1 is the one-term FP8 mode
+template <int TERMS>
+constexpr int act_fmt() { return TERMS == 2 ? MOE_FP4_GROUPED_FMT : kFmtE4M3; }
+template <int F>
+constexpr int fmt_blk_bytes() { return F == kFmtE2M3 ? 24 : 32; }  // bytes per block and term
+// LDS row of one 128-element chunk: hi | lo | pad (E2M3: 96 | 96 | 16, E4M3: 128 | 128 | 16)
+template <int F>
+constexpr int fmt_pitch() { return 2 * 4 * fmt_blk_bytes<F>() + 16; }
+
+// Smallest X with a <= 7.5 * 2^X (7.5 = 1.875 * 2^2, the largest E2M3 value), clamped to the
+// ue8m0 range; a == 0 gives -127.
+__device__ __forceinline__ int mx6_exponent(float a) {
+  if (!(a > 0.f)) return -127;
+  const uint32_t b = __float_as_uint(a);
+  int E = (int)((b >> 23) & 0xff) - 127;
+  uint32_t man = b & 0x7fffffu;
+  if (E == -127) {  // subnormal: normalise
+    const int sh = __clz((int)man) - 8;
+    man = (man << sh) & 0x7fffffu;
+    E = -126 - sh;
+  }
+  // mantissa <= 1.875  <=>  man <= 0.875 * 2^23
+  const int X = (man <= 0x700000u) ? E - 2 : E - 1;
+  return max(-127, min(127, X));
+}
+
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef unsigned v6u_t __attribute__((ext_vector_type(6)));
+
+// v[0..31] / 2^X -> 32 E2M3 codes, code i at bits 6 i of six dwords (the order of the MFMA's
+// E2M3 A operand: one lane's 32 consecutive K values), rounded to nearest with ties to the
+// even code. v_cvt_scalef32_2xpk16_fp6_f32 divides by the scale operand's power of two and
+// interleaves its two 16-value sources (code 2 k from the first, 2 k + 1 from the second),
+// so the even and odd values go in separately. It reads its sources after writing part of
+// its result, and the compiler's allocation may place the result over them (measured:
+// values 12..31 then came out wrong); the asm's early-clobber result keeps them apart.
+__device__ __forceinline__ v6u_t cvt_e2m3_x32(const float (&v)[32], int X) {
+  v16f_t ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = v[2 * i];
+    od[i] = v[2 * i + 1];
+  }
+  const float sc = __uint_as_float((uint32_t)(X + 127) << 23);  // 2^X (exponent field only)
+  v6u_t r;
+  __asm__("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(sc));
+  return r;
+}
+
+// code i of six packed dwords
+__device__ __forceinline__ uint32_t e2m3_code(const v6u_t& w, int i) {
+  const int bit = 6 * i, d = bit >> 5, sh = bit & 31;
+  uint32_t c = w[d] >> sh;
+  if (sh > 26) c |= w[d + 1] << (32 - sh);
+  return c & 63u;
+}
+
+// value of an E2M3 code times 2^X (exact in fp32)
+__device__ __forceinline__ float e2m3_value(uint32_t c, int X) {
+  const uint32_t e = (c >> 3) & 3u, m = c & 7u;
+  const uint32_t mag8 = e ? (8u + m) << (e - 1) : m;  // in units of 1/8
+  const float v = ldexpf((float)mag8, X - 3);
+  return (c & 32u) ? -v : v;
+}
+
+// v[0..31] (fp32) -> hi, lo E2M3 codes (six dwords each) and their scale bytes: hi = the block
+// quantised with its scale, lo = the residual v - hi (exact in fp32) quantised with its own.
+// E2M3 has no NaN or infinity: a block holding one gets scale byte 255 (NaN) on both terms, so
+// every product with it is NaN, as the element itself would have made it.
+__device__ __forceinline__ void mx6_encode_block(const float (&v)[32], v6u_t& hi, v6u_t& lo,
+                                                 uint32_t& sh, uint32_t& sl) {
+  float amax = 0.f;
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    amax = fmaxf(amax, fabsf(v[i]));
+    finite = finite && fabsf(v[i]) <= 3.4028234663852886e38f;  // false for NaN and +-inf
+  }
+  const int X = mx6_exponent(amax);
+  hi = cvt_e2m3_x32(v, X);
+  float r[32];
+  float rmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    r[i] = v[i] - e2m3_value(e2m3_code(hi, i), X);
+    rmax = fmaxf(rmax, fabsf(r[i]));
+  }
+  const int Xl = mx6_exponent(rmax);
+  lo = cvt_e2m3_x32(r, Xl);
+  sh = finite ? (uint32_t)(X + 127) : 255u;
+  sl = finite ? (uint32_t)(Xl + 127) : 255u;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -324,6 +426,25 @@ __global__ __launch_bounds__(kSortWGThreads) void sort_scatter_kernel(const int3
 // 2. x -> MXFP8 hi / lo (hi only for TERMS = 1), one thread per (token, 32-block); blocks
 //    past H are zero (scale byte 127)
 // ---------------------------------------------------------------------------------------
+// Bytes of one activation row of Kp elements in global memory, and the store of block b of
+// a row: E4M3 32 bytes (h0, h1), E2M3 24 bytes (h0 and the first half of h1: six dwords).
+template <int F>
+__device__ __host__ constexpr long act_row_bytes(int Kp) { return (long)Kp / kBlock * fmt_blk_bytes<F>(); }
+
+template <int F>
+__device__ __forceinline__ void store_act_block(uint8_t* row, int b, uint4 h0, uint4 h1) {
+  if constexpr (F == kFmtE2M3) {
+    uint2* d = reinterpret_cast<uint2*>(row + 24L * b);  // 8-byte aligned
+    d[0] = make_uint2(h0.x, h0.y);
+    d[1] = make_uint2(h0.z, h0.w);
+    d[2] = make_uint2(h1.x, h1.y);
+  } else {
+    uint4* d = reinterpret_cast<uint4*>(row + 32L * b);
+    d[0] = h0;
+    d[1] = h1;
+  }
+}
+
 template <int TERMS>
 __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                       int Hp, uint8_t* __restrict__ qhi,
@@ -350,16 +471,21 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
         v[8 * q + 2 * i + 1] = bf16_bits_to_f32(ww[i] >> 16);
       }
     }
-    mx8_encode_block<TERMS>(v, h0, h1, l0, l1, sh, sl);
+    if constexpr (act_fmt<TERMS>() == kFmtE2M3) {
+      v6u_t hi, lo;
+      mx6_encode_block(v, hi, lo, sh, sl);
+      h0 = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      h1 = make_uint4(hi[4], hi[5], 0, 0);
+      l0 = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      l1 = make_uint4(lo[4], lo[5], 0, 0);
+    } else {
+      mx8_encode_block<TERMS>(v, h0, h1, l0, l1, sh, sl);
+    }
   }
-  uint4* dh = reinterpret_cast<uint4*>(qhi + t * Hp + kBlock * b);
-  dh[0] = h0;
-  dh[1] = h1;
+  store_act_block<act_fmt<TERMS>()>(qhi + t * act_row_bytes<act_fmt<TERMS>()>(Hp), b, h0, h1);
   shi[t * nbk + b] = (uint8_t)sh;
   if constexpr (TERMS == 2) {
-    uint4* dl = reinterpret_cast<uint4*>(qlo + t * Hp + kBlock * b);
-    dl[0] = l0;
-    dl[1] = l1;
+    store_act_block<act_fmt<TERMS>()>(qlo + t * act_row_bytes<act_fmt<TERMS>()>(Hp), b, l0, l1);
     slo[t * nbk + b] = (uint8_t)sl;
   }
 }
@@ -389,9 +515,12 @@ struct GemmCtx {
   long r0, r1, r2, r3;  // byte offsets of the A rows of this thread's pieces (four; two hi
                         // pieces with one term)
   long sr;              // byte offset of the scale row of this thread's scale dword
-  int part;             // 16-byte piece of the row (0..7 hi, 8..15 lo), same for all pieces
+  int part;             // E4M3: 16-byte piece of the row (0..7 hi, 8..15 lo), same for all
+                        // pieces; E2M3: piece of the first row (0..5 hi, 6..11 lo)
+  int part1, part2;     // E2M3: pieces of the second and third row
   int KB;               // K blocks of 32
-  int Kp;               // padded K (row pitch of the A data, bytes)
+  int Kp;               // row pitch of the A data, bytes
+  int Ksp;              // row pitch of the A scales, bytes (padded K / 32)
 };
 
 // The staged values travel in five separate registers (d0..d3, s): a struct or array
@@ -401,13 +530,24 @@ struct GemmCtx {
 template <int TERMS>
 __device__ __forceinline__ void stage_load(const GemmCtx& cx, int c, uint4& d0, uint4& d1,
                                            uint4& d2, uint4& d3, uint32_t& sv) {
-  const long off = 128L * c + 16 * (cx.part & 7);
-  const uint8_t* base = cx.part < 8 ? cx.ahi : cx.alo;
-  d0 = *reinterpret_cast<const uint4*>(base + cx.r0 + off);
-  d1 = *reinterpret_cast<const uint4*>(base + cx.r1 + off);
-  if constexpr (TERMS == 2) {
-    d2 = *reinterpret_cast<const uint4*>(base + cx.r2 + off);
-    d3 = *reinterpret_cast<const uint4*>(base + cx.r3 + off);
+  if constexpr (act_fmt<TERMS>() == kFmtE2M3) {
+    // three pieces: 96 bytes per row, chunk and term
+    auto piece = [&](long r, int part) {
+      const uint8_t* base = part < 6 ? cx.ahi : cx.alo;
+      return *reinterpret_cast<const uint4*>(base + r + 96L * c + 16 * (part < 6 ? part : part - 6));
+    };
+    d0 = piece(cx.r0, cx.part);
+    d1 = piece(cx.r1, cx.part1);
+    d2 = piece(cx.r2, cx.part2);
+  } else {
+    const long off = 128L * c + 16 * (cx.part & 7);
+    const uint8_t* base = cx.part < 8 ? cx.ahi : cx.alo;
+    d0 = *reinterpret_cast<const uint4*>(base + cx.r0 + off);
+    d1 = *reinterpret_cast<const uint4*>(base + cx.r1 + off);
+    if constexpr (TERMS == 2) {
+      d2 = *reinterpret_cast<const uint4*>(base + cx.r2 + off);
+      d3 = *reinterpret_cast<const uint4*>(base + cx.r3 + off);
+    }
   }
   const int tid = threadIdx.x;
   const uint8_t* sb = (TERMS == 2 && (tid & 1)) ? cx.aslo : cx.ashi;
@@ -420,14 +560,27 @@ template <int TERMS>
 __device__ __forceinline__ void stage_store(uint8_t* lds, uint8_t* lds_s, uint4 d0, uint4 d1,
                                             uint4 d2, uint4 d3, uint32_t sv) {
   const int tid = threadIdx.x;
-  constexpr int kParts = 8 * TERMS;
-  uint8_t* p = lds + (tid / kParts) * kAPitch + 16 * (tid % kParts);
-  constexpr int kRowStep = (kBThreads / kParts) * kAPitch;
-  *reinterpret_cast<uint4*>(p) = d0;
-  *reinterpret_cast<uint4*>(p + kRowStep) = d1;
-  if constexpr (TERMS == 2) {
-    *reinterpret_cast<uint4*>(p + 2 * kRowStep) = d2;
-    *reinterpret_cast<uint4*>(p + 3 * kRowStep) = d3;
+  if constexpr (act_fmt<TERMS>() == kFmtE2M3) {
+    // piece q = tid + kBThreads i: row q / 12, part q % 12 (0..5 hi, 6..11 lo)
+    constexpr int kP = fmt_pitch<kFmtE2M3>();
+    auto dst = [&](int q) {
+      const int row = q / 12, part = q - 12 * (q / 12);
+      return lds + row * kP + (part < 6 ? 16 * part : 96 + 16 * (part - 6));
+    };
+    *reinterpret_cast<uint4*>(dst(tid)) = d0;
+    *reinterpret_cast<uint4*>(dst(tid + kBThreads)) = d1;
+    *reinterpret_cast<uint4*>(dst(tid + 2 * kBThreads)) = d2;
+  } else {
+    constexpr int kP = fmt_pitch<kFmtE4M3>();
+    constexpr int kParts = 8 * TERMS;
+    uint8_t* p = lds + (tid / kParts) * kP + 16 * (tid % kParts);
+    constexpr int kRowStep = (kBThreads / kParts) * kP;
+    *reinterpret_cast<uint4*>(p) = d0;
+    *reinterpret_cast<uint4*>(p + kRowStep) = d1;
+    if constexpr (TERMS == 2) {
+      *reinterpret_cast<uint4*>(p + 2 * kRowStep) = d2;
+      *reinterpret_cast<uint4*>(p + 3 * kRowStep) = d3;
+    }
   }
   if (tid < 2 * kBlockRows) *reinterpret_cast<uint32_t*>(lds_s + 4 * tid) = sv;
 }
@@ -438,7 +591,7 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, uint8_t* lds_s, uint4 
 __device__ __forceinline__ i32x8_t a_operand(const uint8_t* lds, int m, int lane, bool lo,
                                              uint32_t m0, uint32_t m1) {
   const int r = lane & 15, g = lane >> 4;
-  const uint8_t* row = lds + (16 * m + r) * kAPitch + (lo ? 128 : 0);
+  const uint8_t* row = lds + (16 * m + r) * fmt_pitch<kFmtE4M3>() + (lo ? 128 : 0);
   const uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
   const uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
   return i32x8_t{(int)(p0.x & m0), (int)(p0.y & m0), (int)(p0.z & m0), (int)(p0.w & m0),
@@ -450,13 +603,26 @@ __device__ __forceinline__ i32x8_t a_operand(const uint8_t* lds, int m, int lane
 __device__ __forceinline__ i32x8_t a_operand_br(const uint8_t* lds, int m, int lane, bool lo,
                                                 uint32_t m0, uint32_t m1) {
   const int r = lane & 15, g = lane >> 4;
-  const uint8_t* row = lds + (16 * m + r) * kAPitch + (lo ? 128 : 0);
+  const uint8_t* row = lds + (16 * m + r) * fmt_pitch<kFmtE4M3>() + (lo ? 128 : 0);
   uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
   uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
   if (!m0) p0 = make_uint4(0, 0, 0, 0);
   if (!m1) p1 = make_uint4(0, 0, 0, 0);
   return i32x8_t{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
                  (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+}
+
+// E2M3 A operand (hi or lo) of subtile m: lane 16 g + r holds row r's K-block g, its 32
+// codes in six dwords (24 bytes at 24 g of the row's 96); zeroed with the lane mask mk past K.
+__device__ __forceinline__ i32x8_t a_operand6(const uint8_t* lds, int m, int lane, bool lo,
+                                              uint32_t mk) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint8_t* p = lds + (16 * m + r) * fmt_pitch<kFmtE2M3>() + (lo ? 96 : 0) + 24 * g;
+  const uint2 p0 = *reinterpret_cast<const uint2*>(p);
+  const uint2 p1 = *reinterpret_cast<const uint2*>(p + 8);
+  const uint2 p2 = *reinterpret_cast<const uint2*>(p + 16);
+  return i32x8_t{(int)(p0.x & mk), (int)(p0.y & mk), (int)(p1.x & mk), (int)(p1.y & mk),
+                 (int)(p2.x & mk), (int)(p2.y & mk), 0, 0};
 }
 
 __device__ __forceinline__ i32x8_t b_operand(uint4 w) {
@@ -518,17 +684,19 @@ struct Acc {
   f32x4_t a[kMSub][NB];
 };
 
-// sb: the B word's scale byte, or 127 (scale 1) past K.
+// sb: the B word's scale byte, or 127 (scale 1) past K. F: the A operand's format code.
+template <int F>
 __device__ __forceinline__ void mfma2(f32x4_t& acc, const i32x8_t& ahi, const i32x8_t& alo,
                                       const BWord& b, int sw_hi, int sw_lo, int sb) {
   const i32x8_t bq = b_operand(b.w);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bq, acc, 0, 4, 0, sw_hi, 0, sb);
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, 0, 4, 0, sw_lo, 0, sb);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bq, acc, F, 4, 0, sw_hi, 0, sb);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, bq, acc, F, 4, 0, sw_lo, 0, sb);
 }
 
+template <int F>
 __device__ __forceinline__ void mfma1(f32x4_t& acc, const i32x8_t& ahi, const BWord& b, int sw_hi,
                                       int sb) {
-  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, b_operand(b.w), acc, 0, 4, 0, sw_hi, 0, sb);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, b_operand(b.w), acc, F, 4, 0, sw_hi, 0, sb);
 }
 
 // BSETS 2 or 3: the K loop runs BSETS chunks per trip with BSETS B sets used in turn and
@@ -548,7 +716,8 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   const int g = lane >> 4;
   const int r = lane & 15;
   const int nch = (cx.KB + 3) / 4;
-  constexpr int kBuf = kBlockRows * kAPitch;
+  constexpr int F = act_fmt<TERMS>();
+  constexpr int kBuf = kBlockRows * fmt_pitch<F>();
   constexpr int kBufS = kBlockRows * 8;
   uint4 d0, d1, d2, d3, e0, e1, e2, e3;
   uint32_t sv, se;
@@ -576,27 +745,30 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
     const uint32_t h0 = 4 * (C) + (g >> 1) < cx.KB ? ~0u : 0u;                                  \
     const uint32_t h1 = 4 * (C) + 2 + (g >> 1) < cx.KB ? ~0u : 0u;                              \
     const bool s_ok = 4 * (C) + g < cx.KB;                                                      \
+    const uint32_t mk = s_ok ? ~0u : 0u; /* E2M3: a lane holds one whole K-block */             \
     const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;                 \
     const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;                 \
     if (any_on) {                                                                               \
       _Pragma("unroll") for (int m = 0; m < kMSub; ++m) {                                       \
         if (16 * m < rows) { /* wave-uniform */                                                 \
-          const i32x8_t ahi = PAIR ? a_operand(A, m, lane, false, h0, h1)                       \
-                                   : a_operand_br(A, m, lane, false, h0, h1);                   \
+          const i32x8_t ahi = F == kFmtE2M3 ? a_operand6(A, m, lane, false, mk)                 \
+                              : PAIR        ? a_operand(A, m, lane, false, h0, h1)              \
+                                            : a_operand_br(A, m, lane, false, h0, h1);          \
           const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;                         \
           if constexpr (TERMS == 2) {                                                           \
-            const i32x8_t alo = PAIR ? a_operand(A, m, lane, true, h0, h1)                      \
-                                     : a_operand_br(A, m, lane, true, h0, h1);                  \
+            const i32x8_t alo = F == kFmtE2M3 ? a_operand6(A, m, lane, true, mk)                \
+                                : PAIR        ? a_operand(A, m, lane, true, h0, h1)             \
+                                              : a_operand_br(A, m, lane, true, h0, h1);         \
             const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;                   \
-            mfma2(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo, sb0);                             \
-            if constexpr (NB > 1) mfma2(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo, sb1);       \
-            if constexpr (NB > 2) mfma2(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo, sb2);       \
-            if constexpr (NB > 3) mfma2(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo, sb3);       \
+            mfma2<F>(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo, sb0);                          \
+            if constexpr (NB > 1) mfma2<F>(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo, sb1);    \
+            if constexpr (NB > 2) mfma2<F>(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo, sb2);    \
+            if constexpr (NB > 3) mfma2<F>(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo, sb3);    \
           } else {                                                                              \
-            mfma1(acc.a[m][0], ahi, BS.w0, sw_hi, sb0);                                         \
-            if constexpr (NB > 1) mfma1(acc.a[m][1], ahi, BS.w1, sw_hi, sb1);                   \
-            if constexpr (NB > 2) mfma1(acc.a[m][2], ahi, BS.w2, sw_hi, sb2);                   \
-            if constexpr (NB > 3) mfma1(acc.a[m][3], ahi, BS.w3, sw_hi, sb3);                   \
+            mfma1<F>(acc.a[m][0], ahi, BS.w0, sw_hi, sb0);                                      \
+            if constexpr (NB > 1) mfma1<F>(acc.a[m][1], ahi, BS.w1, sw_hi, sb1);                \
+            if constexpr (NB > 2) mfma1<F>(acc.a[m][2], ahi, BS.w2, sw_hi, sb2);                \
+            if constexpr (NB > 3) mfma1<F>(acc.a[m][3], ahi, BS.w3, sw_hi, sb3);                \
           }                                                                                     \
         }                                                                                       \
       }                                                                                         \
@@ -653,18 +825,31 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
 template <int TERMS, typename RowOf>
 __device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
   const int tid = threadIdx.x;
-  constexpr int kParts = 8 * TERMS;              // 16-byte pieces per staged row
-  constexpr int kRows = kBThreads / kParts;      // rows covered by one piece index
-  static_assert(kRows * (2 * TERMS) == kBlockRows, "pieces cover the block's rows");
-  cx.r0 = (long)row_of(tid / kParts) * cx.Kp;
-  cx.r1 = (long)row_of(tid / kParts + kRows) * cx.Kp;
-  cx.r2 = cx.r3 = cx.r0;
-  if constexpr (TERMS == 2) {
-    cx.r2 = (long)row_of(tid / kParts + 2 * kRows) * cx.Kp;
-    cx.r3 = (long)row_of(tid / kParts + 3 * kRows) * cx.Kp;
+  if constexpr (act_fmt<TERMS>() == kFmtE2M3) {
+    // 12 pieces per row (6 hi, 6 lo), pieces tid, tid + 256, tid + 512 of the 768
+    static_assert(kBlockRows * 12 == 3 * kBThreads, "pieces cover the block's rows");
+    cx.r0 = (long)row_of(tid / 12) * cx.Kp;
+    cx.r1 = (long)row_of((tid + kBThreads) / 12) * cx.Kp;
+    cx.r2 = (long)row_of((tid + 2 * kBThreads) / 12) * cx.Kp;
+    cx.r3 = cx.r0;
+    cx.part = tid % 12;
+    cx.part1 = (tid + kBThreads) % 12;
+    cx.part2 = (tid + 2 * kBThreads) % 12;
+  } else {
+    constexpr int kParts = 8 * TERMS;              // 16-byte pieces per staged row
+    constexpr int kRows = kBThreads / kParts;      // rows covered by one piece index
+    static_assert(kRows * (2 * TERMS) == kBlockRows, "pieces cover the block's rows");
+    cx.r0 = (long)row_of(tid / kParts) * cx.Kp;
+    cx.r1 = (long)row_of(tid / kParts + kRows) * cx.Kp;
+    cx.r2 = cx.r3 = cx.r0;
+    if constexpr (TERMS == 2) {
+      cx.r2 = (long)row_of(tid / kParts + 2 * kRows) * cx.Kp;
+      cx.r3 = (long)row_of(tid / kParts + 3 * kRows) * cx.Kp;
+    }
+    cx.part = tid % kParts;
+    cx.part1 = cx.part2 = cx.part;
   }
-  cx.part = tid % kParts;
-  cx.sr = (long)row_of(min(tid >> 1, kBlockRows - 1)) * (cx.Kp / kBlock);
+  cx.sr = (long)row_of(min(tid >> 1, kBlockRows - 1)) * cx.Ksp;
 }
 
 // Workgroup -> (row block, column tile). The dispatcher hands workgroups to the eight XCDs
@@ -710,7 +895,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     size_t stride, size_t off_gc, size_t off_uc, size_t off_gs, size_t off_us, int H, int I,
     int n_tiles, uint8_t* __restrict__ hhi, uint8_t* __restrict__ hlo,
     uint8_t* __restrict__ hshi, uint8_t* __restrict__ hslo, int Ip) {
-  __shared__ __align__(16) uint8_t lds[2 * kBlockRows * kAPitch];
+  constexpr int F = act_fmt<TERMS>();
+  constexpr int kHP = kBN + 1;  // epilogue h tile: [kBlockRows][kHP] fp32 over the A buffers
+  __shared__ __align__(16) uint8_t lds[std::max(2 * kBlockRows * fmt_pitch<F>(), kBlockRows * kHP * 4)];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
   int blk, nt;
   if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk, nt)) return;  // workgroup-uniform
@@ -729,7 +916,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   cx.ashi = xshi;
   cx.aslo = xslo;
   cx.KB = KB;
-  cx.Kp = Hp;
+  cx.Kp = (int)act_row_bytes<F>(Hp);
+  cx.Ksp = Hp / kBlock;
   gemm_ctx_rows<TERMS>(cx, [&](int i) { return perm[row0 + min(i, rows - 1)] / k; });
 
   const uint8_t* base = packed + (size_t)e * stride;
@@ -757,8 +945,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
   float* htile = reinterpret_cast<float*>(lds);  // [kBlockRows][kBN + 1]
-  constexpr int kHP = kBN + 1;
-  static_assert(kBlockRows * kHP * 4 <= 2 * kBlockRows * kAPitch, "h tile fits the A buffers");
 #pragma unroll
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
@@ -779,16 +965,22 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int i = 0; i < 32; ++i) v[i] = htile[r * kHP + 32 * b + i];
       uint4 h0, h1, l0, l1;
       uint32_t sh, sl;
-      mx8_encode_block<TERMS>(v, h0, h1, l0, l1, sh, sl);
+      if constexpr (F == kFmtE2M3) {
+        v6u_t hi, lo;
+        mx6_encode_block(v, hi, lo, sh, sl);
+        h0 = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        h1 = make_uint4(hi[4], hi[5], 0, 0);
+        l0 = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        l1 = make_uint4(lo[4], lo[5], 0, 0);
+      } else {
+        mx8_encode_block<TERMS>(v, h0, h1, l0, l1, sh, sl);
+      }
       const long pos = row0 + r;
-      uint4* dh = reinterpret_cast<uint4*>(hhi + pos * Ip + col);
-      dh[0] = h0;
-      dh[1] = h1;
+      const long rb = pos * act_row_bytes<F>(Ip);
+      store_act_block<F>(hhi + rb, col / kBlock, h0, h1);
       hshi[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sh;
       if constexpr (TERMS == 2) {
-        uint4* dl = reinterpret_cast<uint4*>(hlo + pos * Ip + col);
-        dl[0] = l0;
-        dl[1] = l1;
+        store_act_block<F>(hlo + rb, col / kBlock, l0, l1);
         hslo[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sl;
       }
     }
@@ -807,7 +999,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     const int32_t* __restrict__ blk_rows, const int32_t* __restrict__ n_blocks,
     const uint8_t* __restrict__ packed, size_t stride, size_t off_dc, size_t off_ds, int H, int I,
     int n_tiles, float* __restrict__ ypair) {
-  __shared__ __align__(16) uint8_t lds[2 * kBlockRows * kAPitch];
+  constexpr int F = act_fmt<TERMS>();
+  __shared__ __align__(16) uint8_t lds[2 * kBlockRows * fmt_pitch<F>()];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
   int blk, nt;
   if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk, nt)) return;  // workgroup-uniform
@@ -826,7 +1019,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   cx.ashi = hshi;
   cx.aslo = hslo;
   cx.KB = KB;
-  cx.Kp = Ip;
+  cx.Kp = (int)act_row_bytes<F>(Ip);
+  cx.Ksp = Ip / kBlock;
   gemm_ctx_rows<TERMS>(cx, [&](int i) { return row0 + min(i, rows - 1); });
 
   const uint8_t* base = packed + (size_t)e * stride;
@@ -951,9 +1145,25 @@ __global__ __launch_bounds__(256) void dequant_act_kernel(const uint8_t* __restr
   const long t = idx / H;
   const int h = (int)(idx - t * H);
   const long sb = t * (Hp / kBlock) + h / kBlock;
-  float r = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)qhi[t * Hp + h], 0), (int)shi[sb] - 127);
-  if constexpr (TERMS == 2)
-    r += ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)qlo[t * Hp + h], 0), (int)slo[sb] - 127);
+  float r;
+  if constexpr (act_fmt<TERMS>() == kFmtE2M3) {
+    // code h % 32 of the block's six dwords
+    const long rb = t * act_row_bytes<kFmtE2M3>(Hp) + 24L * (h / kBlock);
+    const uint32_t* wh = reinterpret_cast<const uint32_t*>(qhi + rb);
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(qlo + rb);
+    v6u_t vh, vl;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      vh[i] = wh[i];
+      vl[i] = wl[i];
+    }
+    const int i = h % kBlock;
+    r = e2m3_value(e2m3_code(vh, i), (int)shi[sb] - 127) + e2m3_value(e2m3_code(vl, i), (int)slo[sb] - 127);
+  } else {
+    r = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)qhi[t * Hp + h], 0), (int)shi[sb] - 127);
+    if constexpr (TERMS == 2)
+      r += ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)qlo[t * Hp + h], 0), (int)slo[sb] - 127);
+  }
   out[idx] = r;
 }
 

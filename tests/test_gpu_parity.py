@@ -148,9 +148,10 @@ def test_pack_round_trip_bit_exact(dev, H, I, E):
 def test_act_quant_bit_exact(dev, terms, H):
     """The grouped path's activation quantiser (x -> MX hi [+ lo], ue8m0 per 32), decoded
     back to fp32, equals the oracle's MX quantisation bit for bit: codes and scales are
-    rounding decisions on the same bf16 inputs. Blocks with zeros, a single value, grid ties,
-    values 2^-12 below their block maximum, rows scaled over 2^-40 .. 2^40, and a ragged
-    last 128-chunk (H 96, 2880)."""
+    rounding decisions on the same bf16 inputs. terms 1 is the one-term E4M3 (FP8) mode,
+    terms 2 the default grouped path's two E2M3 (FP6) terms. Blocks with zeros, a single
+    value, E4M3 and E2M3 grid ties, values 2^-12 below their block maximum, rows scaled over
+    2^-40 .. 2^40, and a ragged last 128-chunk (H 96, 2880)."""
     C, D = _mods()
     rng = np.random.default_rng(H + terms)
     T = 37
@@ -161,6 +162,8 @@ def test_act_quant_bit_exact(dev, terms, H):
     v[2, :32] = np.arange(32) / 4.0               # E4M3 ties after scaling
     v[3, :32] = np.where(np.arange(32) % 2 == 0, 1.0, 2.0 ** -12)
     v[4, :32] = -(np.arange(32) + 0.5) * 0.0625   # every half-step between grid values
+    g6 = O.mx_grid("e2m3")
+    v[5, :32] = np.append((g6[:-1] + g6[1:]) / 2.0, 7.5)  # E2M3 midpoints at scale 1
     x_bits = O.f64_to_bf16_bits(v)
     x = D.upload_bf16(x_bits, dev)
     nbytes = C.moe_fp4_debug_act_quant_bytes(T, H)
@@ -169,7 +172,7 @@ def test_act_quant_bit_exact(dev, terms, H):
     C.moe_fp4_debug_act_quant(x, T, H, terms, ws, nbytes, out)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    ref = O.mx_quantize(O.bf16_to_f64(x_bits), "e4m3", terms)
+    ref = O.mx_quantize(O.bf16_to_f64(x_bits), "e2m3" if terms == 2 else "e4m3", terms)
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[:3].tolist()}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
 
