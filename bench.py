@@ -224,7 +224,7 @@ def main() -> int:
                     help="stack16_decode: route each later layer straight from the residual "
                          "stream (fused) or run residual + RMSNorm as its own launch (separate)")
     ap.add_argument("--act-terms", type=int, choices=[1, 2], default=2,
-                    help="grouped-path workloads: activations as two MXFP8 terms (default, meets "
+                    help="grouped-path workloads: activations as two MXFP6 terms (default, meets "
                          "the output tolerance) or one (the opt-in FP8-activation path)")
     ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -436,7 +436,7 @@ def grouped_measure(torch, C, D, S, layer, wl, dev, K: int, W: int, terms: int) 
     """One grouped-path workload on a resident layer: K graph-replayed steps of top-k on the
     workload's fresh router logits + moe_fp4_expert_ffn (the grouped GEMM path), then a
     stream-launched pass with the library's kernel timing. Algorithmic flops are 6 H I per
-    (token, slot) pair (2 H I for each of gate, up and down; the two MXFP8 activation terms
+    (token, slot) pair (2 H I for each of gate, up and down; the two MXFP6 activation terms
     are not counted twice); algorithmic bytes are each distinct expert once plus the
     activations, logits and routing."""
     H, I, E, k, T = wl.hidden, wl.inter, layer.n_experts, wl.k, wl.tokens
@@ -1002,14 +1002,19 @@ def run_batched(args) -> int:
                 achieved = pairs * 4.0 * H * I / t_s / 1e12
                 roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP4_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP4_PEAK_TFLOPS, 4),
-                            "frac_of_fp8_peak": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                            # matrix-core time the operands imply: two E2M3 products per
+                            # pair at the FP4 rate, or one E4M3 product at the FP8 rate
+                            "mfma_busy_frac": round(achieved / MFMA_FP8_PEAK_TFLOPS if fp8
+                                                    else 2 * achieved / MFMA_FP4_PEAK_TFLOPS, 4),
                             "traffic": None, "kernel": "grouped_gate_up",
                             "flops_per_launch": pairs * 4.0 * H * I, "avg_launch_us": round(gu["avg_us"], 3)}
             else:
                 Hp, Ip = (H + 127) // 128 * 128, (I + 127) // 128 * 128
-                nterm = 1 if fp8 else 2  # MXFP8 terms of x and h
-                alg = (d_avg * gate_up_bytes(H, I) + T * Hp * nterm * (1 + 1 / 32)
-                       + pairs * Ip * nterm * (1 + 1 / 32))
+                # activation bytes per element and term (E4M3 one term, E2M3 two) + the
+                # ue8m0 scale byte per 32 elements of each term
+                nterm, elem = (1, 1.0) if fp8 else (2, 0.75)
+                alg = (d_avg * gate_up_bytes(H, I) + T * Hp * nterm * (elem + 1 / 32)
+                       + pairs * Ip * nterm * (elem + 1 / 32))
                 achieved = alg / t_s / 1e9
                 roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -1063,7 +1068,7 @@ def run_batched(args) -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
                    "tokens": T, "routing": wl.routing, "launch": args.mode, "parallelism": "none (1 GPU)",
-                   "activations": "bf16" if small else ("MXFP8 one term" if fp8 else "MXFP8 hi + lo")},
+                   "activations": "bf16" if small else ("MXFP8 one term" if fp8 else "MXFP6 hi + lo")},
         "tokens_per_s": round(T * K / elapsed_s, 1),
         "tflops": round(tflops, 2),
         "decode_path_step_us": decode_pct,

@@ -7,15 +7,16 @@
 //    indices into expert order (perm), and a table of 64-row M-blocks per expert. The order
 //    of pairs inside an expert's group is not fixed (LDS atomics), and nothing depends on
 //    it: every MFMA row is computed on its own, with the same K order.
-// 2. quant_x_kernel: x -> two-term MXFP8 (E4M3) hi + lo with one ue8m0 scale per 32 elements
-//    each. The pair reproduces bf16 inputs to about 2^-8 of the block maximum; one FP8 term
-//    alone does not meet the output tolerance. The scale exponent is the smallest X with
-//    max|v| <= 448 * 2^X, so no element overflows the E4M3 range. The opt-in single-term
-//    mode (TERMS = 1) keeps only hi: DeepSeek's own FP8 activation numerics with ue8m0
-//    scales ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug), half the activation bytes
-//    and half the matrix-core work.
+// 2. quant_x_kernel: x -> two-term MXFP6 (E2M3) hi + lo with one ue8m0 scale per 32 elements
+//    each (lo = the same quantisation of x - hi). One 8-bit or 6-bit term alone does not
+//    meet the output tolerance; two E2M3 terms do, and E2M3 codes enter the block-scaled
+//    MFMA at the FP4 rate, twice the FP8 one. The scale exponent is the smallest X with
+//    max|v| <= vmax * 2^X (vmax 7.5 for E2M3, 448 for E4M3), so no element overflows the
+//    element range. The opt-in single-term mode (TERMS = 1) is one E4M3 term: DeepSeek's own
+//    FP8 activation numerics with ue8m0 scales ([8GB-GPU], section RTX 50xx 上的三个从不抛错的
+//    Bug). Building with MOE_FP4_GROUPED_FMT=0 makes the two-term path E4M3 hi + lo instead.
 // 3. gemm_gate_up_kernel: per (M-block, 128 rows of I): g and u for 128 rows of gate and up,
-//    h = silu(g) * u, quantised in the epilogue to MXFP8 hi + lo (blocks of 32 along I).
+//    h = silu(g) * u, quantised in the epilogue to the same two terms (blocks of 32 along I).
 // 4. gemm_down_kernel: per (M-block, 128 rows of H): y_e = W_down h, times the pair's router
 //    weight, written fp32 per pair.
 // 5. combine_kernel: y[t] = sum of the token's valid pairs in canonical slot order (ascending
@@ -28,6 +29,8 @@
 //    wavefront reads its B operand as one contiguous 1 KB load.
 //  * A, FP8 (8 dwords): lane 16 g + r holds row r; byte e sits at K = 64 (e / 16) + 16 g + e % 16,
 //    i.e. two 16-byte pieces of the row at K offsets 16 g and 64 + 16 g.
+//  * A, FP6 E2M3 (6 of the 8 dwords): lane 16 g + r holds row r, K = 32 g + s at bits 6 s: one
+//    lane carries one whole K-block of its row, 24 bytes.
 //  * Scales: lane (row or column, g) supplies the ue8m0 byte of K-block g (K = 32 g .. + 31)
 //    of its row / column (operand byte 0).
 //  * C: row i, column j at lane j + 16 (i / 4), element i % 4.
@@ -80,7 +83,7 @@ constexpr int kSortMaxGroups = 256;        // workgroups of the split sort
 constexpr long kSortSplitMinPairs = 8192;  // pairs from which the sort is split (measured)
 
 // ---------------------------------------------------------------------------------------
-// MXFP8 (E4M3) encoding of one 32-element block, two terms.
+// MXFP8 (E4M3) encoding of one 32-element block, one or two terms.
 // ---------------------------------------------------------------------------------------
 // Smallest X with a <= 448 * 2^X (448 = 1.75 * 2^8, the largest E4M3 value), clamped to the
 // ue8m0 range; a == 0 gives -127.
@@ -423,8 +426,8 @@ __global__ __launch_bounds__(kSortWGThreads) void sort_scatter_kernel(const int3
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. x -> MXFP8 hi / lo (hi only for TERMS = 1), one thread per (token, 32-block); blocks
-//    past H are zero (scale byte 127)
+// 2. x -> MX hi / lo (E2M3 two terms; E4M3 hi only for TERMS = 1), one thread per (token,
+//    32-block); blocks past H are zero (scale byte 127)
 // ---------------------------------------------------------------------------------------
 // Bytes of one activation row of Kp elements in global memory, and the store of block b of
 // a row: E4M3 32 bytes (h0, h1), E2M3 24 bytes (h0 and the first half of h1: six dwords).
@@ -705,7 +708,8 @@ __device__ __forceinline__ void mfma1(f32x4_t& acc, const i32x8_t& ahi, const BW
 // two chunks ahead; the smaller register budget of down keeps it spill-free.
 // ADEPTH 2 (with BSETS 2): the A staging loads run two chunks ahead of their LDS store, in
 // two register sets used on alternate chunks (no copies between them).
-// TERMS 1: the A rows hold one MXFP8 term (hi), one MFMA per B word.
+// TERMS 1: the A rows hold one MXFP8 term (hi), one MFMA per B word. TERMS 2: two terms of
+// the two-term format (E2M3 by default).
 template <int NB, int BSETS, int ADEPTH, int TERMS, bool NT>
 __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, int rows,
                                             uint8_t* lds, uint8_t* lds_s, Acc<NB>& acc) {

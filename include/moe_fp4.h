@@ -162,7 +162,7 @@ int moe_fp4_route_logits(const float* logits, int T, int n_experts, int k, int32
  * ------------------------------------------------------------------------------------ */
 
 /* Workspace bytes moe_fp4_expert_ffn (any path) needs: the larger of h of every (token,
- * slot) pair in bf16 (decode path) and the grouped path's sort tables, MXFP8 activations
+ * slot) pair in bf16 (decode path) and the grouped path's sort tables, MX activations
  * and per-pair fp32 outputs (about T * k * (hidden * 4 + 2 * inter) bytes). 0 for invalid
  * arguments. */
 size_t moe_fp4_workspace_bytes(int T, int k, int n_experts, int hidden, int inter);
@@ -184,9 +184,11 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
  *    launches; best at batch 1; needs k * inter <= 32768).
  *  MOE_FP4_PATH_GROUPED: pairs are grouped by expert on the device (no host readback) and
  *    run through a grouped GEMM on the block-scaled FP4 matrix cores; the activations x and
- *    h enter the matrix cores as two-term MXFP8 (E4M3 hi + lo, one ue8m0 scale per 32
- *    elements each), accumulation is fp32, each pair's weighted output is combined per token
- *    in canonical slot order (five launches; needs n_experts <= 2048).
+ *    h enter the matrix cores as two-term MXFP6 (E2M3 hi + lo, one ue8m0 scale per 32
+ *    elements each; E2M3 operands run at the FP4 rate), accumulation is fp32, each pair's
+ *    weighted output is combined per token in canonical slot order (five launches; needs
+ *    n_experts <= 2048). A NaN or infinity in a 32-element block of x or h (E2M3 has
+ *    neither) gives the block a NaN scale, so the outputs it reaches are NaN.
  *  MOE_FP4_PATH_SMALL_M: for a few tokens per call (several draft tokens of one sequence,
  *    a few streams): the pairs that chose the same expert share one read of its weights in
  *    groups of up to G pairs (the tokens of a group are rows of one matrix-core tile), h is
@@ -197,8 +199,9 @@ int moe_fp4_expert_ffn(const uint16_t* x, const int32_t* topk_ids, const float* 
  *  MOE_FP4_PATH_GROUPED_FP8: opt-in; GROUPED with the activations x and h as one MXFP8
  *    term (E4M3, one ue8m0 scale per 32 elements): DeepSeek's FP8 activation numerics
  *    ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug: activations quantised with ue8m0
- *    scales). Half the activation bytes and matrix-core work of GROUPED; the result is that
- *    of the quantised activations, which on the 384-expert layer lies further from the exact
+ *    scales). Two thirds of GROUPED's activation bytes and the same matrix-core time (one
+ *    FP8 product instead of two at the FP4 rate); the result is that of the quantised
+ *    activations, which on the 384-expert layer lies further from the exact
  *    bf16 computation than the 2e-2 normwise bar of the other paths. AUTO never picks it.
  *  MOE_FP4_PATH_AUTO: GROUPED from 24 tokens on; SMALL_M from 2 to 23 tokens where its
  *    limits hold; DECODE otherwise (one token, or a shape SMALL_M refuses). Measured on the
@@ -377,14 +380,15 @@ int moe_fp4_debug_dequant(const void* packed, int n_experts, int hidden, int int
                           int matrix, float* out, void* stream);
 
 /* Debug helper: the grouped path's activation quantisation of x [T x hidden] bf16 (device),
- * decoded back to fp32 out [T x hidden] (device): per 32-element block, one or two MXFP8
- * E4M3 terms (hi, then lo = the same quantisation of x - hi) with one ue8m0 scale each, the
- * scale the smallest power of two that fits the block's maximum in 448, codes rounded to
- * nearest with ties to the even code ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug:
- * ue8m0-scaled FP8 activations). This scale rule is the library's own reading, not the OCP
- * MX one (2^(floor(log2 max) - 8) with clipping): where the block maximum's significand
- * exceeds 1.75 it takes the next power of two, so no element is clipped. terms 2: the GROUPED path's operand; terms 1: the
- * GROUPED_FP8 path's. out is the exact sum of the decoded terms. workspace:
+ * decoded back to fp32 out [T x hidden] (device): per 32-element block, terms 1: one MXFP8
+ * E4M3 term (the GROUPED_FP8 path's operand); terms 2: two MXFP6 E2M3 terms (the GROUPED
+ * path's: hi, then lo = the same quantisation of x - hi), with one ue8m0 scale each, the
+ * scale the smallest power of two that fits the block's maximum in the format's largest
+ * value (448 for E4M3, 7.5 for E2M3), codes rounded to nearest with ties to the even code
+ * ([8GB-GPU], section RTX 50xx 上的三个从不抛错的 Bug: ue8m0-scaled activations). This scale
+ * rule is the library's own reading, not the OCP MX one (2^(floor(log2 max) - emax) with
+ * clipping): where the block maximum's significand exceeds the largest value's (1.75 for
+ * E4M3, 1.875 for E2M3) it takes the next power of two, so no element is clipped. out is the exact sum of the decoded terms. workspace:
  * moe_fp4_debug_act_quant_bytes(T, hidden) bytes of device memory, 16-byte aligned, contents
  * irrelevant. Errors: INVALID_ARG (null pointer, T < 0, terms not 1 or 2), BAD_SHAPE,
  * MISALIGNED, WORKSPACE, HIP. */
