@@ -77,6 +77,20 @@ constexpr int kBWaves = 4;
 constexpr int kBThreads = kBWaves * 64;
 constexpr int kNS = 2;                  // 16-row weight tiles per wave (per matrix)
 constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
+// Down: 16-row tiles of W_down per wave, its wavefronts per SIMD and B sets. Measured with the
+// E2M3 operands: 4 tiles at 2 waves per SIMD with 2 B sets took down from 2.01 to 1.87 ms at
+// 8192 tokens (6.29 to 6.20 at 32768) against 2 tiles at 4 waves per SIMD with one set.
+#ifndef MOE_FP4_DN_NS
+#define MOE_FP4_DN_NS 4
+#endif
+#ifndef MOE_FP4_DN_WPE
+#define MOE_FP4_DN_WPE 2
+#endif
+#ifndef MOE_FP4_DN_BSETS
+#define MOE_FP4_DN_BSETS 2
+#endif
+constexpr int kDNS = MOE_FP4_DN_NS;
+constexpr int kBND = 16 * kDNS * kBWaves;  // rows of H per down workgroup
 constexpr int kMSub = kBlockRows / 16;  // 16-row MFMA subtiles per M-block
 constexpr int kSortThreads = 1024;
 constexpr int kSortMaxGroups = 256;        // workgroups of the split sort
@@ -495,20 +509,19 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------------------------------
 // Grouped GEMM core shared by both stages. A workgroup owns one M-block (up to kBlockRows
-// rows of one expert's group) and kBN weight rows: wave w takes kNS = 2 consecutive 16-row
-// tiles of each of its matrices, so every A operand read from LDS feeds 2 (down) or 4
-// (gate and up) pairs of MFMAs. Per 128-element chunk of K:
+// rows of one expert's group) and a tile of weight rows: each wave takes 4 B words per chunk
+// (gate/up: 2 consecutive 16-row tiles of each matrix; down: 4 tiles of W_down), so every A
+// operand read from LDS feeds 4 pairs of MFMAs. Per 128-element chunk of K:
 //  * the block's A rows (hi, lo, scales) are staged in one of two LDS buffers; each thread
-//    moves four 16-byte pieces and (threads < 2 * kBlockRows) one scale dword, loaded from
-//    global memory about one chunk ahead of their store;
-//  * each wave loads its B words (one 1 KB word per tile) two chunks ahead;
+//    moves three (E2M3) or four (E4M3) 16-byte pieces and (threads < 2 * kBlockRows) one
+//    scale dword, loaded from global memory about one chunk ahead of their store;
+//  * each wave loads its B words (one 1 KB word per tile) two or three chunks ahead;
 //  * 16-row subtiles past the block's rows are skipped (wave-uniform);
 //  * one barrier per chunk.
-// Every load is issued with a clamped chunk index, so the wait counts stay exact. The GEMM
-// kernels are held to 2 (gate/up: 4 B words and 64 accumulators per lane) and 4 (down)
-// wavefronts per SIMD (at most 256 / 128 registers per lane; the two LDS buffers of 17.9 KB
-// each allow 4 workgroups per CU), so other workgroups' chunks cover each wave's memory
-// waits.
+// Every load is issued with a clamped chunk index, so the wait counts stay exact. Both GEMM
+// kernels are held to 2 wavefronts per SIMD (4 B words, 64 accumulators and 2-3 B sets per
+// lane; at most 256 registers), two workgroups per CU, so the other workgroup's chunks
+// cover each wave's memory waits.
 // ---------------------------------------------------------------------------------------
 struct GemmCtx {
   const uint8_t* ahi;
@@ -995,7 +1008,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 // 4. down projection, times the router weight, fp32 per pair
 // ---------------------------------------------------------------------------------------
 template <int TERMS, bool NT>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_down_kernel(
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_FP4_DN_WPE))) void gemm_down_kernel(
     const uint8_t* __restrict__ hhi, const uint8_t* __restrict__ hlo,
     const uint8_t* __restrict__ hshi, const uint8_t* __restrict__ hslo, int Ip,
     const int32_t* __restrict__ perm, const float* __restrict__ wts,
@@ -1015,7 +1028,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   const int wv = tid >> 6;
   const int lane = tid & 63;
   const int KB = I / kBlock;
-  const int tile0 = (nt * kBWaves + wv) * kNS;  // first 16-row tile of down (rows of H)
+  const int tile0 = (nt * kBWaves + wv) * kDNS;  // first 16-row tile of down (rows of H)
 
   GemmCtx cx;
   cx.ahi = hhi;
@@ -1031,23 +1044,30 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   const int nt16 = H / 16;
   const size_t tb0 = (size_t)min(tile0, nt16 - 1) * 16 * KB;
   const size_t tb1 = (size_t)min(tile0 + 1, nt16 - 1) * 16 * KB;
+  const size_t tb2 = (size_t)min(tile0 + 2, nt16 - 1) * 16 * KB;
+  const size_t tb3 = (size_t)min(tile0 + 3, nt16 - 1) * 16 * KB;
   BPtrs bp;
   bp.c0 = base + off_dc + 16 * tb0;
   bp.c1 = base + off_dc + 16 * tb1;
-  bp.c2 = bp.c3 = bp.c0;
+  bp.c2 = base + off_dc + 16 * tb2;
+  bp.c3 = base + off_dc + 16 * tb3;
   bp.s0 = base + off_ds + tb0;
   bp.s1 = base + off_ds + tb1;
-  bp.s2 = bp.s3 = bp.s0;
+  bp.s2 = base + off_ds + tb2;
+  bp.s3 = base + off_ds + tb3;
   bp.on0 = tile0 < nt16;
   bp.on1 = tile0 + 1 < nt16;
-  bp.on2 = bp.on3 = false;
-  Acc<2> acc;
+  bp.on2 = kDNS > 2 && tile0 + 2 < nt16;
+  bp.on3 = kDNS > 3 && tile0 + 3 < nt16;
+  Acc<kDNS> acc;
 #pragma unroll
-  for (int m = 0; m < kMSub; ++m) acc.a[m][0] = acc.a[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<2, 1, 1, TERMS, NT>(cx, bp, rows, lds, lds_s, acc);
+  for (int m = 0; m < kMSub; ++m)
+#pragma unroll
+    for (int q = 0; q < kDNS; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gemm_k_loop<kDNS, MOE_FP4_DN_BSETS, 1, TERMS, NT>(cx, bp, rows, lds, lds_s, acc);
 
 #pragma unroll
-  for (int s2 = 0; s2 < kNS; ++s2) {
+  for (int s2 = 0; s2 < kDNS; ++s2) {
     const int tile = tile0 + s2;
     if (tile < nt16) {
       const int n = 16 * tile + (lane & 15);
@@ -1278,7 +1298,7 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
                     ws + B.hslo, B.Ip);
   if (e != hipSuccess) return e;
 
-  const int dn_tiles = (hidden + kBN - 1) / kBN;
+  const int dn_tiles = (hidden + kBND - 1) / kBND;
   const long dn_grid = ((long)B.nb_max * dn_tiles + 7) / 8 * 8;
   if (dn_grid > 0x7fffffffL) return hipErrorInvalidValue;
   float* ypair = reinterpret_cast<float*>(ws + B.ypair);
