@@ -291,7 +291,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf) {
 __global__ __launch_bounds__(kSortThreads) void sort_kernel(
     const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ blk_expert, int32_t* __restrict__ blk_row0,
-    int32_t* __restrict__ blk_rows, int32_t* __restrict__ n_blocks) {
+    int32_t* __restrict__ n_blocks) {
   extern __shared__ int sm[];
   int* cnt = sm;                // E
   int* cur = sm + E;            // E
@@ -328,7 +328,6 @@ __global__ __launch_bounds__(kSortThreads) void sort_kernel(
       for (int b = 0; b < nb; ++b) {
         blk_expert[blk_base + b] = e;
         blk_row0[blk_base + b] = row_base + b * kBlockRows;
-        blk_rows[blk_base + b] = min(kBlockRows, n - b * kBlockRows);
       }
       row_base += n;
       blk_base += nb;
@@ -373,7 +372,7 @@ __global__ __launch_bounds__(kSortWGThreads) void sort_count_kernel(const int32_
 __global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(
     int G, int E, int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
     int32_t* __restrict__ blk_expert, int32_t* __restrict__ blk_row0,
-    int32_t* __restrict__ blk_rows, int32_t* __restrict__ n_blocks) {
+    int32_t* __restrict__ n_blocks) {
   extern __shared__ int sm[];
   int* tot = sm;              // E
   int* sbuf = sm + E;         // kSortThreads
@@ -404,7 +403,6 @@ __global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(
       for (int b = 0; b < nb; ++b) {
         blk_expert[blk_base + b] = e;
         blk_row0[blk_base + b] = row_base + b * kBlockRows;
-        blk_rows[blk_base + b] = min(kBlockRows, n - b * kBlockRows);
       }
       // workgroup g's first row for expert e: after the rows of the workgroups before it
       int start = row_base;
@@ -870,32 +868,45 @@ __device__ __forceinline__ void gemm_ctx_rows(GemmCtx& cx, RowOf row_of) {
 }
 
 // Workgroup -> (row block, column tile). The dispatcher hands workgroups to the eight XCDs
-// in turn (b mod 8) and each XCD has its own L2, so the logical index gives every XCD one
+// in turn (b mod 8) and each XCD has its own L2, so the logical index L gives every XCD one
 // contiguous range of the n_blocks x n_tiles items (sized from the actual block count, so
-// the XCDs get equal shares). Inside a range the row blocks run fastest within groups of
-// kColGroup column tiles: the row blocks of one expert, which are consecutive blocks, read
-// the same weight tile close together in time on one XCD (the later reads hit its L2), and
-// each row block's activations are reused by the group's tiles. Returns false for the
-// workgroups past the items (the grid is nb_max x n_tiles rounded up to a multiple of 8).
+// the XCDs get equal shares). L runs over groups of up to kGroupBlocks row blocks of one
+// expert (a group starts at the expert's first block, the next kGroupBlocks blocks later);
+// inside a group the column tiles go in order and the group's row blocks run fastest. The
+// row blocks that read one weight tile are adjacent in time on one XCD, and a row block's
+// activation rows are read again for each column tile a group's width later, while they
+// are still in that L2: weights and activations both come from HBM about once. The item's
+// expert, first sorted row and row count are returned; false for the workgroups past the
+// items (the grid is nb_max x n_tiles rounded up to a multiple of 8).
 constexpr int kXcds = 8;
-#ifndef MOE_FP4_COL_GROUP
-#define MOE_FP4_COL_GROUP 4  // column tiles whose row blocks are interleaved on one XCD
+#ifndef MOE_FP4_GROUP_BLOCKS
+#define MOE_FP4_GROUP_BLOCKS 8  // row blocks of one expert whose items are interleaved
 #endif
-constexpr int kColGroup = MOE_FP4_COL_GROUP;
+constexpr int kGroupBlocks = MOE_FP4_GROUP_BLOCKS;
 
-__device__ __forceinline__ bool map_block_tile(int b, int nb, int n_tiles, int& blk, int& nt) {
+__device__ __forceinline__ bool map_block_tile(int b, int nb, int n_tiles,
+                                               const int32_t* __restrict__ blk_expert,
+                                               const int32_t* __restrict__ blk_row0,
+                                               const int32_t* __restrict__ offsets, int& e,
+                                               int& row0, int& rows, int& nt) {
   const long G = (long)nb * n_tiles;
   const long per = (G + kXcds - 1) / kXcds;
   const int j = b / kXcds;
   if (j >= per) return false;
   const long L = (long)(b - j * kXcds) * per + j;
   if (L >= G) return false;
-  const long span = (long)nb * kColGroup;
-  const int cg = (int)(L / span);
-  const int r = (int)(L - cg * span);
-  const int cols = min(kColGroup, n_tiles - cg * kColGroup);
-  blk = r / cols;
-  nt = cg * kColGroup + (r - blk * cols);
+  const int bl = (int)(L / n_tiles);  // a row block of the item's group
+  e = blk_expert[bl];
+  const int o0 = offsets[e];
+  const int n = offsets[e + 1] - o0;  // the expert's sorted rows
+  const int jb = (blk_row0[bl] - o0) / kBlockRows;  // bl's index among the expert's blocks
+  const int g0 = jb / kGroupBlocks * kGroupBlocks;
+  const int ng = min(kGroupBlocks, (n + kBlockRows - 1) / kBlockRows - g0);
+  const long local = L - (long)(bl - jb + g0) * n_tiles;  // in [0, ng x n_tiles)
+  nt = (int)(local / ng);
+  const int jj = g0 + (int)(local - (long)nt * ng);
+  row0 = o0 + jj * kBlockRows;
+  rows = min(kBlockRows, n - jj * kBlockRows);
   return true;
 }
 
@@ -907,7 +918,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     const uint8_t* __restrict__ xhi, const uint8_t* __restrict__ xlo,
     const uint8_t* __restrict__ xshi, const uint8_t* __restrict__ xslo, int Hp,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_expert,
-    const int32_t* __restrict__ blk_row0, const int32_t* __restrict__ blk_rows,
+    const int32_t* __restrict__ blk_row0, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ n_blocks, int k, const uint8_t* __restrict__ packed,
     size_t stride, size_t off_gc, size_t off_uc, size_t off_gs, size_t off_us, int H, int I,
     int n_tiles, uint8_t* __restrict__ hhi, uint8_t* __restrict__ hlo,
@@ -916,11 +927,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   constexpr int kHP = kBN + 1;  // epilogue h tile: [kBlockRows][kHP] fp32 over the A buffers
   __shared__ __align__(16) uint8_t lds[std::max(2 * kBlockRows * fmt_pitch<F>(), kBlockRows * kHP * 4)];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
-  int blk, nt;
-  if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk, nt)) return;  // workgroup-uniform
-  const int e = blk_expert[blk];
-  const int row0 = blk_row0[blk];
-  const int rows = blk_rows[blk];
+  int e, row0, rows, nt;
+  if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk_expert, blk_row0, offsets, e, row0,
+                      rows, nt))
+    return;  // workgroup-uniform
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int lane = tid & 63;
@@ -1013,17 +1023,16 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_F
     const uint8_t* __restrict__ hshi, const uint8_t* __restrict__ hslo, int Ip,
     const int32_t* __restrict__ perm, const float* __restrict__ wts,
     const int32_t* __restrict__ blk_expert, const int32_t* __restrict__ blk_row0,
-    const int32_t* __restrict__ blk_rows, const int32_t* __restrict__ n_blocks,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_blocks,
     const uint8_t* __restrict__ packed, size_t stride, size_t off_dc, size_t off_ds, int H, int I,
     int n_tiles, float* __restrict__ ypair) {
   constexpr int F = act_fmt<TERMS>();
   __shared__ __align__(16) uint8_t lds[2 * kBlockRows * fmt_pitch<F>()];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
-  int blk, nt;
-  if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk, nt)) return;  // workgroup-uniform
-  const int e = blk_expert[blk];
-  const int row0 = blk_row0[blk];
-  const int rows = blk_rows[blk];
+  int e, row0, rows, nt;
+  if (!map_block_tile((int)blockIdx.x, n_blocks[0], n_tiles, blk_expert, blk_row0, offsets, e, row0,
+                      rows, nt))
+    return;  // workgroup-uniform
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int lane = tid & 63;
@@ -1224,7 +1233,6 @@ BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter)
   L.perm = take(P * 4);
   L.blk_expert = take(nb_max * 4);
   L.blk_row0 = take(nb_max * 4);
-  L.blk_rows = take(nb_max * 4);
   L.n_blocks = take(4);
   L.sort_cnt = (long)P >= kSortSplitMinPairs ? take((size_t)kSortMaxGroups * (size_t)n_experts * 4) : 0;
   L.xhi = take((size_t)T * Hp);
@@ -1254,7 +1262,6 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
   int32_t* perm = reinterpret_cast<int32_t*>(ws + B.perm);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + B.blk_expert);
   int32_t* brow0 = reinterpret_cast<int32_t*>(ws + B.blk_row0);
-  int32_t* brows = reinterpret_cast<int32_t*>(ws + B.blk_rows);
   int32_t* nblk = reinterpret_cast<int32_t*>(ws + B.n_blocks);
   const long P = (long)T * k;
   if (P > 0x7fffffffL) return hipErrorInvalidValue;
@@ -1263,7 +1270,7 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
   if (P < kSortSplitMinPairs) {
     const uint32_t sort_lds = (uint32_t)((3 * n_experts + kSortThreads) * sizeof(int));
     e = launch_kernel(kKindBatchedSort, sort_kernel, dim3(1), dim3(kSortThreads), sort_lds, s, ids,
-                      (int)P, n_experts, offsets, perm, bexp, brow0, brows, nblk);
+                      (int)P, n_experts, offsets, perm, bexp, brow0, nblk);
     if (e != hipSuccess) return e;
   } else {  // many workgroups, each over `chunk` consecutive pairs
     const int G = (int)std::min<long>(kSortMaxGroups, (P + 1023) / 1024);
@@ -1275,7 +1282,7 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
     if (e != hipSuccess) return e;
     const uint32_t scan_lds = (uint32_t)((n_experts + kSortThreads) * sizeof(int));
     e = launch_kernel(kKindBatchedSort, sort_scan_kernel, dim3(1), dim3(kSortThreads), scan_lds, s, G,
-                      n_experts, cnt, offsets, bexp, brow0, brows, nblk);
+                      n_experts, cnt, offsets, bexp, brow0, nblk);
     if (e != hipSuccess) return e;
     e = launch_kernel(kKindBatchedSort, sort_scatter_kernel, dim3(G), dim3(kSortWGThreads), hist_lds,
                       s, ids, (int)P, n_experts, chunk, cnt, perm);
@@ -1293,7 +1300,7 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
   if (gu_grid > 0x7fffffffL) return hipErrorInvalidValue;
   e = launch_kernel(kKindBatchedGateUp, gemm_gate_up_kernel<TERMS, NT>, dim3((unsigned)gu_grid), dim3(kBThreads), 0,
                     s, ws + B.xhi, ws + B.xlo, ws + B.xshi, ws + B.xslo, B.Hp, perm, bexp, brow0,
-                    brows, nblk, k, packed, L.stride, L.m[0].codes, L.m[1].codes, L.m[0].scales,
+                    offsets, nblk, k, packed, L.stride, L.m[0].codes, L.m[1].codes, L.m[0].scales,
                     L.m[1].scales, hidden, inter, gu_tiles, ws + B.hhi, ws + B.hlo, ws + B.hshi,
                     ws + B.hslo, B.Ip);
   if (e != hipSuccess) return e;
@@ -1304,7 +1311,7 @@ static hipError_t batched_ffn(const uint16_t* x, const int32_t* ids, const float
   float* ypair = reinterpret_cast<float*>(ws + B.ypair);
   e = launch_kernel(kKindBatchedDown, gemm_down_kernel<TERMS, NT>, dim3((unsigned)dn_grid), dim3(kBThreads), 0, s,
                     ws + B.hhi, ws + B.hlo, ws + B.hshi, ws + B.hslo, B.Ip, perm, w, bexp, brow0,
-                    brows, nblk, packed, L.stride, L.m[2].codes, L.m[2].scales, hidden, inter,
+                    offsets, nblk, packed, L.stride, L.m[2].codes, L.m[2].scales, hidden, inter,
                     dn_tiles, ypair);
   if (e != hipSuccess) return e;
 

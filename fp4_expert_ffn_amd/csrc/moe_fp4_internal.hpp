@@ -141,7 +141,7 @@ hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,
 constexpr int kBlockRows = 64;  // rows of one expert's group per GEMM workgroup
 
 struct BatchedLayout {
-  size_t offsets, perm, blk_expert, blk_row0, blk_rows, n_blocks, sort_cnt;
+  size_t offsets, perm, blk_expert, blk_row0, n_blocks, sort_cnt;
   size_t xhi, xlo, xshi, xslo, hhi, hlo, hshi, hslo, ypair;
   size_t bytes, nb_max;
   int Hp, Ip;
