@@ -39,11 +39,12 @@
 #include "moe_fp4_device.hpp"
 #include "moe_fp4_internal.hpp"
 
-// B sets of the grouped gate/up K loop (2 or 3: how many chunks ahead its B words load) and
-// its A staging depth (1, or 2 with 2 B sets: chunks between an A load and its LDS store).
-// Measured at 8192 and 32768 tokens: 3 sets 1-2 % ahead of 2; A depth 2 no faster than 1.
+// B sets of the grouped gate/up K loop (1-3: how many chunks ahead its B words load) and its
+// A staging depth (1, or 2 with 2 B sets: chunks between an A load and its LDS store). With
+// 4 B words per wave 3 sets were 1-2 % ahead of 2 (8192 and 32768 tokens); with the 6 words
+// of the default shape 3 sets spill and 2 beat 1 by 4-6 %. A depth 2 was no faster than 1.
 #ifndef MOE_FP4_GU_BSETS
-#define MOE_FP4_GU_BSETS 3
+#define MOE_FP4_GU_BSETS 2
 #endif
 #ifndef MOE_FP4_GU_ADEPTH
 #define MOE_FP4_GU_ADEPTH 1
@@ -75,13 +76,22 @@ __device__ __forceinline__ uint4 ld_w16(const uint8_t* p) {
 
 constexpr int kBWaves = 4;
 constexpr int kBThreads = kBWaves * 64;
-constexpr int kNS = 2;                  // 16-row weight tiles per wave (per matrix)
+// Gate/up: 16-row tiles per wave and matrix (B words per wave: twice that, at most 6). Three
+// tiles (h columns per workgroup 192, so 2880 is 15 whole tiles) against two, both at 2 waves
+// per SIMD: gate/up 2.43 -> 2.04 ms at 8192 tokens, 8.12 -> 6.96 ms at 32768. Each A operand
+// read from LDS then feeds six B words instead of four.
+#ifndef MOE_FP4_GU_NS
+#define MOE_FP4_GU_NS 3
+#endif
+constexpr int kNS = MOE_FP4_GU_NS;
+static_assert(kNS >= 1 && 2 * kNS <= 6, "gate/up B words per wave");
 constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
 // Down: 16-row tiles of W_down per wave, its wavefronts per SIMD and B sets. Measured with the
 // E2M3 operands: 4 tiles at 2 waves per SIMD with 2 B sets took down from 2.01 to 1.87 ms at
-// 8192 tokens (6.29 to 6.20 at 32768) against 2 tiles at 4 waves per SIMD with one set.
+// 8192 tokens (6.29 to 6.20 at 32768) against 2 tiles at 4 waves per SIMD with one set; 5
+// tiles with 2 sets from 1.63 to 1.50 ms (5.19 to 4.78); 6 tiles spill.
 #ifndef MOE_FP4_DN_NS
-#define MOE_FP4_DN_NS 4
+#define MOE_FP4_DN_NS 5
 #endif
 #ifndef MOE_FP4_DN_WPE
 #define MOE_FP4_DN_WPE 2
@@ -90,6 +100,7 @@ constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
 #define MOE_FP4_DN_BSETS 2
 #endif
 constexpr int kDNS = MOE_FP4_DN_NS;
+static_assert(kDNS >= 1 && kDNS <= 6, "down B words per wave");
 constexpr int kBND = 16 * kDNS * kBWaves;  // rows of H per down workgroup
 constexpr int kMSub = kBlockRows / 16;  // 16-row MFMA subtiles per M-block
 constexpr int kSortThreads = 1024;
@@ -507,18 +518,18 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------------------------------
 // Grouped GEMM core shared by both stages. A workgroup owns one M-block (up to kBlockRows
-// rows of one expert's group) and a tile of weight rows: each wave takes 4 B words per chunk
-// (gate/up: 2 consecutive 16-row tiles of each matrix; down: 4 tiles of W_down), so every A
-// operand read from LDS feeds 4 pairs of MFMAs. Per 128-element chunk of K:
+// rows of one expert's group) and a tile of weight rows: each wave takes 5-6 B words per chunk
+// (gate/up: 3 consecutive 16-row tiles of each matrix; down: 5 tiles of W_down), so every A
+// operand read from LDS feeds 5-6 pairs of MFMAs. Per 128-element chunk of K:
 //  * the block's A rows (hi, lo, scales) are staged in one of two LDS buffers; each thread
 //    moves three (E2M3) or four (E4M3) 16-byte pieces and (threads < 2 * kBlockRows) one
 //    scale dword, loaded from global memory about one chunk ahead of their store;
-//  * each wave loads its B words (one 1 KB word per tile) two or three chunks ahead;
+//  * each wave loads its B words (one 1 KB word per tile) one or two chunks ahead;
 //  * 16-row subtiles past the block's rows are skipped (wave-uniform);
 //  * one barrier per chunk.
 // Every load is issued with a clamped chunk index, so the wait counts stay exact. Both GEMM
-// kernels are held to 2 wavefronts per SIMD (4 B words, 64 accumulators and 2-3 B sets per
-// lane; at most 256 registers), two workgroups per CU, so the other workgroup's chunks
+// kernels are held to 2 wavefronts per SIMD (5-6 B words, 80-96 accumulators and 2 B sets
+// per lane; at most 256 registers), two workgroups per CU, so the other workgroup's chunks
 // cover each wave's memory waits.
 // ---------------------------------------------------------------------------------------
 struct GemmCtx {
@@ -669,26 +680,26 @@ __device__ __forceinline__ BWord load_b(const uint8_t* codes, const uint8_t* sca
 // The B words of one wave: NB = (matrices) x kNS tiles, word q = matrix * kNS + tile. Named
 // members (an array carried around the K loop would be placed in private memory).
 struct BPtrs {
-  const uint8_t *c0, *c1, *c2, *c3;  // code base of word q (tile-major word 0)
-  const uint8_t *s0, *s1, *s2, *s3;  // scale base of word q
-  bool on0, on1, on2, on3;           // tile q lies inside its matrix
+  const uint8_t *c0, *c1, *c2, *c3, *c4, *c5;  // code base of word q (tile-major word 0)
+  const uint8_t *s0, *s1, *s2, *s3, *s4, *s5;  // scale base of word q
+  bool on0;                                    // the wave's first tile lies inside its matrix
 };
 
 template <int NB>
 struct BSet {
-  BWord w0, w1, w2, w3;
+  BWord w0, w1, w2, w3, w4, w5;
 };
 
 template <int NB, bool NT>
 __device__ __forceinline__ BSet<NB> load_bset(const BPtrs& p, int c, int KB) {
   BSet<NB> r;
   r.w0 = load_b<NT>(p.c0, p.s0, c, KB);
-  r.w1 = r.w0;
-  r.w2 = r.w0;
-  r.w3 = r.w0;
+  r.w1 = r.w2 = r.w3 = r.w4 = r.w5 = r.w0;
   if constexpr (NB > 1) r.w1 = load_b<NT>(p.c1, p.s1, c, KB);
   if constexpr (NB > 2) r.w2 = load_b<NT>(p.c2, p.s2, c, KB);
   if constexpr (NB > 3) r.w3 = load_b<NT>(p.c3, p.s3, c, KB);
+  if constexpr (NB > 4) r.w4 = load_b<NT>(p.c4, p.s4, c, KB);
+  if constexpr (NB > 5) r.w5 = load_b<NT>(p.c5, p.s5, c, KB);
   return r;
 }
 
@@ -763,6 +774,7 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
     const uint32_t mk = s_ok ? ~0u : 0u; /* E2M3: a lane holds one whole K-block */             \
     const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;                 \
     const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;                 \
+    const int sb4 = s_ok ? (int)BS.w4.s : 127, sb5 = s_ok ? (int)BS.w5.s : 127;                 \
     if (any_on) {                                                                               \
       _Pragma("unroll") for (int m = 0; m < kMSub; ++m) {                                       \
         if (16 * m < rows) { /* wave-uniform */                                                 \
@@ -779,11 +791,15 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
             if constexpr (NB > 1) mfma2<F>(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo, sb1);    \
             if constexpr (NB > 2) mfma2<F>(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo, sb2);    \
             if constexpr (NB > 3) mfma2<F>(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo, sb3);    \
+            if constexpr (NB > 4) mfma2<F>(acc.a[m][4], ahi, alo, BS.w4, sw_hi, sw_lo, sb4);    \
+            if constexpr (NB > 5) mfma2<F>(acc.a[m][5], ahi, alo, BS.w5, sw_hi, sw_lo, sb5);    \
           } else {                                                                              \
             mfma1<F>(acc.a[m][0], ahi, BS.w0, sw_hi, sb0);                                      \
             if constexpr (NB > 1) mfma1<F>(acc.a[m][1], ahi, BS.w1, sw_hi, sb1);                \
             if constexpr (NB > 2) mfma1<F>(acc.a[m][2], ahi, BS.w2, sw_hi, sb2);                \
             if constexpr (NB > 3) mfma1<F>(acc.a[m][3], ahi, BS.w3, sw_hi, sb3);                \
+            if constexpr (NB > 4) mfma1<F>(acc.a[m][4], ahi, BS.w4, sw_hi, sb4);                \
+            if constexpr (NB > 5) mfma1<F>(acc.a[m][5], ahi, BS.w5, sw_hi, sb5);                \
           }                                                                                     \
         }                                                                                       \
       }                                                                                         \
@@ -949,25 +965,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
   const uint8_t* base = packed + (size_t)e * stride;
   const int nt16 = I / 16;
-  const size_t tb0 = (size_t)min(tile0, nt16 - 1) * 16 * KB;  // tile-major word index
-  const size_t tb1 = (size_t)min(tile0 + 1, nt16 - 1) * 16 * KB;
+  // word j < kNS: gate tile tile0 + j; word kNS + j: up tile tile0 + j (tile-major word index
+  // tb(j); tiles past the matrix read its last tile)
+  auto tb = [&](int j) { return (size_t)min(tile0 + j, nt16 - 1) * 16 * KB; };
   BPtrs bp;
-  bp.c0 = base + off_gc + 16 * tb0;  // word 0: gate tile0, 1: gate tile0+1, 2: up tile0, 3: up tile0+1
-  bp.c1 = base + off_gc + 16 * tb1;
-  bp.c2 = base + off_uc + 16 * tb0;
-  bp.c3 = base + off_uc + 16 * tb1;
-  bp.s0 = base + off_gs + tb0;
-  bp.s1 = base + off_gs + tb1;
-  bp.s2 = base + off_us + tb0;
-  bp.s3 = base + off_us + tb1;
-  bp.on0 = bp.on2 = tile0 < nt16;
-  bp.on1 = bp.on3 = tile0 + 1 < nt16;
-  Acc<4> acc;
+  bp.c0 = base + off_gc + 16 * tb(0);
+  bp.s0 = base + off_gs + tb(0);
+  bp.c1 = base + (kNS > 1 ? off_gc + 16 * tb(1) : off_uc + 16 * tb(0));
+  bp.s1 = base + (kNS > 1 ? off_gs + tb(1) : off_us + tb(0));
+  bp.c2 = base + (kNS > 2 ? off_gc + 16 * tb(2) : off_uc + 16 * tb(2 - kNS));
+  bp.s2 = base + (kNS > 2 ? off_gs + tb(2) : off_us + tb(2 - kNS));
+  bp.c3 = base + off_uc + 16 * tb(3 - kNS);
+  bp.s3 = base + off_us + tb(3 - kNS);
+  bp.c4 = base + off_uc + 16 * tb(4 - kNS);
+  bp.s4 = base + off_us + tb(4 - kNS);
+  bp.c5 = base + off_uc + 16 * tb(5 - kNS);
+  bp.s5 = base + off_us + tb(5 - kNS);
+  bp.on0 = tile0 < nt16;
+  Acc<2 * kNS> acc;
 #pragma unroll
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  gemm_k_loop<4, MOE_FP4_GU_BSETS, MOE_FP4_GU_ADEPTH, TERMS, NT>(cx, bp, rows, lds, lds_s, acc);
+    for (int q = 0; q < 2 * kNS; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  gemm_k_loop<2 * kNS, MOE_FP4_GU_BSETS, MOE_FP4_GU_ADEPTH, TERMS, NT>(cx, bp, rows, lds, lds_s, acc);
 
   // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
@@ -977,14 +997,15 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 16 * m + 4 * (lane >> 4) + q;  // block row
-      const int col = 32 * wv + (lane & 15);        // tile tile0 (cols +0..15), tile0+1 (+16..31)
-      htile[i * kHP + col] = silu_f32(acc.a[m][0][q]) * acc.a[m][2][q];
-      htile[i * kHP + col + 16] = silu_f32(acc.a[m][1][q]) * acc.a[m][3][q];
+#pragma unroll
+      for (int j = 0; j < kNS; ++j)  // tile tile0 + j: columns 16 j .. 16 j + 15 of the wave's
+        htile[i * kHP + 16 * (kNS * wv + j) + (lane & 15)] =
+            silu_f32(acc.a[m][j][q]) * acc.a[m][kNS + j][q];
     }
   __syncthreads();
-  static_assert(kBlockRows * (kBN / 32) == kBThreads, "one (row, 32-block) per thread");
-  {
-    const int r = tid / (kBN / 32), b = tid % (kBN / 32);
+  // one (row, 32-block) per thread and round
+  for (int it = tid; it < kBlockRows * (kBN / 32); it += kBThreads) {
+    const int r = it / (kBN / 32), b = it % (kBN / 32);
     const int col = nt * kBN + 32 * b;  // first I index of this 32-block
     if (r < rows && col < I) {
       float v[32];
@@ -1051,23 +1072,22 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_F
 
   const uint8_t* base = packed + (size_t)e * stride;
   const int nt16 = H / 16;
-  const size_t tb0 = (size_t)min(tile0, nt16 - 1) * 16 * KB;
-  const size_t tb1 = (size_t)min(tile0 + 1, nt16 - 1) * 16 * KB;
-  const size_t tb2 = (size_t)min(tile0 + 2, nt16 - 1) * 16 * KB;
-  const size_t tb3 = (size_t)min(tile0 + 3, nt16 - 1) * 16 * KB;
+  // word j: tile tile0 + j (tile-major word index tb(j); tiles past H read the last tile)
+  auto tb = [&](int j) { return (size_t)min(tile0 + j, nt16 - 1) * 16 * KB; };
   BPtrs bp;
-  bp.c0 = base + off_dc + 16 * tb0;
-  bp.c1 = base + off_dc + 16 * tb1;
-  bp.c2 = base + off_dc + 16 * tb2;
-  bp.c3 = base + off_dc + 16 * tb3;
-  bp.s0 = base + off_ds + tb0;
-  bp.s1 = base + off_ds + tb1;
-  bp.s2 = base + off_ds + tb2;
-  bp.s3 = base + off_ds + tb3;
+  bp.c0 = base + off_dc + 16 * tb(0);
+  bp.c1 = base + off_dc + 16 * tb(1);
+  bp.c2 = base + off_dc + 16 * tb(2);
+  bp.c3 = base + off_dc + 16 * tb(3);
+  bp.c4 = base + off_dc + 16 * tb(4);
+  bp.c5 = base + off_dc + 16 * tb(5);
+  bp.s0 = base + off_ds + tb(0);
+  bp.s1 = base + off_ds + tb(1);
+  bp.s2 = base + off_ds + tb(2);
+  bp.s3 = base + off_ds + tb(3);
+  bp.s4 = base + off_ds + tb(4);
+  bp.s5 = base + off_ds + tb(5);
   bp.on0 = tile0 < nt16;
-  bp.on1 = tile0 + 1 < nt16;
-  bp.on2 = kDNS > 2 && tile0 + 2 < nt16;
-  bp.on3 = kDNS > 3 && tile0 + 3 < nt16;
   Acc<kDNS> acc;
 #pragma unroll
   for (int m = 0; m < kMSub; ++m)
@@ -1075,23 +1095,21 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_F
     for (int q = 0; q < kDNS; ++q) acc.a[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   gemm_k_loop<kDNS, MOE_FP4_DN_BSETS, 1, TERMS, NT>(cx, bp, rows, lds, lds_s, acc);
 
+  // per block row: its pair and router weight once, then the wave's tiles
 #pragma unroll
-  for (int s2 = 0; s2 < kDNS; ++s2) {
-    const int tile = tile0 + s2;
-    if (tile < nt16) {
-      const int n = 16 * tile + (lane & 15);
+  for (int m = 0; m < kMSub; ++m)
 #pragma unroll
-      for (int m = 0; m < kMSub; ++m)
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * m + 4 * (lane >> 4) + q;
+      if (i < rows) {
+        const int pair = perm[row0 + i];
+        const float wp = wts[pair];
+        float* yrow = ypair + (size_t)pair * H + (lane & 15);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = 16 * m + 4 * (lane >> 4) + q;
-          if (i < rows) {
-            const int pair = perm[row0 + i];
-            ypair[(size_t)pair * H + n] = wts[pair] * acc.a[m][s2][q];
-          }
-        }
+        for (int s2 = 0; s2 < kDNS; ++s2)
+          if (tile0 + s2 < nt16) yrow[16 * (tile0 + s2)] = wp * acc.a[m][s2][q];
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------------------
