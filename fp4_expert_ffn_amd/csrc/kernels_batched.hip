@@ -613,41 +613,27 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, uint8_t* lds_s, uint4 
 // A operand (hi or lo) of 16-row subtile m for this lane; halves of K-blocks past K are
 // zeroed with the lane masks m0 / m1 (all ones or zero: a select, not a branch, so the
 // LDS reads of one subtile can be scheduled under the previous subtile's MFMAs).
-__device__ __forceinline__ i32x8_t a_operand(const uint8_t* lds, int m, int lane, bool lo,
-                                             uint32_t m0, uint32_t m1) {
+// The A rows need no masking past K: every producer writes its rows' padding K-blocks (up to
+// the next multiple of 128) as zero codes with scale byte 127, and the staging never reads
+// beyond them.
+__device__ __forceinline__ i32x8_t a_operand(const uint8_t* lds, int m, int lane, bool lo) {
   const int r = lane & 15, g = lane >> 4;
   const uint8_t* row = lds + (16 * m + r) * fmt_pitch<kFmtE4M3>() + (lo ? 128 : 0);
   const uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
   const uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-  return i32x8_t{(int)(p0.x & m0), (int)(p0.y & m0), (int)(p0.z & m0), (int)(p0.w & m0),
-                 (int)(p1.x & m1), (int)(p1.y & m1), (int)(p1.z & m1), (int)(p1.w & m1)};
-}
-
-// The same with branches (zeroing only when a mask is clear): fewer live registers, which
-// down's budget needs; its LDS reads wait inside the branches.
-__device__ __forceinline__ i32x8_t a_operand_br(const uint8_t* lds, int m, int lane, bool lo,
-                                                uint32_t m0, uint32_t m1) {
-  const int r = lane & 15, g = lane >> 4;
-  const uint8_t* row = lds + (16 * m + r) * fmt_pitch<kFmtE4M3>() + (lo ? 128 : 0);
-  uint4 p0 = *reinterpret_cast<const uint4*>(row + 16 * g);
-  uint4 p1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-  if (!m0) p0 = make_uint4(0, 0, 0, 0);
-  if (!m1) p1 = make_uint4(0, 0, 0, 0);
   return i32x8_t{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w,
                  (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
 }
 
 // E2M3 A operand (hi or lo) of subtile m: lane 16 g + r holds row r's K-block g, its 32
-// codes in six dwords (24 bytes at 24 g of the row's 96); zeroed with the lane mask mk past K.
-__device__ __forceinline__ i32x8_t a_operand6(const uint8_t* lds, int m, int lane, bool lo,
-                                              uint32_t mk) {
+// codes in six dwords (24 bytes at 24 g of the row's 96).
+__device__ __forceinline__ i32x8_t a_operand6(const uint8_t* lds, int m, int lane, bool lo) {
   const int r = lane & 15, g = lane >> 4;
   const uint8_t* p = lds + (16 * m + r) * fmt_pitch<kFmtE2M3>() + (lo ? 96 : 0) + 24 * g;
   const uint2 p0 = *reinterpret_cast<const uint2*>(p);
   const uint2 p1 = *reinterpret_cast<const uint2*>(p + 8);
   const uint2 p2 = *reinterpret_cast<const uint2*>(p + 16);
-  return i32x8_t{(int)(p0.x & mk), (int)(p0.y & mk), (int)(p1.x & mk), (int)(p1.y & mk),
-                 (int)(p2.x & mk), (int)(p2.y & mk), 0, 0};
+  return i32x8_t{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p2.x, (int)p2.y, 0, 0};
 }
 
 __device__ __forceinline__ i32x8_t b_operand(uint4 w) {
@@ -761,32 +747,28 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   // One chunk C with B set BS: MFMAs on the A buffer of C, then A of C + 1 into the other
   // buffer (last read in chunk C - 1, before its barrier), the A loads of C + 2, the B loads
   // of C + 2 into BS (clamped), one barrier. A halves of this lane: K-blocks
-  // 4 C + 2 h + g / 2; its scale: K-block 4 C + g. Past K the data is zeroed and the scale
-  // forced to 1: padding scale bytes are never written, and a NaN scale (byte 255) would
-  // poison the product even with zero data.
+  // 4 C + 2 h + g / 2 (E4M3) or 4 C + g (E2M3); its scale: K-block 4 C + g. Past K the A rows
+  // hold zero codes with scale byte 127 (written by their producers), and the B scale is
+  // forced to 1: the B lanes there read another word, whose scale byte may be 255 (NaN),
+  // which would poison the zero products.
 #define MOE_FP4_KSTEP(C, BS, X0, X1, X2, X3, XS)                                                 \
   {                                                                                             \
     const uint8_t* A = lds + ((C) & 1) * kBuf;                                                  \
     const uint8_t* AS = lds_s + ((C) & 1) * kBufS;                                              \
-    const uint32_t h0 = 4 * (C) + (g >> 1) < cx.KB ? ~0u : 0u;                                  \
-    const uint32_t h1 = 4 * (C) + 2 + (g >> 1) < cx.KB ? ~0u : 0u;                              \
     const bool s_ok = 4 * (C) + g < cx.KB;                                                      \
-    const uint32_t mk = s_ok ? ~0u : 0u; /* E2M3: a lane holds one whole K-block */             \
     const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;                 \
     const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;                 \
     const int sb4 = s_ok ? (int)BS.w4.s : 127, sb5 = s_ok ? (int)BS.w5.s : 127;                 \
     if (any_on) {                                                                               \
       _Pragma("unroll") for (int m = 0; m < kMSub; ++m) {                                       \
         if (16 * m < rows) { /* wave-uniform */                                                 \
-          const i32x8_t ahi = F == kFmtE2M3 ? a_operand6(A, m, lane, false, mk)                 \
-                              : PAIR        ? a_operand(A, m, lane, false, h0, h1)              \
-                                            : a_operand_br(A, m, lane, false, h0, h1);          \
-          const int sw_hi = s_ok ? (int)AS[8 * (16 * m + r) + g] : 127;                         \
+          const i32x8_t ahi = F == kFmtE2M3 ? a_operand6(A, m, lane, false)                     \
+                                            : a_operand(A, m, lane, false);                     \
+          const int sw_hi = (int)AS[8 * (16 * m + r) + g];                                      \
           if constexpr (TERMS == 2) {                                                           \
-            const i32x8_t alo = F == kFmtE2M3 ? a_operand6(A, m, lane, true, mk)                \
-                                : PAIR        ? a_operand(A, m, lane, true, h0, h1)             \
-                                              : a_operand_br(A, m, lane, true, h0, h1);         \
-            const int sw_lo = s_ok ? (int)AS[8 * (16 * m + r) + 4 + g] : 127;                   \
+            const i32x8_t alo = F == kFmtE2M3 ? a_operand6(A, m, lane, true)                    \
+                                              : a_operand(A, m, lane, true);                    \
+            const int sw_lo = (int)AS[8 * (16 * m + r) + 4 + g];                                \
             mfma2<F>(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo, sb0);                          \
             if constexpr (NB > 1) mfma2<F>(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo, sb1);    \
             if constexpr (NB > 2) mfma2<F>(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo, sb2);    \
@@ -1030,6 +1012,23 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       if constexpr (TERMS == 2) {
         store_act_block<F>(hlo + rb, col / kBlock, l0, l1);
         hslo[pos * (Ip / kBlock) + col / kBlock] = (uint8_t)sl;
+      }
+    }
+  }
+  // the row padding I .. Ip (K-blocks of the down GEMM's last chunk past I): zero codes and
+  // scale byte 127, written once per row by the last column tile's workgroup
+  if (nt == n_tiles - 1) {
+    const int pad = (Ip - I) / kBlock;  // 0..3 blocks
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int it = tid; it < rows * pad; it += kBThreads) {
+      const int r = it / pad, b = I / kBlock + (it - (it / pad) * pad);
+      const long pos = row0 + r;
+      const long rb = pos * act_row_bytes<F>(Ip);
+      store_act_block<F>(hhi + rb, b, z, z);
+      hshi[pos * (Ip / kBlock) + b] = 127;
+      if constexpr (TERMS == 2) {
+        store_act_block<F>(hlo + rb, b, z, z);
+        hslo[pos * (Ip / kBlock) + b] = 127;
       }
     }
   }
