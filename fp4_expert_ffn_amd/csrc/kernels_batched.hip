@@ -42,7 +42,8 @@
 // B sets of the grouped gate/up K loop (1-3: how many chunks ahead its B words load) and its
 // A staging depth (1, or 2 with 2 B sets: chunks between an A load and its LDS store). With
 // 4 B words per wave 3 sets were 1-2 % ahead of 2 (8192 and 32768 tokens); with the 6 words
-// of the default shape 3 sets spill and 2 beat 1 by 4-6 %. A depth 2 was no faster than 1.
+// of the default shape 3 sets spill and 2 beat 1 by 4-6 %. A depth 2 was no faster than 1
+// with either shape (6.78 against 6.71 ms at 32768 tokens with six words).
 #ifndef MOE_FP4_GU_BSETS
 #define MOE_FP4_GU_BSETS 2
 #endif
@@ -89,9 +90,11 @@ constexpr int kBN = 16 * kNS * kBWaves; // weight rows per workgroup
 // Down: 16-row tiles of W_down per wave, its wavefronts per SIMD and B sets. Measured with the
 // E2M3 operands: 4 tiles at 2 waves per SIMD with 2 B sets took down from 2.01 to 1.87 ms at
 // 8192 tokens (6.29 to 6.20 at 32768) against 2 tiles at 4 waves per SIMD with one set; 5
-// tiles with 2 sets from 1.63 to 1.50 ms (5.19 to 4.78); 6 tiles spill.
+// tiles with 2 sets from 1.63 to 1.50 ms (5.19 to 4.78); 6 tiles (384 rows of H per
+// workgroup, 248 registers once the A operands needed no masks) from 1.48 to 1.38 ms (4.68
+// to 4.40).
 #ifndef MOE_FP4_DN_NS
-#define MOE_FP4_DN_NS 5
+#define MOE_FP4_DN_NS 6
 #endif
 #ifndef MOE_FP4_DN_WPE
 #define MOE_FP4_DN_WPE 2
@@ -518,9 +521,9 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------------------------------
 // Grouped GEMM core shared by both stages. A workgroup owns one M-block (up to kBlockRows
-// rows of one expert's group) and a tile of weight rows: each wave takes 5-6 B words per chunk
-// (gate/up: 3 consecutive 16-row tiles of each matrix; down: 5 tiles of W_down), so every A
-// operand read from LDS feeds 5-6 pairs of MFMAs. Per 128-element chunk of K:
+// rows of one expert's group) and a tile of weight rows: each wave takes 6 B words per chunk
+// (gate/up: 3 consecutive 16-row tiles of each matrix; down: 6 tiles of W_down), so every A
+// operand read from LDS feeds 6 pairs of MFMAs. Per 128-element chunk of K:
 //  * the block's A rows (hi, lo, scales) are staged in one of two LDS buffers; each thread
 //    moves three (E2M3) or four (E4M3) 16-byte pieces and (threads < 2 * kBlockRows) one
 //    scale dword, loaded from global memory about one chunk ahead of their store;
@@ -528,8 +531,8 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict
 //  * 16-row subtiles past the block's rows are skipped (wave-uniform);
 //  * one barrier per chunk.
 // Every load is issued with a clamped chunk index, so the wait counts stay exact. Both GEMM
-// kernels are held to 2 wavefronts per SIMD (5-6 B words, 80-96 accumulators and 2 B sets
-// per lane; at most 256 registers), two workgroups per CU, so the other workgroup's chunks
+// kernels are held to 2 wavefronts per SIMD (6 B words, 96 accumulators and 2 B sets per
+// lane; at most 256 registers), two workgroups per CU, so the other workgroup's chunks
 // cover each wave's memory waits.
 // ---------------------------------------------------------------------------------------
 struct GemmCtx {
