@@ -50,6 +50,9 @@
 #ifndef MOE_FP4_GU_ADEPTH
 #define MOE_FP4_GU_ADEPTH 1
 #endif
+#ifndef MOE_FP4_GU_WPE
+#define MOE_FP4_GU_WPE 2  // wavefronts per SIMD the gate/up kernel is compiled for
+#endif
 
 namespace moe_fp4 {
 
@@ -239,6 +242,20 @@ __device__ __forceinline__ v6u_t cvt_e2m3_x32(const float (&v)[32], int X) {
   return r;
 }
 
+typedef float v32f_t __attribute__((ext_vector_type(32)));
+
+// The 32 codes of six packed dwords back to fp32, times 2^X, by the hardware conversion
+// (code i -> element i, exact: every E2M3 value times 2^X with X >= -100 is a normal fp32,
+// and code 32 gives -0 like the software decode below; measured against the E2M3 definition
+// for every code). The scale operand is the power of two itself. As with the conversion the
+// other way, the result is kept apart from the source registers (early clobber).
+__device__ __forceinline__ v32f_t e2m3_decode_x32(const v6u_t& w, int X) {
+  const float sc = __uint_as_float((uint32_t)(X + 127) << 23);  // 2^X, X in [-126, 127]
+  v32f_t r;
+  __asm__("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(r) : "v"(w), "v"(sc));
+  return r;
+}
+
 // code i of six packed dwords
 __device__ __forceinline__ uint32_t e2m3_code(const v6u_t& w, int i) {
   const int bit = 6 * i, d = bit >> 5, sh = bit & 31;
@@ -272,10 +289,19 @@ __device__ __forceinline__ void mx6_encode_block(const float (&v)[32], v6u_t& hi
   hi = cvt_e2m3_x32(v, X);
   float r[32];
   float rmax = 0.f;
+  if (X >= -100) {  // the residual against the hardware decode of hi
+    const v32f_t hv = e2m3_decode_x32(hi, X);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    r[i] = v[i] - e2m3_value(e2m3_code(hi, i), X);
-    rmax = fmaxf(rmax, fabsf(r[i]));
+    for (int i = 0; i < 32; ++i) {
+      r[i] = v[i] - hv[i];
+      rmax = fmaxf(rmax, fabsf(r[i]));
+    }
+  } else {  // tiny blocks: hi's values may be subnormal; decoded in software
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      r[i] = v[i] - e2m3_value(e2m3_code(hi, i), X);
+      rmax = fmaxf(rmax, fabsf(r[i]));
+    }
   }
   const int Xl = mx6_exponent(rmax);
   lo = cvt_e2m3_x32(r, Xl);
@@ -713,6 +739,112 @@ __device__ __forceinline__ void mfma1(f32x4_t& acc, const i32x8_t& ahi, const BW
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, b_operand(b.w), acc, F, 4, 0, sw_hi, 0, sb);
 }
 
+// The MFMAs of one chunk: for each 16-row subtile m of the block (those holding rows), its
+// A operand (hi, and lo with two terms) and scale bytes from LDS against the wave's NB B
+// words. With MOE_FP4_A_PIPE (two terms) the LDS reads run under MFMAs without more
+// registers: lo of m is read before the hi MFMAs of m are issued, hi of m + 1 before the
+// lo MFMAs of m.
+#ifndef MOE_FP4_A_PIPE
+#define MOE_FP4_A_PIPE 1
+#endif
+template <int F, int TERMS>
+struct AOperand {
+  i32x8_t hi, lo;
+  int sh, sl;
+};
+
+template <int F, int TERMS>
+__device__ __forceinline__ AOperand<F, TERMS> load_a_operand(const uint8_t* A, const uint8_t* AS,
+                                                             int m, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  AOperand<F, TERMS> o;
+  o.hi = F == kFmtE2M3 ? a_operand6(A, m, lane, false) : a_operand(A, m, lane, false);
+  o.sh = (int)AS[8 * (16 * m + r) + g];
+  if constexpr (TERMS == 2) {
+    o.lo = F == kFmtE2M3 ? a_operand6(A, m, lane, true) : a_operand(A, m, lane, true);
+    o.sl = (int)AS[8 * (16 * m + r) + 4 + g];
+  } else {
+    o.lo = o.hi;
+    o.sl = o.sh;
+  }
+  return o;
+}
+
+template <int F, int NB, int TERMS>
+__device__ __forceinline__ void subtile_mfmas(f32x4_t (&a)[NB], const AOperand<F, TERMS>& o,
+                                              const BSet<NB>& BS, bool s_ok) {
+  // past K the B lanes read another word: its scale byte is replaced by 1 (127)
+  const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;
+  const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;
+  const int sb4 = s_ok ? (int)BS.w4.s : 127, sb5 = s_ok ? (int)BS.w5.s : 127;
+  if constexpr (TERMS == 2) {
+    mfma2<F>(a[0], o.hi, o.lo, BS.w0, o.sh, o.sl, sb0);
+    if constexpr (NB > 1) mfma2<F>(a[1], o.hi, o.lo, BS.w1, o.sh, o.sl, sb1);
+    if constexpr (NB > 2) mfma2<F>(a[2], o.hi, o.lo, BS.w2, o.sh, o.sl, sb2);
+    if constexpr (NB > 3) mfma2<F>(a[3], o.hi, o.lo, BS.w3, o.sh, o.sl, sb3);
+    if constexpr (NB > 4) mfma2<F>(a[4], o.hi, o.lo, BS.w4, o.sh, o.sl, sb4);
+    if constexpr (NB > 5) mfma2<F>(a[5], o.hi, o.lo, BS.w5, o.sh, o.sl, sb5);
+  } else {
+    mfma1<F>(a[0], o.hi, BS.w0, o.sh, sb0);
+    if constexpr (NB > 1) mfma1<F>(a[1], o.hi, BS.w1, o.sh, sb1);
+    if constexpr (NB > 2) mfma1<F>(a[2], o.hi, BS.w2, o.sh, sb2);
+    if constexpr (NB > 3) mfma1<F>(a[3], o.hi, BS.w3, o.sh, sb3);
+    if constexpr (NB > 4) mfma1<F>(a[4], o.hi, BS.w4, o.sh, sb4);
+    if constexpr (NB > 5) mfma1<F>(a[5], o.hi, BS.w5, o.sh, sb5);
+  }
+}
+
+// One term's MFMAs of one subtile: the accumulators a against the NB B words.
+template <int F, int NB>
+__device__ __forceinline__ void term_mfmas(f32x4_t (&a)[NB], const i32x8_t& op, int sw,
+                                           const BSet<NB>& BS, bool s_ok) {
+  const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;
+  const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;
+  const int sb4 = s_ok ? (int)BS.w4.s : 127, sb5 = s_ok ? (int)BS.w5.s : 127;
+  mfma1<F>(a[0], op, BS.w0, sw, sb0);
+  if constexpr (NB > 1) mfma1<F>(a[1], op, BS.w1, sw, sb1);
+  if constexpr (NB > 2) mfma1<F>(a[2], op, BS.w2, sw, sb2);
+  if constexpr (NB > 3) mfma1<F>(a[3], op, BS.w3, sw, sb3);
+  if constexpr (NB > 4) mfma1<F>(a[4], op, BS.w4, sw, sb4);
+  if constexpr (NB > 5) mfma1<F>(a[5], op, BS.w5, sw, sb5);
+}
+
+template <int F>
+__device__ __forceinline__ i32x8_t a_term(const uint8_t* A, int m, int lane, bool lo) {
+  return F == kFmtE2M3 ? a_operand6(A, m, lane, lo) : a_operand(A, m, lane, lo);
+}
+
+template <int F, int NB, int TERMS>
+__device__ __forceinline__ void chunk_mfmas(const uint8_t* A, const uint8_t* AS, int rows, int lane,
+                                            const BSet<NB>& BS, bool s_ok, Acc<NB>& acc) {
+  if constexpr (MOE_FP4_A_PIPE && TERMS == 2) {
+    const int r = lane & 15, g = lane >> 4;
+    i32x8_t hi = a_term<F>(A, 0, lane, false);
+    int sh = (int)AS[8 * r + g];
+#pragma unroll
+    for (int m = 0; m < kMSub; ++m) {
+      if (16 * m < rows) {  // wave-uniform
+        const i32x8_t lo = a_term<F>(A, m, lane, true);
+        const int sl = (int)AS[8 * (16 * m + r) + 4 + g];
+        term_mfmas<F, NB>(acc.a[m], hi, sh, BS, s_ok);
+        if (m + 1 < kMSub) {
+          hi = a_term<F>(A, m + 1, lane, false);
+          sh = (int)AS[8 * (16 * (m + 1) + r) + g];
+        }
+        term_mfmas<F, NB>(acc.a[m], lo, sl, BS, s_ok);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < kMSub; ++m) {
+      if (16 * m < rows) {  // wave-uniform
+        const AOperand<F, TERMS> o = load_a_operand<F, TERMS>(A, AS, m, lane);
+        subtile_mfmas<F, NB, TERMS>(acc.a[m], o, BS, s_ok);
+      }
+    }
+  }
+}
+
 // BSETS 2 or 3: the K loop runs BSETS chunks per trip with BSETS B sets used in turn and
 // reloaded in place, BSETS chunks ahead (gate/up, which has the registers for it). BSETS 1:
 // one B set rotates (current = next), a register copy that waits for the next set's loads,
@@ -729,7 +861,6 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
   static_assert(BSETS >= 1 && BSETS <= 3, "B sets");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const int r = lane & 15;
   const int nch = (cx.KB + 3) / 4;
   constexpr int F = act_fmt<TERMS>();
   constexpr int kBuf = kBlockRows * fmt_pitch<F>();
@@ -759,36 +890,7 @@ __device__ __forceinline__ void gemm_k_loop(const GemmCtx& cx, const BPtrs& bp, 
     const uint8_t* A = lds + ((C) & 1) * kBuf;                                                  \
     const uint8_t* AS = lds_s + ((C) & 1) * kBufS;                                              \
     const bool s_ok = 4 * (C) + g < cx.KB;                                                      \
-    const int sb0 = s_ok ? (int)BS.w0.s : 127, sb1 = s_ok ? (int)BS.w1.s : 127;                 \
-    const int sb2 = s_ok ? (int)BS.w2.s : 127, sb3 = s_ok ? (int)BS.w3.s : 127;                 \
-    const int sb4 = s_ok ? (int)BS.w4.s : 127, sb5 = s_ok ? (int)BS.w5.s : 127;                 \
-    if (any_on) {                                                                               \
-      _Pragma("unroll") for (int m = 0; m < kMSub; ++m) {                                       \
-        if (16 * m < rows) { /* wave-uniform */                                                 \
-          const i32x8_t ahi = F == kFmtE2M3 ? a_operand6(A, m, lane, false)                     \
-                                            : a_operand(A, m, lane, false);                     \
-          const int sw_hi = (int)AS[8 * (16 * m + r) + g];                                      \
-          if constexpr (TERMS == 2) {                                                           \
-            const i32x8_t alo = F == kFmtE2M3 ? a_operand6(A, m, lane, true)                    \
-                                              : a_operand(A, m, lane, true);                    \
-            const int sw_lo = (int)AS[8 * (16 * m + r) + 4 + g];                                \
-            mfma2<F>(acc.a[m][0], ahi, alo, BS.w0, sw_hi, sw_lo, sb0);                          \
-            if constexpr (NB > 1) mfma2<F>(acc.a[m][1], ahi, alo, BS.w1, sw_hi, sw_lo, sb1);    \
-            if constexpr (NB > 2) mfma2<F>(acc.a[m][2], ahi, alo, BS.w2, sw_hi, sw_lo, sb2);    \
-            if constexpr (NB > 3) mfma2<F>(acc.a[m][3], ahi, alo, BS.w3, sw_hi, sw_lo, sb3);    \
-            if constexpr (NB > 4) mfma2<F>(acc.a[m][4], ahi, alo, BS.w4, sw_hi, sw_lo, sb4);    \
-            if constexpr (NB > 5) mfma2<F>(acc.a[m][5], ahi, alo, BS.w5, sw_hi, sw_lo, sb5);    \
-          } else {                                                                              \
-            mfma1<F>(acc.a[m][0], ahi, BS.w0, sw_hi, sb0);                                      \
-            if constexpr (NB > 1) mfma1<F>(acc.a[m][1], ahi, BS.w1, sw_hi, sb1);                \
-            if constexpr (NB > 2) mfma1<F>(acc.a[m][2], ahi, BS.w2, sw_hi, sb2);                \
-            if constexpr (NB > 3) mfma1<F>(acc.a[m][3], ahi, BS.w3, sw_hi, sb3);                \
-            if constexpr (NB > 4) mfma1<F>(acc.a[m][4], ahi, BS.w4, sw_hi, sb4);                \
-            if constexpr (NB > 5) mfma1<F>(acc.a[m][5], ahi, BS.w5, sw_hi, sb5);                \
-          }                                                                                     \
-        }                                                                                       \
-      }                                                                                         \
-    }                                                                                           \
+    if (any_on) chunk_mfmas<F, NB, TERMS>(A, AS, rows, lane, BS, s_ok, acc);                     \
     stage_store<TERMS>(lds + (((C) + 1) & 1) * kBuf, lds_s + (((C) + 1) & 1) * kBufS, X0, X1,   \
                        X2, X3, XS);                                                             \
     const int cn = min((C) + 2, nch - 1);                                                       \
@@ -915,7 +1017,7 @@ __device__ __forceinline__ bool map_block_tile(int b, int nb, int n_tiles,
 // 3. gate / up / SiLU / h quantisation
 // ---------------------------------------------------------------------------------------
 template <int TERMS, bool NT>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_gate_up_kernel(
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_FP4_GU_WPE))) void gemm_gate_up_kernel(
     const uint8_t* __restrict__ xhi, const uint8_t* __restrict__ xlo,
     const uint8_t* __restrict__ xshi, const uint8_t* __restrict__ xslo, int Hp,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_expert,
