@@ -151,7 +151,8 @@ def test_act_quant_bit_exact(dev, terms, H):
     rounding decisions on the same bf16 inputs. terms 1 is the one-term E4M3 (FP8) mode,
     terms 2 the default grouped path's two E2M3 (FP6) terms. Blocks with zeros, a single
     value, E4M3 and E2M3 grid ties, values 2^-12 below their block maximum, rows scaled over
-    2^-40 .. 2^40, and a ragged last 128-chunk (H 96, 2880)."""
+    2^-40 .. 2^40, blocks at 2^-98, 2^-110, bf16-subnormal magnitudes (block exponent
+    clamped to -127) and 2^124, and a ragged last 128-chunk (H 96, 2880)."""
     C, D = _mods()
     rng = np.random.default_rng(H + terms)
     T = 37
@@ -164,6 +165,11 @@ def test_act_quant_bit_exact(dev, terms, H):
     v[4, :32] = -(np.arange(32) + 0.5) * 0.0625   # every half-step between grid values
     g6 = O.mx_grid("e2m3")
     v[5, :32] = np.append((g6[:-1] + g6[1:]) / 2.0, 7.5)  # E2M3 midpoints at scale 1
+    z = rng.standard_normal((4, 32))
+    v[6, :32] = z[0] * 2.0 ** -98    # block exponent near -100
+    v[7, :32] = z[1] * 2.0 ** -110   # block exponent near -112
+    v[8, :32] = z[2] * 2.0 ** -129   # bf16 subnormals: exponent clamped to -127
+    v[9, :32] = z[3] * 2.0 ** 124    # near the top of the range
     x_bits = O.f64_to_bf16_bits(v)
     x = D.upload_bf16(x_bits, dev)
     nbytes = C.moe_fp4_debug_act_quant_bytes(T, H)
