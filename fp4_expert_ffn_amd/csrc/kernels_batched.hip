@@ -1027,7 +1027,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_F
     int n_tiles, uint8_t* __restrict__ hhi, uint8_t* __restrict__ hlo,
     uint8_t* __restrict__ hshi, uint8_t* __restrict__ hslo, int Ip) {
   constexpr int F = act_fmt<TERMS>();
-  constexpr int kHP = kBN + 1;  // epilogue h tile: [kBlockRows][kHP] fp32 over the A buffers
+  // epilogue h tile over the A buffers: row r's 32-block b at r * kHP + kHBP * b (fp32). With
+  // 36-float blocks and a row pitch of 24 mod 64 floats, the sixteen 16-byte reads served
+  // together fall on distinct banks (a 193-float pitch had 8-way conflicts) and the
+  // accumulator stores are at most 2-way.
+  constexpr int kHBP = 36;
+  constexpr int kHP = (kBN / 32) * kHBP + ((24 - (kBN / 32) * kHBP) % 64 + 64) % 64;
   __shared__ __align__(16) uint8_t lds[std::max(2 * kBlockRows * fmt_pitch<F>(), kBlockRows * kHP * 4)];
   __shared__ __align__(16) uint8_t lds_s[2 * kBlockRows * 8];
   int e, row0, rows, nt;
@@ -1078,16 +1083,17 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_F
 
   // epilogue: h (fp32) for the block's rows x kBN columns into LDS (the loop ended with a
   // barrier), then per (row, 32-block) quantisation by one thread
-  float* htile = reinterpret_cast<float*>(lds);  // [kBlockRows][kBN + 1]
+  float* htile = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int m = 0; m < kMSub; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 16 * m + 4 * (lane >> 4) + q;  // block row
 #pragma unroll
-      for (int j = 0; j < kNS; ++j)  // tile tile0 + j: columns 16 j .. 16 j + 15 of the wave's
-        htile[i * kHP + 16 * (kNS * wv + j) + (lane & 15)] =
-            silu_f32(acc.a[m][j][q]) * acc.a[m][kNS + j][q];
+      for (int j = 0; j < kNS; ++j) {  // tile tile0 + j: columns 16 j .. 16 j + 15 of the wave's
+        const int col = 16 * (kNS * wv + j) + (lane & 15);
+        htile[i * kHP + kHBP * (col >> 5) + (col & 31)] = silu_f32(acc.a[m][j][q]) * acc.a[m][kNS + j][q];
+      }
     }
   __syncthreads();
   // one (row, 32-block) per thread and round
@@ -1097,7 +1103,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(MOE_F
     if (r < rows && col < I) {
       float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = htile[r * kHP + 32 * b + i];
+      for (int i = 0; i < 32; ++i) v[i] = htile[r * kHP + kHBP * b + i];
       uint4 h0, h1, l0, l1;
       uint32_t sh, sl;
       if constexpr (F == kFmtE2M3) {
