@@ -132,10 +132,11 @@ hipError_t launch_down_combine(const int32_t* ids, const float* w, int T, int k,
 // ----------------------------------------------------------------------------------------
 // Batched path: pairs grouped by expert, grouped GEMM on the block-scaled matrix cores.
 // Workspace regions (byte offsets, 256-aligned) for T tokens:
-//   offsets [E+1], perm [T k], M-block table (expert, first row, rows) [nb_max each],
+//   offsets [E+1], perm [T k], M-block table (expert, first sorted row) [nb_max each],
 //   n_blocks [1], the split sort's per-workgroup counts [256 x E],
-//   x as MXFP8 hi / lo [T x Hp] + scales [T x Hp/32] each,
-//   h as MXFP8 hi / lo [T k x Ip] + scales each, per-pair weighted y_e fp32 [T k x H].
+//   x as MX hi / lo [T x Hp bytes reserved each: 24 bytes per 32-block as two E2M3 terms,
+//   32 as one E4M3 term] + scales [T x Hp/32] each,
+//   h the same over [T k x Ip], per-pair weighted y_e fp32 [T k x H].
 // Hp, Ip: hidden, inter rounded up to 128.
 // ----------------------------------------------------------------------------------------
 constexpr int kBlockRows = 64;  // rows of one expert's group per GEMM workgroup
