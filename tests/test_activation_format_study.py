@@ -5,7 +5,8 @@ study runs the oracle FFN at the real shape (hidden 4096, intermediate 2880, 6 e
 token) with x and h replaced by their MX quantisation and compares it with the exact
 oracle, per token, against the output tolerance (normwise max relative error 2e-2, cosine
 0.9995): one FP8 term is far from it, two terms (hi + lo) are well inside it. The grouped
-path uses two E4M3 terms.
+path uses two E2M3 (FP6) terms, which run at the FP4 rate; two E4M3 terms are the reference
+point.
 """
 
 import numpy as np
@@ -38,7 +39,8 @@ def test_activation_format_study():
     err1, cos1 = res[("e4m3", 1)]
     err2, cos2 = res[("e4m3", 2)]
     err6, cos6 = res[("e2m3", 2)]
-    # two terms: inside the tolerance with a wide margin (the grouped path's choice)
+    # two terms: inside the tolerance with a wide margin (two E2M3 terms are the grouped
+    # path's choice)
     assert err2 <= 5e-3 and cos2 >= 0.99999, res
     assert err6 <= 1e-2 and cos6 >= 0.9999, res
     # one FP8 term is an order of magnitude worse than two
