@@ -150,7 +150,7 @@ struct BatchedLayout {
 
 BatchedLayout batched_layout(int T, int k, int n_experts, int hidden, int inter);
 
-// terms: 2 = x and h as two-term MXFP8 (hi + lo), 1 = one term (hi only)
+// terms: 2 = x and h as two MX terms (hi + lo; E2M3 by default), 1 = one E4M3 term (hi only)
 hipError_t launch_batched_ffn(const uint16_t* x, const int32_t* ids, const float* w, int T, int k,
                               const uint8_t* packed, int n_experts, int hidden, int inter,
                               uint16_t* y, void* workspace, int terms, hipStream_t s);
@@ -191,7 +191,7 @@ hipError_t launch_probe_mfma_loop(int fmt_a, int n_workgroups, int iters, uint32
                                   hipStream_t s);
 int probe_mfma_chains();
 
-// The grouped path's activation quantisation of x [T x H] (MXFP8 E4M3, terms 1 or 2)
+// The grouped path's activation quantisation of x [T x H] (terms 1: one E4M3 term; 2: two E2M3 terms)
 // decoded back to fp32 out [T x H]; workspace debug_act_quant_bytes(T, H).
 size_t debug_act_quant_bytes(int T, int H);
 hipError_t launch_debug_act_quant(const uint16_t* x, int T, int H, int terms, void* ws,

@@ -101,7 +101,7 @@ def test_expert_ffn_path_checks(L):
     for path in (C.PATH_AUTO, C.PATH_DECODE, C.PATH_GROUPED):
         assert ffn_ex(path, wsb=8) == C.ERR_WORKSPACE
         assert ffn_ex(path, T=0, wsb=0) == C.OK
-    # the workspace covers the grouped path: sort tables, MXFP8 x and h, fp32 per-pair y
+    # the workspace covers the grouped path: sort tables, MX x and h, fp32 per-pair y
     need = C.moe_fp4_workspace_bytes(64, 6, 384, 4096, 2880)
     assert need >= 64 * 6 * (4096 * 4 + 2 * 2944) + 64 * 2 * 4096
     assert C.moe_fp4_workspace_bytes(0, 6, 384, 4096, 2880) == 0
