@@ -766,6 +766,41 @@ def test_row_counts_and_repeat_determinism(dev, small_layer, T, path):
     check_ffn(outs[0][sample], ref, f"T={T} path {path}")
 
 
+def _routing_with_counts(rng, T, k, E, fixed):
+    """Distinct ids per token; expert e of `fixed` (e -> n) takes slot j in tokens 0 .. n - 1,
+    the other slots random among the experts not in `fixed`."""
+    rest = np.array([e for e in range(E) if e not in fixed])
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        row = [e for e, n in fixed.items() if t < n]
+        row += list(rng.permutation(rest)[: k - len(row)])
+        ids[t] = row
+    w = rng.random((T, k)).astype(np.float32) + np.float32(0.05)
+    return ids, w
+
+
+@pytest.mark.parametrize("path", [GROUPED, GROUPED_FP8], ids=["grouped", "grouped_fp8"])
+@pytest.mark.parametrize("case", ["one_expert_everywhere", "group_edges"])
+def test_grouped_item_order_every_token(dev, small_layer, path, case):
+    """The grouped kernels walk (row block, column tile) items grouped by expert, up to eight
+    row blocks per group. Every token is checked against the oracle where an expert spans
+    several groups: one expert in every one of 1400 tokens (22 row blocks: groups of 8, 8
+    and 6), and experts with exactly 512 and 513 pairs (one full group; a full group and a
+    second group of one single-row block)."""
+    wl, layer = small_layer
+    rng = np.random.default_rng(31 if case == "group_edges" else 32)
+    if case == "one_expert_everywhere":
+        T = 1400
+        ids, w = _routing_with_counts(rng, T, 6, wl.n_experts, {3: T})
+    else:
+        T = 600
+        ids, w = _routing_with_counts(rng, T, 6, wl.n_experts, {0: 513, 1: 512})
+    x_bits = S.activations(wl, 0, 9, tokens=T)
+    y = _run_ffn(layer, x_bits, ids, w, dev, path)
+    ref = _ref(path, x_bits, ids, w, S.expert_source(wl), wl.n_experts, wl.hidden, wl.inter)
+    check_ffn(y, ref, f"{case} path {path}")
+
+
 @pytest.mark.parametrize("E,k,T", [(3, 2, 24), (4, 2, 16), (16, 6, 8)])
 def test_small_m_shared_experts(dev, E, k, T):
     """Many pairs per expert: groups larger than the tile's 8 rows split into several groups
