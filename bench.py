@@ -45,6 +45,17 @@ def gate_up_bytes(hidden: int, inter: int) -> int:
     return n // 2 + n // 32
 
 
+def grouped_gate_up_bytes(d_avg: float, T: int, k: int, hidden: int, inter: int, fp8: bool) -> float:
+    """Algorithmic bytes of one grouped gate/up launch: each distinct expert's gate and up
+    once, x read and h written as MX activations (per element and term: E4M3 one term,
+    E2M3 two; plus the ue8m0 scale byte per 32 elements of each term), over H and I rounded
+    up to 128."""
+    Hp, Ip = (hidden + 127) // 128 * 128, (inter + 127) // 128 * 128
+    nterm, elem = (1, 1.0) if fp8 else (2, 0.75)
+    return (d_avg * gate_up_bytes(hidden, inter) + T * Hp * nterm * (elem + 1 / 32)
+            + T * k * Ip * nterm * (elem + 1 / 32))
+
+
 TRAFFIC_SUMMARIES = [os.path.join(ROOT, "profiles", "decode_layer_hbm_traffic.md"),
                      os.path.join(ROOT, "profiles", "grouped_hbm_traffic.md"),
                      os.path.join(ROOT, "profiles", "small_m_kernel_trace_and_traffic.md")]
@@ -502,6 +513,12 @@ def grouped_measure(torch, C, D, S, layer, wl, dev, K: int, W: int, terms: int) 
         gflops = pairs * 4.0 * H * I  # gate and up
         out["gate_up_tflops"] = round(gflops / (gu * 1e-6) / 1e12, 1)
         out["gate_up_frac_fp4_peak"] = round(gflops / (gu * 1e-6) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4)
+        # HBM bytes per gate/up launch from the committed counter summary (null when it has
+        # none for this workload or the kernel source changed since), against the algorithmic
+        tr = measured_traffic("gemm_gate_up_kernel", wl.name) if terms == 2 else None
+        out["gate_up_traffic_bytes"] = tr
+        out["gate_up_traffic_ratio"] = (round(tr / grouped_gate_up_bytes(d_avg, T, k, H, I, False), 3)
+                                        if tr else None)
     del lgs, x, ids, w, y
     return out
 
@@ -1009,12 +1026,7 @@ def run_batched(args) -> int:
                             "traffic": None, "kernel": "grouped_gate_up",
                             "flops_per_launch": pairs * 4.0 * H * I, "avg_launch_us": round(gu["avg_us"], 3)}
             else:
-                Hp, Ip = (H + 127) // 128 * 128, (I + 127) // 128 * 128
-                # activation bytes per element and term (E4M3 one term, E2M3 two) + the
-                # ue8m0 scale byte per 32 elements of each term
-                nterm, elem = (1, 1.0) if fp8 else (2, 0.75)
-                alg = (d_avg * gate_up_bytes(H, I) + T * Hp * nterm * (elem + 1 / 32)
-                       + pairs * Ip * nterm * (elem + 1 / 32))
+                alg = grouped_gate_up_bytes(d_avg, T, k, H, I, fp8)
                 achieved = alg / t_s / 1e9
                 roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
