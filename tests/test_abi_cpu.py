@@ -41,10 +41,16 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
+    """moe_fp4_strerror: its own text for every status the header defines, "unknown status"
+    for any other value."""
     assert C.moe_fp4_version() >= 100
-    for st in (0, -1, -2, -3, -4, -5):
-        assert C.strerror(st)
-    assert C.strerror(-99) == "unknown status"
+    codes = (C.OK, C.ERR_INVALID_ARG, C.ERR_BAD_SHAPE, C.ERR_MISALIGNED, C.ERR_WORKSPACE,
+             C.ERR_HIP, C.ERR_TOO_LARGE)
+    texts = [C.strerror(st) for st in codes]
+    assert all(texts) and "unknown status" not in texts
+    assert len(set(texts)) == len(codes)
+    for st in (-7, -99, 1, 2**31 - 1):
+        assert C.strerror(st) == "unknown status"
 
 
 def test_packed_sizes():
